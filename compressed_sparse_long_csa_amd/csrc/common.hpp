@@ -1,0 +1,117 @@
+// Device helpers shared by the libcsa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------------ FP8 E4M3 (OCP)
+// Decode by definition: bias 7, subnormals m * 2^-9, S.1111.111 = NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7fc00000u);
+  else if (e == 0u) v = static_cast<float>(m) * 0x1p-9f;
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// Round to nearest even, saturating at +-448; NaN -> 0x7f.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a == a)) return 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  if (e < -6) {                                   // subnormal spacing 2^-9
+    const uint32_t q = static_cast<uint32_t>(rintf(a * 0x1p9f));   // 0..8; 8 is the min normal code
+    return sign | q;
+  }
+  float q = rintf(ldexpf(a, 3 - e));             // in [8, 16]
+  if (q >= 16.0f) { q = 8.0f; e += 1; }
+  const uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | (static_cast<uint32_t>(q) - 8u);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// ------------------------------------------------------------------ E2M1 (OCP MX)
+// Round to nearest even on {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at +-6.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7u | sign;
+  if (a < 1.0f) {
+    const uint32_t q = static_cast<uint32_t>(rintf(a * 2.0f));     // 0, 1 or 2 (2 = 1.0)
+    return sign | q;
+  }
+  if (a >= 6.0f) return sign | 0x7u;
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;   // 0, 1, 2
+  float q = rintf(ldexpf(a, 1 - e));                                   // in [2, 4]
+  if (q >= 4.0f) { q = 2.0f; e += 1; }
+  if (e > 2) return sign | 0x7u;
+  return sign | (static_cast<uint32_t>(e + 1) << 1) | (static_cast<uint32_t>(q) - 2u);
+}
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float v = e == 0u ? 0.5f * static_cast<float>(m)
+                          : ldexpf(1.0f + 0.5f * static_cast<float>(m), static_cast<int>(e) - 1);
+  return (c & 8u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ wave reductions
+// Butterfly over the 64 lanes; the order of operations is fixed by the lane
+// pattern, so every lane ends with the same bits on every run.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// RoPE angle pos * base^(-2i/R) reduced to [-pi, pi] in double precision, so
+// positions up to 2^24 and beyond keep full float accuracy in sin / cos.
+__device__ __forceinline__ void rope_sincos(int64_t pos, int i, int R, float base, float* s,
+                                            float* c) {
+  const double theta = exp2(-2.0 * static_cast<double>(i) / static_cast<double>(R) *
+                            log2(static_cast<double>(base)));
+  double ang = static_cast<double>(pos) * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang = ang - two_pi * rint(ang / two_pi);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *s = static_cast<float>(sd);
+  *c = static_cast<float>(cd);
+}
+
+}  // namespace csa

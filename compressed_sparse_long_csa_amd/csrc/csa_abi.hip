@@ -1,0 +1,207 @@
+// C ABI of libcsa: argument validation, format / path dispatch, error state.
+// The contract of every entry point is documented in include/csa.h.
+#include <stdio.h>
+#include <stdarg.h>
+
+#include "kernels.hpp"
+
+namespace csa {
+
+namespace {
+thread_local char g_err[512] = "";
+
+csa_status fail(csa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+csa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return CSA_OK;
+}
+
+bool fmt_ok(csa_fmt f) { return f >= CSA_F32 && f <= CSA_SPLIT; }
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace csa
+
+using namespace csa;
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(csa_status s) {
+  switch (s) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+    default: return "CSA_ERR_UNKNOWN";
+  }
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+size_t csa_row_bytes(csa_fmt fmt, int D, int rope_dim) {
+  if (!fmt_ok(fmt) || D < 1) return 0;
+  if (fmt == CSA_MXFP4 && D % 32 != 0) return 0;
+  if (fmt == CSA_SPLIT && (rope_dim < 1 || rope_dim >= D)) return 0;
+  return row_bytes(fmt, D, rope_dim);
+}
+
+csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gate_cols,
+                        int64_t n_tok, int D, int m, int nseg, const int64_t* seg_tok_off,
+                        const int64_t* seg_pos0, const int64_t* seg_out_row, int normalize,
+                        const float* norm_w, float eps, int rope_dim, float rope_base, void* out,
+                        csa_fmt out_fmt, hipStream_t stream) {
+  if (n_tok < 0) return fail(CSA_ERR_INVALID_ARG, "csa_compress: n_tok < 0");
+  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "csa_compress: m must be >= 1");
+  if (D < 2) return fail(CSA_ERR_INVALID_ARG, "csa_compress: D must be >= 2");
+  if (D > 4096) return fail(CSA_ERR_UNSUPPORTED, "csa_compress: D > 4096");
+  if (n_tok % m != 0) return fail(CSA_ERR_INVALID_ARG, "csa_compress: n_tok %% m != 0");
+  if (x_fmt != CSA_F32 && x_fmt != CSA_BF16)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: x_fmt must be CSA_F32 or CSA_BF16");
+  if (!fmt_ok(out_fmt)) return fail(CSA_ERR_INVALID_ARG, "csa_compress: bad out_fmt");
+  if (gate_cols != 1 && gate_cols != D)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: gate_cols must be 1 or D");
+  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_dim must be even and in [0, D]");
+  if (out_fmt == CSA_MXFP4 && D % 32 != 0)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: MXFP4 needs D %% 32 == 0");
+  if (out_fmt == CSA_SPLIT && (rope_dim == 0 || D - rope_dim < 1))
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: SPLIT needs 0 < rope_dim < D");
+  if (nseg < 1) return fail(CSA_ERR_INVALID_ARG, "csa_compress: nseg must be >= 1");
+  if (!(eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "csa_compress: eps must be >= 0");
+  if (n_tok == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (!x || !gate || !seg_tok_off || !seg_pos0 || !seg_out_row || !out)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: null pointer");
+  CompressArgs a{x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0, seg_out_row,
+                 normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt};
+  return launched(launch_compress(a, stream), "csa_compress");
+}
+
+csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                         const void* keys, csa_fmt fmt, const int64_t* key_off,
+                         const int64_t* q_pos, int m, float* scores, int64_t ld,
+                         hipStream_t stream) {
+  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "indexer_score: nq < 0");
+  if (n_heads < 1 || d_idx < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: n_heads, d_idx must be >= 1");
+  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: m must be >= 1");
+  if (ld < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: ld must be >= 1");
+  if (fmt != CSA_F32 && fmt != CSA_FP8 && fmt != CSA_MXFP4)
+    return fail(CSA_ERR_INVALID_ARG, "indexer_score: fmt must be CSA_F32, CSA_FP8 or CSA_MXFP4");
+  if (fmt == CSA_F32) {
+    if (n_heads > 64 || d_idx > 256)
+      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: F32 path supports n_heads <= 64, d_idx <= 256");
+  } else {
+    if (d_idx != 128 || n_heads % 16 != 0 || n_heads > 128)
+      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: FP8/MXFP4 paths need d_idx == 128 and n_heads in {16,32,64,128}");
+    if (n_heads == 48 || n_heads == 80 || n_heads == 96 || n_heads == 112)
+      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: n_heads must be 16, 32, 64 or 128");
+  }
+  if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (!q_idx || !w || !keys || !key_off || !q_pos || !scores)
+    return fail(CSA_ERR_INVALID_ARG, "indexer_score: null pointer");
+  IndexerArgs a{q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld};
+  return launched(launch_indexer(a, stream), "indexer_score");
+}
+
+csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
+                       int32_t* idx, float* top_scores, hipStream_t stream) {
+  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "topk_select: nq < 0");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "topk_select: k must be in [1, 4096]");
+  if (ld < 1) return fail(CSA_ERR_INVALID_ARG, "topk_select: ld must be >= 1");
+  if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "topk_select: null pointer");
+  TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};
+  return launched(launch_topk(a, stream), "topk_select");
+}
+
+static csa_status attn_common(const char* name, const AttnArgs& a, hipStream_t stream) {
+  if (a.nq < 0) return fail(CSA_ERR_INVALID_ARG, "%s: query count < 0", name);
+  if (a.H < 1 || a.D < 2) return fail(CSA_ERR_INVALID_ARG, "%s: H, D must be positive", name);
+  if (a.m < 1) return fail(CSA_ERR_INVALID_ARG, "%s: m must be >= 1", name);
+  if (a.n_win < 0) return fail(CSA_ERR_INVALID_ARG, "%s: n_win < 0", name);
+  if (a.idx != nullptr && a.k < 1) return fail(CSA_ERR_INVALID_ARG, "%s: k must be >= 1 with idx", name);
+  if (a.rope_dim < 0 || a.rope_dim % 2 != 0 || a.rope_dim > a.D)
+    return fail(CSA_ERR_INVALID_ARG, "%s: rope_dim must be even and in [0, D]", name);
+  if (!(a.eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
+  if (a.variant < CSA_VARIANT_AUTO || a.variant > CSA_VARIANT_LOW_OCC)
+    return fail(CSA_ERR_INVALID_ARG, "%s: bad variant", name);
+  if (!fmt_ok(a.q_fmt) || !fmt_ok(a.kv_fmt) || !fmt_ok(a.win_fmt) || !fmt_ok(a.out_fmt))
+    return fail(CSA_ERR_INVALID_ARG, "%s: bad format", name);
+  const bool all_f32 = a.q_fmt == CSA_F32 && a.kv_fmt == CSA_F32 && a.win_fmt == CSA_F32 &&
+                       a.out_fmt == CSA_F32;
+  const bool mfma = a.q_fmt == CSA_BF16 && a.kv_fmt == CSA_SPLIT && a.win_fmt == CSA_BF16 &&
+                    a.out_fmt == CSA_BF16;
+  if (all_f32) {
+    if (a.D % 128 != 0 || a.D > 512)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: F32 path needs D in {128, 256, 384, 512}", name);
+  } else if (mfma) {
+    if (a.D != 512 || a.rope_dim != 64)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path needs D == 512 and rope_dim == 64", name);
+    if (a.H % 16 != 0) return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path needs H %% 16 == 0", name);
+    if (a.idx != nullptr && a.k > 2048)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path supports k <= 2048", name);
+  } else {
+    return fail(CSA_ERR_UNSUPPORTED,
+                "%s: supported formats are all-F32, or q/win/out BF16 with a SPLIT cache", name);
+  }
+  if (a.nq == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (!a.q || !a.q_pos || !a.kv || !a.kv_off || !a.sinks || !a.out)
+    return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (a.n_win > 0 && !a.win) return fail(CSA_ERR_INVALID_ARG, "%s: null window pointer", name);
+  return launched(launch_attn(a, stream), name);
+}
+
+csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
+                              const int64_t* q_pos, const float* q_norm_w, float eps,
+                              int rope_dim, float rope_base, const void* kv, csa_fmt kv_fmt,
+                              const int64_t* kv_off, int m, const int32_t* idx, int k,
+                              const void* win, csa_fmt win_fmt, int n_win,
+                              const int32_t* win_len, const float* sinks, float scale,
+                              void* out, csa_fmt out_fmt, csa_variant variant,
+                              hipStream_t stream) {
+  if (B > 0 && n_win > 0 && !win_len)
+    return fail(CSA_ERR_INVALID_ARG, "hybrid_attn_decode: null win_len");
+  AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt, kv_off, m,
+             idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
+             scale, out, out_fmt, static_cast<int>(variant)};
+  return attn_common("hybrid_attn_decode", a, stream);
+}
+
+csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int D,
+                               const int64_t* q_pos, const float* q_norm_w, float eps,
+                               int rope_dim, float rope_base, const void* kv, csa_fmt kv_fmt,
+                               const int64_t* kv_off, int m, const int32_t* idx, int k,
+                               const void* tok, csa_fmt tok_fmt, const int64_t* tok_off,
+                               const int64_t* tok_pos0, int n_win, const float* sinks,
+                               float scale, void* out, csa_fmt out_fmt, csa_variant variant,
+                               hipStream_t stream) {
+  if (nq > 0 && n_win > 0 && (!tok_off || !tok_pos0))
+    return fail(CSA_ERR_INVALID_ARG, "hybrid_attn_prefill: null tok_off / tok_pos0");
+  AttnArgs a{q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt, kv_off, m,
+             idx, k, tok, tok_fmt, n_win, n_win > 0 ? 2 : 0, nullptr, tok_off, tok_pos0, sinks,
+             scale, out, out_fmt,
+             static_cast<int>(variant)};
+  return attn_common("hybrid_attn_prefill", a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal launch interface between the C ABI (csa_abi.hip) and the kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace csa {
+
+__host__ __device__ inline size_t row_bytes(csa_fmt fmt, int D, int R) {
+  switch (fmt) {
+    case CSA_F32: return 4u * static_cast<size_t>(D);
+    case CSA_BF16: return 2u * static_cast<size_t>(D);
+    case CSA_FP8: return static_cast<size_t>(D);
+    case CSA_MXFP4: return static_cast<size_t>(D / 2 + D / 32);
+    case CSA_SPLIT: return static_cast<size_t>(D - R) + 2u * static_cast<size_t>(R);
+    default: return 0;
+  }
+}
+
+struct CompressArgs {
+  const void* x; csa_fmt x_fmt; const float* gate; int gate_cols;
+  int64_t n_tok; int D; int m; int nseg;
+  const int64_t* seg_tok_off; const int64_t* seg_pos0; const int64_t* seg_out_row;
+  int normalize; const float* norm_w; float eps; int rope_dim; float rope_base;
+  void* out; csa_fmt out_fmt;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+
+struct IndexerArgs {
+  const void* q; const float* w; int nq; int H; int d; const void* keys; csa_fmt fmt;
+  const int64_t* key_off; const int64_t* q_pos; int m; float* scores; int64_t ld;
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const float* scores; int64_t ld; int nq; const int64_t* n_valid; int k;
+  int32_t* idx; float* top_scores;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// Attention over [selected or all compressed entries] ++ [window rows].
+// The window of query b is `win_count` consecutive rows starting at row
+// `win_row0` of `win`, where for decode win_row0 = b*n_win and the count is
+// win_len[b]; for prefill they come from the token run (tok_off, tok_pos0).
+struct AttnArgs {
+  const void* q; csa_fmt q_fmt; int nq; int H; int D;
+  const int64_t* q_pos; const float* q_norm_w; float eps; int rope_dim; float rope_base;
+  const void* kv; csa_fmt kv_fmt; const int64_t* kv_off; int m;
+  const int32_t* idx; int k;
+  const void* win; csa_fmt win_fmt; int n_win;
+  int win_mode;                                         // 0 none, 1 decode, 2 prefill
+  const int32_t* win_len;                               // decode
+  const int64_t* tok_off; const int64_t* tok_pos0;      // prefill
+  const float* sinks; float scale; void* out; csa_fmt out_fmt; int variant;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace csa

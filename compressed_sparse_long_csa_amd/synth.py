@@ -122,13 +122,13 @@ def decode_inputs(seed, lengths, *, m, H, D, R, n_win=128, kv_fmt=SPLIT, q_fmt=B
     kv_off = np.zeros(B, dtype=np.int64)
     kv_off[1:] = np.cumsum(n_ent)[:-1]
     kv = random_rows(rng, int(n_ent.sum()), D, kv_fmt, R)
-    win = random_rows(rng, B * n_win, D, win_fmt, R).reshape(B, n_win, -1)
+    win = random_rows(rng, B * n_win, D, win_fmt, R).reshape(B, n_win, row_bytes(win_fmt, D, R))
     win_len = np.minimum(n_win, lengths).astype(np.int32)
-    q = random_rows(rng, B * H, D, q_fmt, R).reshape(B, H, -1)
+    q = random_rows(rng, B * H, D, q_fmt, R).reshape(B, H, row_bytes(q_fmt, D, R))
     keys = q_idx = w = None
     if csa:
         keys = random_rows(rng, int(n_ent.sum()), d_I, idx_fmt)
-        q_idx = random_rows(rng, B * H_I, d_I, idx_fmt).reshape(B, H_I, -1)
+        q_idx = random_rows(rng, B * H_I, d_I, idx_fmt).reshape(B, H_I, row_bytes(idx_fmt, d_I))
         w = rng.uniform(0.0, 1.0, size=(B, H_I)).astype(np.float32)
     sinks = rng.standard_normal(H).astype(np.float32)
     return DecodeInputs(B=B, H=H, D=D, R=R, m=m, n_win=n_win, lengths=lengths,
@@ -196,3 +196,15 @@ def config_decode_inputs(cfg_id, seed=None, B=None, L=None):
                          win_fmt=c["win_fmt"], csa=c["csa"], k=c.get("k", 0),
                          idx_fmt=c.get("idx_fmt", FP8), H_I=c.get("H_I", 0),
                          d_I=c.get("d_I", 0))
+
+
+def random_selection(rng, n_ent, k):
+    """Per row: an ascending random subset of min(k, N) entry indices, -1 padded
+    (a stand-in for a top-k result when only the attention is under test)."""
+    n_ent = np.asarray(n_ent)
+    out = np.full((n_ent.shape[0], k), -1, dtype=np.int32)
+    for b, N in enumerate(n_ent):
+        c = min(k, int(N))
+        if c:
+            out[b, :c] = np.sort(rng.choice(int(N), size=c, replace=False)).astype(np.int32)
+    return out

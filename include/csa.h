@@ -1,0 +1,249 @@
+/*
+ * csa.h -- C ABI of libcsa: the CSA / HCA hybrid compressed attention path of
+ * DeepSeek-V4 on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title -- section):
+ *   "DeepSeek-V4" blog (haiqwa.github.io): CSA / HCA sections, RMSNorm归一化,
+ *       Partial RoPE位置编码, 让注意力学会"忽略" (sink), FP4精度加速 (FP4 indexer),
+ *       百万 token 怎么切分到多张卡 (index visibility rule);
+ *   硅星人 article on DeepSeek V4: the CSA paragraph (compressor, lightning
+ *       indexer, top-k 512/1024, 128-token window, core MQA), the HCA paragraph
+ *       (m'=128, no indexer / top-k), the partial-RoPE / mixed-precision cache
+ *       paragraph, the state-cache / classic-cache paragraph;
+ *   QbitAI piece on batch invariance: bit-identical per-token results however
+ *       a token is batched; no split-KV.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked [host].
+ *   - Every call validates its scalar arguments on the host, enqueues its
+ *     kernels on `stream` and returns; nothing is synchronised.  On any status
+ *     other than CSA_OK nothing was enqueued, except CSA_ERR_HIP, which reports
+ *     a failed launch.  csa_last_error() returns a thread-local message.
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing, keeps no pointer after returning and never writes `const`
+ *     inputs.  Calls on different streams touching disjoint outputs may run
+ *     concurrently.
+ *   - Row formats (csa_fmt), for a row of D values:
+ *       CSA_F32    4*D bytes, float32
+ *       CSA_BF16   2*D bytes, bfloat16
+ *       CSA_FP8    D bytes, OCP FP8 E4M3 (bias 7, max 448, no inf)
+ *       CSA_MXFP4  D/2 bytes of E2M1 codes (element 2i in the low nibble of
+ *                  byte i) then D/32 E8M0 scale bytes, one per 32 elements
+ *                  (OCP Microscaling v1.0); 68 bytes for D=128
+ *       CSA_SPLIT  (D-R) E4M3 bytes for dims [0, D-R) then R bfloat16 for the
+ *                  RoPE dims [D-R, D); 576 bytes for D=512, R=64.  This is the
+ *                  cache entry: BF16 RoPE dims, FP8 elsewhere.
+ *   - Batch invariance: every output element of every call depends only on
+ *     the inputs of its own query / entry / row, through a reduction order
+ *     fixed by the shapes (H, D, k, n_win, ...) and never by the batch, its
+ *     order or the launch variant.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, a mismatch */
+  CSA_ERR_UNSUPPORTED = 2, /* a valid combination this build has no kernel for */
+  CSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} csa_status;
+
+typedef enum csa_fmt {
+  CSA_F32 = 0,
+  CSA_BF16 = 1,
+  CSA_FP8 = 2,
+  CSA_MXFP4 = 3,
+  CSA_SPLIT = 4
+} csa_fmt;
+
+typedef enum csa_variant {
+  CSA_VARIANT_AUTO = 0,     /* pick by the number of workgroups the batch gives */
+  CSA_VARIANT_HIGH_OCC = 1, /* one workgroup per (query, 16 heads): for a full GPU */
+  CSA_VARIANT_LOW_OCC = 2   /* also split the output dims over workgroups: for an
+                               under-filled GPU.  All variants give the same bits. */
+} csa_variant;
+
+int csa_abi_version(void);
+const char* csa_status_string(csa_status s);
+const char* csa_last_error(void);
+/* Bytes of one row of D values in `fmt` (rope_dim is used by CSA_SPLIT only);
+ * 0 if the combination is invalid. */
+size_t csa_row_bytes(csa_fmt fmt, int D, int rope_dim);
+
+/*
+ * csa_compress -- the token-level compressor and the cache write path.
+ *
+ * Source: 硅星人 article, CSA paragraph (every 4 tokens' KV fold into one
+ * entry) and HCA paragraph (m' = 128); DeepSeek-V4 blog, RMSNorm归一化 (norm
+ * on the compressed KV head) and Partial RoPE位置编码 (RoPE on the last dims;
+ * BF16 RoPE dims, FP8 other dims); 硅星人 article, state-cache paragraph
+ * (tokens that do not yet fill a block stay in the caller's state cache).
+ *
+ * For every complete block j of m consecutive tokens of a segment:
+ *   w_t   = softmax over the block of the gate logits g_t
+ *           (gate_cols = 1: one logit per token; gate_cols = D: per channel)
+ *   C     = sum_t w_t * x_t
+ *   if normalize: C = gamma * C / sqrt(mean(C^2) + eps)   (gamma = norm_w or 1)
+ *   if rope_dim:  rotate pairs (D-R+2i, D-R+2i+1) by pos * rope_base^(-2i/R),
+ *                 pos = seg_pos0[s] + j*m
+ *   store C in out_fmt at row seg_out_row[s] + j  (round to nearest even;
+ *   E4M3 saturates at +-448; MXFP4 per the OCP MX v1.0 scale rule).
+ * m = 1, normalize = 1, rope on, out_fmt = BF16 writes sliding-window rows.
+ * normalize = 0, rope_dim = 0, out_fmt = FP8 / MXFP4 writes indexer keys or
+ * indexer queries.
+ *
+ *   x            [n_tok, D] tokens, x_fmt CSA_F32 or CSA_BF16
+ *   gate         [n_tok, gate_cols] float32 gate logits
+ *   seg_tok_off  [nseg+1] int64: segment s holds tokens [seg_tok_off[s],
+ *                seg_tok_off[s+1]); seg_tok_off[0] = 0, seg_tok_off[nseg] =
+ *                n_tok, every segment length a multiple of m (a block that
+ *                would straddle a segment boundary is not written)
+ *   seg_pos0     [nseg] int64 absolute position of each segment's first token
+ *   seg_out_row  [nseg] int64 output row of each segment's first entry
+ *   norm_w       [D] float32 or NULL (gamma = 1)
+ *   out          rows of csa_row_bytes(out_fmt, D, rope_dim)
+ * Errors: INVALID_ARG for null pointers, n_tok % m != 0, m < 1, D < 2,
+ * gate_cols not in {1, D}, odd or too large rope_dim, D % 32 for MXFP4,
+ * rope_dim == 0 or D - rope_dim < 1 for SPLIT; UNSUPPORTED for D > 4096.
+ */
+csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gate_cols,
+                        int64_t n_tok /*[host]*/, int D, int m, int nseg,
+                        const int64_t* seg_tok_off, const int64_t* seg_pos0,
+                        const int64_t* seg_out_row, int normalize, const float* norm_w,
+                        float eps, int rope_dim, float rope_base, void* out, csa_fmt out_fmt,
+                        hipStream_t stream);
+
+/*
+ * indexer_score -- lightning-indexer scores.
+ *
+ * Source: 硅星人 article, CSA paragraph and the indexer detail (multi-head
+ * index queries, ReLU, scores against the compressed index keys); DeepSeek-V4
+ * blog, FP4精度加速 (the indexer runs at FP4); DeepSeek-V4 blog, index
+ * visibility is a rule for the indexer.
+ *
+ * Query i sits at absolute position q_pos[i] and sees N_i = floor((q_pos[i]+1)/m)
+ * keys, rows key_off[i] .. key_off[i] + N_i - 1 of `keys`.  For s < N_i:
+ *   scores[i*ld + s] = sum_{h < n_heads} w[i*n_heads + h] * max(0, q_h . k_s)
+ * The dot products are exact (products of the stored values, summed in fp32);
+ * the head sum runs in a fixed order.  scores[i*ld + s] for s >= N_i are not
+ * written.  N_i is clamped to ld on the device.
+ *
+ *   q_idx   [nq, n_heads] rows of d_idx values in `fmt`
+ *   w       [nq, n_heads] float32 head weights
+ *   keys    rows of d_idx values in `fmt`
+ *   fmt     CSA_F32, CSA_FP8 or CSA_MXFP4 (queries and keys share it)
+ *   key_off [nq] int64, q_pos [nq] int64
+ *   scores  [nq, ld] float32
+ * Supported: F32 any n_heads <= 64, d_idx <= 256; FP8 / MXFP4 with n_heads a
+ * multiple of 16 (<= 128) and d_idx == 128.  Else UNSUPPORTED.
+ */
+csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                         const void* keys, csa_fmt fmt, const int64_t* key_off,
+                         const int64_t* q_pos, int m, float* scores, int64_t ld,
+                         hipStream_t stream);
+
+/*
+ * topk_select -- the top-k selector.
+ *
+ * Source: 硅星人 article, CSA paragraph (keep the 512 most relevant compressed
+ * blocks, 1024 for Pro); DeepSeek-V4 blog, index visibility (for CSA the top-k
+ * selector names the visible entries).
+ *
+ * Row i holds n_i = n_valid[i] (or ld when n_valid is NULL) scores.  The
+ * selected set is the min(k, n_i) best entries ordered by score descending
+ * then index ascending (ties go to the lower index).  idx[i*k ...] receives
+ * the selected indices in ascending index order followed by -1 padding;
+ * top_scores (optional) the matching scores, padding -inf.  Integer work:
+ * the set is exact and does not depend on how rows are batched.  Scores must
+ * not be NaN.  n_valid is clamped to [0, ld] on the device.
+ *
+ *   scores  [nq, ld] float32;  idx [nq, k] int32;  top_scores [nq, k] or NULL
+ * Errors: INVALID_ARG for k < 1, k > 4096, ld < 1, nq < 0, null pointers.
+ */
+csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
+                       int32_t* idx, float* top_scores, hipStream_t stream);
+
+/*
+ * hybrid_attn_decode -- sink multi-query attention of one decode token per
+ * sequence over its compressed entries (top-k selected for CSA, all for HCA)
+ * followed by its sliding window.
+ *
+ * Source: 硅星人 article, CSA paragraph (selected entries plus the 128 window
+ * tokens go to core multi-query attention) and HCA paragraph (all entries
+ * plus the window); DeepSeek-V4 blog, Partial RoPE (window of n_win raw
+ * entries used with the compressed ones), RMSNorm on the query heads, and
+ * 让注意力学会"忽略" (sink logit in the denominator); ai-engineering summary
+ * (head dim 512).
+ *
+ * Query b at absolute position p = q_pos[b] has N_b = floor((p+1)/m) visible
+ * entries, rows kv_off[b] .. kv_off[b] + N_b - 1 of `kv`.  The attended list
+ * is E = (idx[b*k .. b*k+k) with -1 and out-of-range values dropped, in the
+ * given order, which must be ascending) or (0..N_b-1 when idx is NULL),
+ * followed by window rows 0 .. win_len[b]-1 of win[b] (oldest first, the last
+ * one at position p).  For every head h:
+ *   qhat = RoPE_p(RMSNorm(q[b,h]))           (gamma = q_norm_w or 1, eps)
+ *   l_j  = scale * qhat . e_j                (the stored entry is key and value)
+ *   out[b,h] = sum_j e^{l_j} e_j / (sum_j e^{l_j} + e^{sinks[h]})
+ * The reduction over E runs in tiles of 64 entries in list order, starting
+ * from the sink, the same in every variant and batch.
+ *
+ *   q, out   [B, H] rows of D values (q_fmt / out_fmt: F32 or BF16)
+ *   kv       rows of D values in kv_fmt (SPLIT, or F32 on the fp32 path)
+ *   win      [B, n_win] rows in win_fmt (BF16, or F32 on the fp32 path)
+ *   win_len  [B] int32 (clamped to [0, n_win] on the device)
+ *   sinks    [H] float32
+ * Paths: all-F32 (q, kv, win, out F32; any D <= 512, H <= 1024); MFMA path
+ * (q BF16, kv SPLIT with D = 512, rope_dim = 64, win BF16, out BF16, H a
+ * multiple of 16, k <= 2048).  Other combinations: UNSUPPORTED.
+ */
+csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
+                              const int64_t* q_pos, const float* q_norm_w, float eps,
+                              int rope_dim, float rope_base, const void* kv, csa_fmt kv_fmt,
+                              const int64_t* kv_off, int m, const int32_t* idx, int k,
+                              const void* win, csa_fmt win_fmt, int n_win,
+                              const int32_t* win_len, const float* sinks, float scale,
+                              void* out, csa_fmt out_fmt, csa_variant variant,
+                              hipStream_t stream);
+
+/*
+ * hybrid_attn_prefill -- the same attention for a chunk of causal queries.
+ *
+ * Source: as hybrid_attn_decode; causal visibility by rule (DeepSeek-V4 blog,
+ * index visibility).
+ *
+ * Query i at absolute position p = q_pos[i] sees entries
+ * kv_off[i] .. kv_off[i] + floor((p+1)/m) - 1 (filtered by its own top-k row
+ * idx[i*k ..] for CSA) and the window positions max(0, p-n_win+1) .. p, read
+ * from a run of per-token rows: the row of position t is
+ * tok_off[i] + (t - tok_pos0[i]) of `tok` (already normalised and rotated,
+ * as written by csa_compress with m = 1).  Window positions below tok_pos0[i]
+ * are skipped.  A token gets the same bits here as from hybrid_attn_decode
+ * given the same entries and window rows.
+ *
+ *   q, out  [nq, H] rows;  kv_off, tok_off, tok_pos0, q_pos  [nq] int64
+ * Formats and paths as hybrid_attn_decode, with tok_fmt in place of win_fmt.
+ */
+csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int D,
+                               const int64_t* q_pos, const float* q_norm_w, float eps,
+                               int rope_dim, float rope_base, const void* kv, csa_fmt kv_fmt,
+                               const int64_t* kv_off, int m, const int32_t* idx, int k,
+                               const void* tok, csa_fmt tok_fmt, const int64_t* tok_off,
+                               const int64_t* tok_pos0, int n_win, const float* sinks,
+                               float scale, void* out, csa_fmt out_fmt, csa_variant variant,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

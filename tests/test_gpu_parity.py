@@ -1,0 +1,208 @@
+"""GPU parity: every libcsa entry point against the float64 oracle on the same
+seeded bytes.  Tolerances: fp32 paths 1e-5 normwise per (query, head); BF16 /
+FP8 / FP4 paths 2e-2 max-abs after dividing by the oracle's RMS per (query,
+head); top-k index sets exact; quantised codes exact except where the
+oracle's value sits on a rounding midpoint (both neighbours are correct)."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_long_csa_amd as csa
+from compressed_sparse_long_csa_amd import synth
+from oracle import formats as OF
+from oracle import method as OM
+
+from gpu_common import (DEV, EPS, ROPE_BASE, assert_f32_close, assert_lowp_close, decode_out,
+                        dev, gpu_bytes, oracle_decode_query, oracle_scores, run_decode,
+                        upload_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa.load_library()
+
+
+# ------------------------------------------------------------------ compressor
+def _quant_ok(gpu_vals, y, fmt, tol):
+    """Elementwise: the GPU value equals the oracle's rounding of y, or the two
+    candidates are neighbours and y lies within `tol` (the fp32 error bound of
+    the GPU's value) of their midpoint, where either rounding is correct."""
+    rnd = {csa.BF16: OF.round_bf16, csa.FP8: OF.round_e4m3}[fmt]
+    want = rnd(y)
+    bad = gpu_vals != want
+    if not bad.any():
+        return 0
+    mid = 0.5 * (gpu_vals[bad] + want[bad])
+    near = np.abs(y[bad] - mid) <= tol[bad]
+    assert near.all(), f"{int((~near).sum())} codes differ away from a rounding midpoint"
+    return int(bad.sum())
+
+
+def _compress_error_bound(x, g, m, y, R, normalize):
+    """A loose bound of |fp32 result - exact| for the compressor: the gated sum
+    of m terms (m * 2^-24 relative to sum_t w_t |x_t|), scaled by the norm
+    factor, plus a few roundings of the result itself."""
+    T, D = x.shape
+    gb = g.reshape(T // m, m, g.shape[1])
+    w = np.exp(gb - gb.max(axis=1, keepdims=True))
+    w = w / w.sum(axis=1, keepdims=True)
+    S = (w * np.abs(x.reshape(T // m, m, D))).sum(axis=1)
+    C = (w * x.reshape(T // m, m, D)).sum(axis=1)
+    r = 1.0 / np.sqrt(np.mean(C * C, axis=1, keepdims=True) + EPS) if normalize else 1.0
+    bound = (m + 4) * 2.0 ** -24 * S * r
+    if R:
+        pair = bound[:, D - R::2] + bound[:, D - R + 1::2]
+        bound[:, D - R::2] = pair
+        bound[:, D - R + 1::2] = pair
+    return 2.0 * bound + 2.0 ** -20 * np.abs(y)
+
+
+@pytest.mark.parametrize("m,gate_cols,out_fmt,D,R", [
+    (4, 1, csa.F32, 128, 64), (128, 1, csa.F32, 128, 64), (4, "D", csa.F32, 64, 16),
+    (4, 1, csa.SPLIT, 512, 64), (128, 1, csa.SPLIT, 512, 64), (1, 1, csa.BF16, 512, 64),
+    (4, 1, csa.FP8, 128, 0), (4, 1, csa.MXFP4, 128, 0), (1, 1, csa.MXFP4, 128, 0),
+])
+def test_compress_matches_oracle(m, gate_cols, out_fmt, D, R):
+    gc = D if gate_cols == "D" else gate_cols
+    seg_len = [m * 7, m * 3, 0, m * 11]               # ragged segments incl. an empty one
+    seg_pos0 = [0, 4 * m, 96 * m, 1000 * m]
+    T = sum(seg_len)
+    tok = synth.token_inputs(11 + m, T, D, gc)
+    off = np.concatenate([[0], np.cumsum(seg_len)]).astype(np.int64)
+    nent = [s // m for s in seg_len]
+    out_row = np.array([5, 5 + nent[0], 0, 5 + nent[0] + nent[1]], dtype=np.int64)
+    n_rows = int(out_row[-1] + nent[-1])
+    rb = csa.row_bytes(out_fmt, D, R)
+    out = torch.zeros(n_rows * rb, dtype=torch.uint8, device=DEV)
+    normalize = R > 0
+    csa.csa_compress(dev(tok.x), csa.F32, dev(tok.gate), gc, T, D, m, 4, dev(off),
+                     dev(np.array(seg_pos0, np.int64)), dev(out_row), normalize, None, EPS, R,
+                     ROPE_BASE, out, out_fmt)
+    raw = out.cpu().numpy().reshape(n_rows, rb)
+    flips = 0
+    for s in range(4):
+        if nent[s] == 0:
+            continue
+        x = tok.x[off[s]: off[s + 1]].astype(np.float64)
+        g = tok.gate[off[s]: off[s + 1]].astype(np.float64)
+        y = OM.compress_entries(x, g, m, seg_pos0[s], eps=EPS, R=R, normalize=normalize)
+        tol = _compress_error_bound(x, g, m, y, R, normalize)
+        rows = raw[out_row[s]: out_row[s] + nent[s]]
+        if out_fmt == csa.F32:
+            assert_f32_close(OF.decode_rows(rows, csa.F32, D), y, what="compress f32")
+        elif out_fmt in (csa.BF16, csa.FP8):
+            flips += _quant_ok(OF.decode_rows(rows, out_fmt, D), y, out_fmt, tol)
+        elif out_fmt == csa.SPLIT:
+            dec = OF.decode_rows(rows, csa.SPLIT, D, R)
+            flips += _quant_ok(dec[:, : D - R], y[:, : D - R], csa.FP8, tol[:, : D - R])
+            flips += _quant_ok(dec[:, D - R:], y[:, D - R:], csa.BF16, tol[:, D - R:])
+        elif out_fmt == csa.MXFP4:
+            want = OF.mxfp4_encode(y)
+            for r in range(rows.shape[0]):
+                for blk in range(D // 32):
+                    if rows[r, D // 2 + blk] != want[r, D // 2 + blk]:
+                        sl = slice(blk * 32, (blk + 1) * 32)
+                        amax = np.abs(y[r, sl]).max()
+                        p2 = 2.0 ** np.round(np.log2(amax))
+                        assert abs(amax - p2) <= tol[r, sl].max()
+                        flips += 1
+                        continue
+                    gv = OF.mxfp4_decode(rows[r:r + 1], D)[0, blk * 32:(blk + 1) * 32]
+                    wv = OF.mxfp4_decode(want[r:r + 1], D)[0, blk * 32:(blk + 1) * 32]
+                    sc = 2.0 ** (int(rows[r, D // 2 + blk]) - 127)
+                    bad = gv != wv
+                    if bad.any():
+                        yy = y[r, blk * 32:(blk + 1) * 32][bad]
+                        mid = 0.5 * (gv[bad] + wv[bad])
+                        assert np.all(np.abs(yy - mid) <= tol[r, blk * 32:(blk + 1) * 32][bad])
+                        flips += int(bad.sum())
+    assert flips <= max(2, raw.size // 1000)
+
+
+# ------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("fmt,H_I,d_I,lengths", [
+    (csa.F32, 4, 64, [2048, 777, 5]),
+    (csa.FP8, 64, 128, [65536, 4099, 1000, 3]),
+    (csa.FP8, 16, 128, [5000]),
+    (csa.MXFP4, 64, 128, [40000, 1024, 9]),
+])
+def test_indexer_matches_oracle(fmt, H_I, d_I, lengths):
+    inp = synth.decode_inputs(21, lengths, m=4, H=16, D=128 if fmt == csa.F32 else 512, R=64,
+                              kv_fmt=csa.F32 if fmt == csa.F32 else csa.SPLIT,
+                              q_fmt=csa.F32 if fmt == csa.F32 else csa.BF16,
+                              win_fmt=csa.F32 if fmt == csa.F32 else csa.BF16,
+                              k=64, idx_fmt=fmt, H_I=H_I, d_I=d_I)
+    B = inp.B
+    ld = int(inp.n_ent.max()) + 3
+    scores = torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(dev(inp.q_idx), dev(inp.w), B, H_I, d_I, dev(inp.keys), fmt,
+                      dev(inp.kv_off), dev(inp.q_pos), inp.m, scores, ld)
+    got = scores.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        N = int(inp.n_ent[b])
+        ref = oracle_scores(inp, b)
+        if N:
+            err = np.abs(got[b, :N] - ref).max() / max(1.0, np.abs(ref).max())
+            assert err <= 1e-5, f"row {b}: relative score error {err:.3g}"
+        assert np.all(got[b, N:] == -7.0), "scores past N must stay untouched"
+
+
+# ------------------------------------------------------------------ top-k
+@pytest.mark.parametrize("ld,k,tie_levels,n_valid", [
+    (16384, 512, 0, None), (16384, 512, 5, None), (5000, 1024, 0, [5000, 4999, 1024, 1000, 1, 0]),
+    (262144, 1024, 0, [262144, 100000]), (3000, 64, 3, [3000, 64, 65, 2]), (70000, 2048, 0, None),
+])
+def test_topk_exact(ld, k, tie_levels, n_valid):
+    nq = len(n_valid) if n_valid else 4
+    s, nv = synth.random_scores(31 + k, nq, ld, n_valid, tie_levels)
+    if tie_levels == 0:
+        s[0, 100:300] = s[0, 50]                    # a run of exact ties
+    idx = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    tops = torch.empty((nq, k), dtype=torch.float32, device=DEV)
+    csa.topk_select(dev(s), ld, nq, dev(nv), k, idx, tops)
+    got = idx.cpu().numpy()
+    gs = tops.cpu().numpy()
+    for i in range(nq):
+        n = int(nv[i])
+        want = OM.top_k(s[i, :n].astype(np.float64), k)
+        c = len(want)
+        assert np.array_equal(got[i, :c], want), f"row {i}"
+        assert np.all(got[i, c:] == -1)
+        assert np.array_equal(gs[i, :c], s[i, want])
+        assert np.all(np.isneginf(gs[i, c:]))
+
+
+# ------------------------------------------------------------------ attention
+def _decode_case(cfg, lengths, seed, csa_mode):
+    c = synth.CONFIGS[cfg]
+    return synth.decode_inputs(seed, lengths, m=c["m"], H=c["H"], D=c["D"], R=c["R"],
+                               n_win=c["n_win"], kv_fmt=c["kv_fmt"], q_fmt=c["q_fmt"],
+                               win_fmt=c["win_fmt"], csa=csa_mode, k=c.get("k", 512),
+                               idx_fmt=c.get("idx_fmt", csa.FP8), H_I=c.get("H_I", 64),
+                               d_I=c.get("d_I", 128))
+
+
+@pytest.mark.parametrize("cfg,lengths,csa_mode", [
+    (1, [2048, 300, 7], True), (1, [2048], False),
+    (2, [65536, 9000, 2051, 130, 5], True),
+    (3, [262144, 40000, 128, 127], False),
+    (2, [4100, 777], False),
+])
+def test_attn_decode_matches_oracle(cfg, lengths, csa_mode):
+    inp = _decode_case(cfg, lengths, 40 + cfg, csa_mode)
+    rng = np.random.default_rng(99)
+    sel = synth.random_selection(rng, inp.n_ent, inp.k) if csa_mode else None
+    out, _ = run_decode(inp, dev(sel) if sel is not None else None)
+    fmt = csa.F32 if inp.q_fmt == csa.F32 else csa.BF16
+    got = decode_out(out, fmt, inp.B, inp.H, inp.D)
+    for b in range(inp.B):
+        s = sel[b][sel[b] >= 0] if sel is not None else None
+        ref = oracle_decode_query(inp, b, s)
+        if fmt == csa.F32:
+            assert_f32_close(got[b], ref, what=f"cfg{cfg} b{b}")
+        else:
+            assert_lowp_close(got[b], ref, what=f"cfg{cfg} b{b}")
