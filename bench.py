@@ -1,0 +1,319 @@
+"""Benchmark of the CSA decode hot path on one MI355X.
+
+One step = one decode token for each of the B sequences through the whole
+path, every kernel from libcsa:
+  1. csa_compress  -- fold the newest block of m tokens of every sequence into
+                      its cache entry (split FP8/BF16 row, RMSNorm, RoPE)
+  2. csa_compress  -- the matching indexer key (FP8)
+  3. csa_compress  -- the new token's sliding-window row (m = 1, BF16)
+  4. indexer_score -- ReLU multi-head scores over every visible entry
+  5. topk_select   -- the k best entries, ascending
+  6. hybrid_attn_decode -- sink MQA over the selected entries + window
+Inputs are seeded synthetic tensors already resident in HBM.  The step is
+captured once in a HIP graph and replayed; W warm-up steps, then K timed
+steps between two synchronised events.  The workload is the CSA decode batch
+of 16 sequences of 65,536 tokens (16,384 compressed entries each, top-k 512,
+FP8 indexer 64 x 128, 64 query heads, head dim 512).
+
+Prints one JSON line.  `roofline` is measured for the dominant kernel
+(indexer_score) with events around its launches on its stream;
+`cpu_baseline` times the float64 oracle on a bounded sample on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import compressed_sparse_long_csa_amd as csa  # noqa: E402
+from compressed_sparse_long_csa_amd import synth  # noqa: E402
+
+METRIC = "CSA/HCA decode query-tokens/s and achieved HBM GB/s at 64K-1M context"
+HBM_PEAK_GBPS = 8000.0
+EPS, BASE = 1e-6, 10000.0
+
+
+def build_workload(cfg_id=2, B=None, L=None, seed=2):
+    c = synth.CONFIGS[cfg_id]
+    inp = synth.config_decode_inputs(cfg_id, seed=seed, B=B, L=L)
+    m, D, R, d_I = c["m"], c["D"], c["R"], c["d_I"]
+    rng = synth.rng_for(seed + 1000)
+    Bn = inp.B
+    # the newest complete block of every sequence, its index-key tokens, and the newest token
+    kv_tok = rng.standard_normal((Bn * m, D), dtype=np.float32)
+    kv_gate = rng.standard_normal((Bn * m, 1), dtype=np.float32)
+    key_tok = rng.standard_normal((Bn * m, d_I), dtype=np.float32)
+    key_gate = rng.standard_normal((Bn * m, 1), dtype=np.float32)
+    win_tok = rng.standard_normal((Bn, D), dtype=np.float32)
+    win_gate = np.zeros((Bn, 1), dtype=np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    W = dict(
+        c=c, inp=inp, B=Bn, m=m, D=D, R=R, d_I=d_I,
+        q=dev(inp.q), q_pos=dev(inp.q_pos), kv=dev(inp.kv), kv_off=dev(inp.kv_off),
+        win=dev(inp.win), win_len=dev(inp.win_len), sinks=dev(inp.sinks),
+        keys=dev(inp.keys), q_idx=dev(inp.q_idx), w=dev(inp.w),
+        kv_tok=dev(kv_tok).to(torch.bfloat16), kv_gate=dev(kv_gate),
+        key_tok=dev(key_tok).to(torch.bfloat16), key_gate=dev(key_gate),
+        win_tok=dev(win_tok).to(torch.bfloat16), win_gate=dev(win_gate),
+    )
+    n_ent = torch.from_numpy(inp.n_ent)
+    last = torch.from_numpy(inp.kv_off) + n_ent - 1
+    seg_off = torch.arange(0, Bn + 1, dtype=torch.int64) * m
+    W["seg_off"] = seg_off.cuda()
+    W["seg_pos0"] = ((n_ent - 1) * m).cuda()                # first token of the newest block
+    W["seg_row"] = last.cuda()
+    W["win_seg_off"] = torch.arange(0, Bn + 1, dtype=torch.int64).cuda()
+    W["win_pos0"] = torch.from_numpy(inp.q_pos).cuda()
+    W["win_row"] = (torch.arange(Bn, dtype=torch.int64) * inp.n_win + (torch.from_numpy(inp.win_len).long() - 1)).cuda()
+    W["n_valid"] = n_ent.cuda()
+    W["ld"] = int(inp.n_ent.max())
+    W["scores"] = torch.empty((Bn, W["ld"]), dtype=torch.float32, device="cuda")
+    W["idx"] = torch.empty((Bn, c["k"]), dtype=torch.int32, device="cuda")
+    W["out"] = torch.empty((Bn, c["H"], D), dtype=torch.bfloat16, device="cuda")
+    return W
+
+
+def make_step(W, check=False):
+    c, inp = W["c"], W["inp"]
+    B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
+
+    def k_compress_kv():
+        csa.csa_compress(W["kv_tok"], csa.BF16, W["kv_gate"], 1, B * m, D, m, B, W["seg_off"],
+                         W["seg_pos0"], W["seg_row"], 1, None, EPS, R, BASE, W["kv"], csa.SPLIT,
+                         check=check)
+
+    def k_compress_key():
+        csa.csa_compress(W["key_tok"], csa.BF16, W["key_gate"], 1, B * m, d_I, m, B,
+                         W["seg_off"], W["seg_pos0"], W["seg_row"], 0, None, EPS, 0, BASE,
+                         W["keys"], csa.FP8, check=check)
+
+    def k_compress_win():
+        csa.csa_compress(W["win_tok"], csa.BF16, W["win_gate"], 1, B, D, 1, B, W["win_seg_off"],
+                         W["win_pos0"], W["win_row"], 1, None, EPS, R, BASE, W["win"], csa.BF16,
+                         check=check)
+
+    def k_indexer():
+        csa.indexer_score(W["q_idx"], W["w"], B, c["H_I"], d_I, W["keys"], csa.FP8, W["kv_off"],
+                          W["q_pos"], m, W["scores"], W["ld"], check=check)
+
+    def k_topk():
+        csa.topk_select(W["scores"], W["ld"], B, W["n_valid"], k, W["idx"], None, check=check)
+
+    def k_attn():
+        csa.hybrid_attn_decode(W["q"], csa.BF16, B, H, D, W["q_pos"], None, EPS, R, BASE, W["kv"],
+                               csa.SPLIT, W["kv_off"], m, W["idx"], k, W["win"], csa.BF16,
+                               inp.n_win, W["win_len"], W["sinks"], inp.scale, W["out"], csa.BF16,
+                               csa.VARIANT_AUTO, check=check)
+
+    kernels = [("csa_compress_kv", k_compress_kv), ("csa_compress_key", k_compress_key),
+               ("csa_compress_win", k_compress_win), ("indexer_score", k_indexer),
+               ("topk_select", k_topk), ("hybrid_attn_decode", k_attn)]
+
+    def step():
+        for _, f in kernels:
+            f()
+    return step, kernels
+
+
+def algorithmic_bytes(W):
+    """Bytes the method must move per step (each input read once, each output
+    written once); scratch round trips (scores, idx) are counted per kernel."""
+    inp, c = W["inp"], W["c"]
+    B, D, R, m, d_I, H, k = W["B"], W["D"], W["R"], W["m"], W["d_I"], c["H"], c["k"]
+    N = inp.n_ent.astype(np.int64)
+    split = (D - R) + 2 * R
+    sel = np.minimum(k, N)
+    per_kernel = {
+        "csa_compress_kv": B * m * (2 * D + 4) + B * split,
+        "csa_compress_key": B * m * (2 * d_I + 4) + B * d_I,
+        "csa_compress_win": B * (2 * D + 4) + B * 2 * D,
+        "indexer_score": int((N * (d_I + 4)).sum()) + B * c["H_I"] * (d_I + 4),
+        "topk_select": int((N * 4).sum()) + B * k * 4,
+        "hybrid_attn_decode": int((sel * split).sum()) + int(inp.win_len.sum()) * 2 * D
+        + B * k * 4 + B * H * D * 2 * 2 + H * 4,
+    }
+    step_bytes = (int((N * d_I).sum()) + B * c["H_I"] * (d_I + 4) + int((sel * split).sum())
+                  + int(inp.win_len.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4)
+    return step_bytes, per_kernel
+
+
+def time_graph(step, steps, warmup):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(1, warmup)):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, g
+
+
+def time_kernels(kernels, steps):
+    """Average duration of every kernel, with events recorded around each
+    launch on the stream the kernel runs on (torch's current stream)."""
+    ev = {n: [] for n, _ in kernels}
+    for _ in range(steps):
+        for n, f in kernels:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    return {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+
+
+def spot_check(W):
+    """Compare the step's attention output for one sequence with the oracle."""
+    from oracle import formats as OF
+    from oracle import method as OM
+    inp = W["inp"]
+    b = 0
+    N = int(inp.n_ent[b])
+    idx = W["idx"][b].cpu().numpy()
+    sel = idx[idx >= 0]
+    kv = W["kv"].cpu().numpy()
+    off = int(inp.kv_off[b])
+    ents = np.zeros((N, W["D"]))
+    ents[sel] = OF.decode_rows(kv[off + sel], csa.SPLIT, W["D"], W["R"])
+    wl = int(inp.win_len[b])
+    win = OF.decode_rows(W["win"][b, :wl].cpu().numpy(), csa.BF16, W["D"])
+    q = OF.decode_rows(inp.q[b], csa.BF16, W["D"])
+    ref = OM.decode_one(q, int(inp.q_pos[b]), ents, win, inp.sinks.astype(np.float64), inp.scale,
+                        W["m"], idx=sel, R=W["R"])
+    got = OF.decode_rows(W["out"][b].view(torch.uint8).cpu().numpy(), csa.BF16, W["D"]).reshape(ref.shape)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    ax = np.abs(ref)
+    _, e = np.frexp(np.where(ax > 0, ax, 1.0))
+    slack = np.where(ax > 0, np.ldexp(1.0, e - 9), 0.0)
+    return float((np.maximum(np.abs(got - ref) - slack, 0) / rms).max())
+
+
+def cpu_baseline(W, budget_s=12.0):
+    """The float64 oracle (indexer -> top-k -> sink MQA) on the same inputs,
+    one decode query at a time, until the time budget is used."""
+    from oracle import formats as OF
+    from oracle import method as OM
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    inp = W["inp"]
+    c = W["c"]
+    kv = inp.kv
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = done % inp.B
+        N = int(inp.n_ent[b])
+        off = int(inp.kv_off[b])
+        keys = OF.decode_rows(inp.keys[off: off + N], csa.FP8, c["d_I"])
+        qi = OF.decode_rows(inp.q_idx[b], csa.FP8, c["d_I"])
+        I = OM.indexer_scores(qi, inp.w[b].astype(np.float64), keys)
+        sel = OM.top_k(I, c["k"])
+        ents = np.zeros((N, W["D"]))
+        ents[sel] = OF.decode_rows(kv[off + sel], csa.SPLIT, W["D"], W["R"])
+        wl = int(inp.win_len[b])
+        win = OF.decode_rows(inp.win[b, :wl], csa.BF16, W["D"])
+        q = OF.decode_rows(inp.q[b], csa.BF16, W["D"])
+        OM.decode_one(q, int(inp.q_pos[b]), ents, win, inp.sinks.astype(np.float64), inp.scale,
+                      W["m"], idx=sel, R=W["R"])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} decode queries (indexer over 16384 FP8 keys, top-512, sink MQA "
+                      f"over 512+128 entries) of the same batch in {dt:.1f} s"}
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    src = os.path.join(ROOT, "compressed_sparse_long_csa_amd", "csrc", "indexer.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        return rec["bytes_per_launch"] if rec.get("source_sha256") == h else None
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(decode shards by sequence; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    csa.load_library()
+    W = build_workload()
+    step, kernels = make_step(W, check=True)
+    step()                                   # validated eager pass
+    torch.cuda.synchronize()
+    step, kernels = make_step(W, check=False)
+    ms, _graph = time_graph(step, args.steps, args.warmup)
+    per_us = time_kernels(kernels, max(20, args.steps // 4))
+    step_bytes, kbytes = algorithmic_bytes(W)
+    err = spot_check(W)
+    B = W["B"]
+    dom = "indexer_score"
+    ach = kbytes[dom] / (per_us[dom] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8/bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) before quantisation; no weights needed)",
+        "config": {"workload": "csa_decode_b16_ctx65536", "batch": B, "context": 65536,
+                   "entries_per_seq": int(W["inp"].n_ent[0]), "top_k": W["c"]["k"],
+                   "heads": W["c"]["H"], "head_dim": W["D"], "indexer": "fp8 64x128",
+                   "window": 128, "graph": True, "variant": "auto"},
+        "hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
+        "step_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_record(dom),
+                     "kernel": dom, "bytes_per_launch": kbytes[dom], "us_per_launch": per_us[dom]},
+        "kernels_us": per_us,
+        "kernel_bytes": kbytes,
+        "check_max_err_over_rms": err,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

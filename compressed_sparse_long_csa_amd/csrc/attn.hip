@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
       const int d = lane * P + t;
       if (d >= D - R) {
         float sn, cs;
-        rope_sincos(p, (d - (D - R)) / 2, R, a.rope_base, &sn, &cs);
+        rope_sincos(p, a.rope_theta[(d - (D - R)) / 2], &sn, &cs);
         const float x0 = qh[t], x1 = qh[t + 1];
         qh[t] = x0 * cs - x1 * sn;
         qh[t + 1] = x0 * sn + x1 * cs;
@@ -135,24 +135,32 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
 constexpr int kD = 512, kR = 64, kDF8 = 448;            // dims, RoPE dims, FP8 dims
 constexpr int kRowSplit = kDF8 + 2 * kR;                // 576 bytes per cache entry
 constexpr int kRowBf16 = 2 * kD;                        // 1024 bytes per window row
+constexpr int kChunksSplit = kRowSplit / 16;            // 36 chunks of 16 bytes
+constexpr int kPitchSplit = kRowSplit + 16;             // LDS row pitch: rows land on distinct banks
+constexpr int kPitchWin = kRowBf16 + 16;
 constexpr int kTile = 64;                               // entries per tile
 constexpr int kThreads = 256;
-constexpr int kBufBytes = kTile * kRowBf16;             // raw tile buffer (largest row format)
+constexpr int kBufBytes = kTile * kPitchWin;            // raw tile buffer (largest row format)
 constexpr int kMaxK = 2048;                             // longest selected list kept in LDS
+constexpr int kPPitch8 = 72;                            // padded rows of the fp8 P arrays
+constexpr int kPPitch16 = 72;                           // padded rows (elements) of the bf16 P array
 constexpr float kPScale = 256.0f;                       // probabilities are stored x 2^8
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Raw rows land in LDS exactly as stored (split: 576-byte rows, window: 1024-byte
-// rows) through direct global->LDS loads; the kernel converts FP8 on read.
+// Raw rows land in LDS as stored (split: 576-byte rows, window: 1024-byte rows)
+// through direct global->LDS loads, one wave instruction per row, at a pitch
+// padded by 16 bytes so that neighbouring rows start on different banks.  Every
+// operand address is then a per-lane base plus a compile-time offset.
 struct __align__(16) AttnSmem {
   uint8_t raw[2][kBufBytes];       // double-buffered tiles
   int32_t sel[kMaxK];              // selected entry list (CSA), -1 where dropped
-  uint8_t phi[16][kTile];          // fp8 high part of p * 2^8   [head][entry]
-  uint8_t plo[16][kTile];          // fp8 residual
-  uint16_t pbf[16][kTile];         // bf16(p * 2^8)
+  uint8_t phi[16][kPPitch8];       // fp8 high part of p * 2^8   [head][entry]
+  uint8_t plo[16][kPPitch8];       // fp8 residual
+  uint16_t pbf[16][kPPitch16];     // bf16(p * 2^8)
   float red_max[4][16];
   float red_sum[4][16];
+  float rope_cs[kR / 2][2];        // cos, sin of the query's RoPE angles
   int valid[2][kTile];
 };
 
@@ -182,6 +190,11 @@ __device__ __forceinline__ uint32_t fp8x2(float a, float b) {
 __device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t v) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v), false);
 }
+// two floats -> packed bf16 (hardware conversion, round to nearest even)
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // 8 FP8 values (exact) -> 8 BF16 values.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(long v) {
@@ -201,30 +214,34 @@ struct Work {
   int n_list, n_ct, n_wt, win_count;
 };
 
-// Issue the direct global->LDS loads of tile `tile` into buffer `buf` and write
-// its per-row validity.  Each wave instruction moves 64 x 16 bytes into 1 KB of
-// contiguous LDS.  Rows that hold no entry get zeros (plain LDS stores) so the
-// P.V product never meets stale bits.
+// Issue the direct global->LDS loads of tile `tile` into buffer `buf` and
+// write its per-row validity.  One wave instruction moves one row (36 lanes x
+// 16 bytes for a split row, 64 lanes for a window row) to the row's padded LDS
+// slot.  Rows without an entry load a real row (entry 0 / window row 0) and
+// are masked by `valid`, so no stale bits reach P.V.
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Work& w, int tile, int buf,
                                            AttnSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint8_t* dst = sm.raw[buf];
   if (tile < w.n_ct) {
-    const uint8_t* kv = static_cast<const uint8_t*>(a.kv);
+    const uint8_t* kv = static_cast<const uint8_t*>(a.kv) + w.kv0 * kRowSplit + lane * 16;
+    // lane l < 16 looks up the entry of this wave's row 4l + wv; readlane makes it scalar
+    int my_e = 0;
+    if (lane < kTile / 4) {
+      const int pos = tile * kTile + lane * 4 + wv;
+      if (pos < w.n_list) {
+        const int e = a.idx != nullptr ? sm.sel[pos] : pos;
+        my_e = e < 0 ? 0 : e;
+      }
+    }
+    if (lane < kChunksSplit) {
 #pragma unroll
-    for (int i = 0; i < kTile * kRowSplit / 16 / kThreads; ++i) {      // 9 per thread
-      const int inst = i * 4 + wv;                                      // wave instruction id
-      const int c = inst * 64 + lane;                                   // 16-byte chunk of the tile
-      const int row = c / (kRowSplit / 16), col = c % (kRowSplit / 16);
-      const int pos = tile * kTile + row;
-      int64_t e = -1;
-      if (pos < w.n_list) e = a.idx != nullptr ? sm.sel[pos] : pos;
-      if (e >= 0) {
+      for (int i = 0; i < kTile / 4; ++i) {                             // 16 rows per wave
+        const int row = i * 4 + wv;
+        const int e = __builtin_amdgcn_readlane(my_e, i);
         __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(kv + (w.kv0 + e) * kRowSplit + col * 16),
-            (__attribute__((address_space(3))) void*)(lds_ptr(dst + inst * 1024)), 16, 0, 0);
-      } else {
-        *reinterpret_cast<uint4*>(dst + c * 16) = make_uint4(0, 0, 0, 0);
+            static_cast<const void*>(kv + static_cast<int64_t>(e) * kRowSplit),
+            (__attribute__((address_space(3))) void*)(lds_ptr(dst + row * kPitchSplit)), 16, 0, 0);
       }
     }
     if (tid < kTile) {
@@ -234,19 +251,16 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Work& w, int
       sm.valid[buf][tid] = ok;
     }
   } else {
-    const uint8_t* win = static_cast<const uint8_t*>(a.win);
+    const uint8_t* win = static_cast<const uint8_t*>(a.win) + w.win_row0 * kRowBf16 + lane * 16;
     const int wt = tile - w.n_ct;
 #pragma unroll
     for (int i = 0; i < kTile / 4; ++i) {                               // 16 rows per wave
       const int row = i * 4 + wv;
       const int j = wt * kTile + row;
-      if (j < w.win_count) {
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(win + (w.win_row0 + j) * kRowBf16 + lane * 16),
-            (__attribute__((address_space(3))) void*)(lds_ptr(dst + row * kRowBf16)), 16, 0, 0);
-      } else {
-        *reinterpret_cast<uint4*>(dst + row * kRowBf16 + lane * 16) = make_uint4(0, 0, 0, 0);
-      }
+      const int src = j < w.win_count ? j : 0;
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(win + static_cast<int64_t>(src) * kRowBf16),
+          (__attribute__((address_space(3))) void*)(lds_ptr(dst + row * kPitchWin)), 16, 0, 0);
     }
     if (tid < kTile) sm.valid[buf][tid] = wt * kTile + tid < w.win_count;
   }
@@ -283,18 +297,24 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   w.kv0 = a.kv_off[b];
   window_of(a, b, w.p, &w.win_row0, &w.win_count);
   if (a.idx != nullptr) {
-    w.n_list = a.k;
+    w.n_list = w.N > 0 ? a.k : 0;
     for (int j = tid; j < a.k; j += kThreads) {
       const int32_t e = a.idx[static_cast<int64_t>(b) * a.k + j];
       sm.sel[j] = (e >= 0 && e < w.N) ? e : -1;
     }
-    __syncthreads();
   } else {
     w.n_list = static_cast<int>(w.N);
   }
   w.n_ct = (w.n_list + kTile - 1) / kTile;
   w.n_wt = (w.win_count + kTile - 1) / kTile;
   const int n_tiles = w.n_ct + w.n_wt;
+  if (tid < kR / 2) {
+    float sn, cs;
+    rope_sincos(w.p, a.rope_theta[tid], &sn, &cs);
+    sm.rope_cs[tid][0] = cs;
+    sm.rope_cs[tid][1] = sn;
+  }
+  __syncthreads();                                      // sel[] and rope_cs ready
 
   if (n_tiles > 0) issue_tile(a, w, 0, 0, sm);
 
@@ -324,17 +344,24 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 #pragma unroll
     for (int t = 0; t < 32; ++t) x[t] = x[t] * r * (a.q_norm_w ? a.q_norm_w[c * 32 + t] : 1.0f);
     if (c * 32 >= kD - kR) {
+      const int p0 = (c * 32 - (kD - kR)) / 2;
 #pragma unroll
       for (int t = 0; t < 32; t += 2) {
-        float sn, cs;
-        rope_sincos(w.p, (c * 32 + t - (kD - kR)) / 2, kR, a.rope_base, &sn, &cs);
+        const float cs = sm.rope_cs[p0 + t / 2][0], sn = sm.rope_cs[p0 + t / 2][1];
         const float x0 = x[t], x1 = x[t + 1];
         x[t] = x0 * cs - x1 * sn;
         x[t + 1] = x0 * sn + x1 * cs;
       }
     }
 #pragma unroll
-    for (int t = 0; t < 32; ++t) qbf[h][c * 32 + t] = f32_to_bf16(x[t]);
+    for (int t = 0; t < 32; t += 8) {
+      uint4 v;
+      v.x = bf16x2_rne(x[t], x[t + 1]);
+      v.y = bf16x2_rne(x[t + 2], x[t + 3]);
+      v.z = bf16x2_rne(x[t + 4], x[t + 5]);
+      v.w = bf16x2_rne(x[t + 6], x[t + 7]);
+      *reinterpret_cast<uint4*>(&qbf[h][c * 32 + t]) = v;
+    }
   }
   __syncthreads();
   // QK operand of this lane: head j16, dims [32*ks + 8*g, +8)
@@ -364,23 +391,31 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
     const int erow = wv * 16 + j16;
     if (!is_win) {
-      const uint8_t* rowp = T + erow * kRowSplit;
+      const uint8_t* rowp = T + erow * kPitchSplit + g * 8;
+      long ka[kDF8 / 32];
 #pragma unroll
-      for (int ks = 0; ks < kDF8 / 32; ++ks) {
-        const bf16x8 av = fp8x8_to_bf16x8(lds_read_b64(rowp + ks * 32 + g * 8));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], s, 0, 0, 0);
-      }
+      for (int ks = 0; ks < kDF8 / 32; ++ks) ka[ks] = lds_read_b64(rowp + ks * 32);
+      bf16x8 kr[kR / 32];
 #pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + (ks * 32 + g * 8) * 2);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[kDF8 / 32 + ks], s, 0, 0, 0);
-      }
+      for (int ks = 0; ks < kR / 32; ++ks)
+        kr[ks] = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + g * 8 + ks * 64);
+#pragma unroll
+      for (int ks = 0; ks < kDF8 / 32; ++ks)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(ka[ks]), qb[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kR / 32; ++ks)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[kDF8 / 32 + ks], s, 0, 0, 0);
     } else {
-      const uint8_t* rowp = T + erow * kRowBf16;
+      const uint8_t* rowp = T + erow * kPitchWin + g * 16;
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(rowp + (ks * 32 + g * 8) * 2);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], s, 0, 0, 0);
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 kw[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          kw[ks] = *reinterpret_cast<const bf16x8*>(rowp + (half * 8 + ks) * 64);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[ks], qb[half * 8 + ks], s, 0, 0, 0);
       }
     }
     // lane holds head j16, entries 16*wv + 4*g + r
@@ -420,8 +455,8 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
       *reinterpret_cast<uint32_t*>(&sm.phi[j16][e0]) = h01 | (h23 << 16);
       *reinterpret_cast<uint32_t*>(&sm.plo[j16][e0]) = l01 | (l23 << 16);
       uint2 bb;
-      bb.x = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-      bb.y = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+      bb.x = bf16x2_rne(v0, v1);
+      bb.y = bf16x2_rne(v2, v3);
       *reinterpret_cast<uint2*>(&sm.pbf[j16][e0]) = bb;
     }
     __syncthreads();
@@ -438,24 +473,39 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
       const long phv = lds_read_b64(&sm.phi[j16][ebase]);
       const long plv = lds_read_b64(&sm.plo[j16][ebase]);
       const bf16x8 pbv = *reinterpret_cast<const bf16x8*>(&sm.pbf[j16][ebase]);
+      if (!is_win) {
+        // fp8 dims: lane j of group g supplies row (ebase + j/2), bytes d0 + 8*(j%2)
+        const uint8_t* b8 = T + (ebase + (j16 >> 1)) * kPitchSplit + dbase + 8 * (j16 & 1);
+        // bf16 RoPE dims: lane j supplies row (ebase + j/4), dims d0 + 4*(j%4)
+        const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchSplit + kDF8 + (dbase - kDF8) * 2 + 8 * (j16 & 3);
+        long v8[NB];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int d0 = dbase + i * 16;
-        if (!is_win && d0 < kDF8) {
-          // lane j of group g supplies row (ebase + j/2), bytes d0 + 8*(j%2)
-          const long av = tr8(T + (ebase + (j16 >> 1)) * kRowSplit + d0 + 8 * (j16 & 1));
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, phv, acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(av, plv, acc[i], 0, 0, 0);
-        } else {
-          // bf16 values: lane j supplies row (ebase + j/4), dims d0 + 4*(j%4)
-          const int pitch = is_win ? kRowBf16 : kRowSplit;
-          const int boff = is_win ? d0 * 2 : kDF8 + (d0 - kDF8) * 2;
-          const uint8_t* ap0 = T + (ebase + (j16 >> 2)) * pitch + boff + 8 * (j16 & 3);
-          const bf16x4 lo4 = tr16(ap0);
-          const bf16x4 hi4 = tr16(ap0 + 4 * pitch);
-          const bf16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv, acc[i], 0, 0, 0);
+        for (int i = 0; i < NB; ++i)
+          if (dbase + i * 16 < kDF8) v8[i] = tr8(b8 + i * 16);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if (dbase + i * 16 < kDF8) {
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], phv, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], plv, acc[i], 0, 0, 0);
+          } else {
+            const bf16x4 lo4 = tr16(b16 + i * 32);
+            const bf16x4 hi4 = tr16(b16 + i * 32 + 4 * kPitchSplit);
+            const bf16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv, acc[i], 0, 0, 0);
+          }
         }
+      } else {
+        const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchWin + dbase * 2 + 8 * (j16 & 3);
+        bf16x8 vw[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const bf16x4 lo4 = tr16(b16 + i * 32);
+          const bf16x4 hi4 = tr16(b16 + i * 32 + 4 * kPitchWin);
+          vw[i] = bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[i], pbv, acc[i], 0, 0, 0);
       }
     }
   }

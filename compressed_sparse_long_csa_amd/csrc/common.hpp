@@ -99,19 +99,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// RoPE angle pos * base^(-2i/R) reduced to [-pi, pi] in double precision, so
-// positions up to 2^24 and beyond keep full float accuracy in sin / cos.
-__device__ __forceinline__ void rope_sincos(int64_t pos, int i, int R, float base, float* s,
-                                            float* c) {
-  const double theta = exp2(-2.0 * static_cast<double>(i) / static_cast<double>(R) *
-                            log2(static_cast<double>(base)));
-  double ang = static_cast<double>(pos) * theta;
+// RoPE rotation of pair i at absolute position pos: angle = pos * theta_i with
+// theta_i = base^(-2i/R) precomputed in double on the host.  The product and
+// the reduction to [-pi, pi] run in double, so positions up to 2^24 and beyond
+// keep full float accuracy in sin / cos.
+__device__ __forceinline__ void rope_sincos(int64_t pos, double theta, float* s, float* c) {
   const double two_pi = 6.283185307179586476925286766559;
-  ang = ang - two_pi * rint(ang / two_pi);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *s = static_cast<float>(sd);
-  *c = static_cast<float>(cd);
+  const double ang = static_cast<double>(pos) * theta;
+  const double red = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);
+  sincosf(static_cast<float>(red), s, c);
+}
+
+// Host-side RoPE frequency table: theta_i = base^(-2i/R), i < R/2.
+constexpr int kMaxRopePairs = 64;
+inline void fill_rope_theta(double* theta, int R, float base) {
+  for (int i = 0; i < kMaxRopePairs; ++i)
+    theta[i] = (R > 0 && i < R / 2) ? pow(static_cast<double>(base), -2.0 * i / R) : 0.0;
 }
 
 }  // namespace csa

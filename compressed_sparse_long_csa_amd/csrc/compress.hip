@@ -23,13 +23,19 @@ __device__ __forceinline__ float load_x(const void* x, csa_fmt fmt, int64_t i) {
                         : bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
-__global__ void __launch_bounds__(kThreads)
-compress_kernel(const void* __restrict__ x, csa_fmt x_fmt, const float* __restrict__ gate,
-                int gate_cols, int64_t n_blocks, int D, int m, int nseg,
-                const int64_t* __restrict__ seg_tok_off, const int64_t* __restrict__ seg_pos0,
-                const int64_t* __restrict__ seg_out_row, int normalize,
-                const float* __restrict__ norm_w, float eps, int R, float base,
-                uint8_t* __restrict__ out, csa_fmt out_fmt) {
+__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int64_t n_blocks) {
+  const void* __restrict__ x = a.x;
+  const csa_fmt x_fmt = a.x_fmt;
+  const float* __restrict__ gate = a.gate;
+  const int gate_cols = a.gate_cols, D = a.D, m = a.m, nseg = a.nseg, normalize = a.normalize;
+  const int64_t* __restrict__ seg_tok_off = a.seg_tok_off;
+  const int64_t* __restrict__ seg_pos0 = a.seg_pos0;
+  const int64_t* __restrict__ seg_out_row = a.seg_out_row;
+  const float* __restrict__ norm_w = a.norm_w;
+  const float eps = a.eps;
+  const int R = a.rope_dim;
+  uint8_t* __restrict__ out = static_cast<uint8_t*>(a.out);
+  const csa_fmt out_fmt = a.out_fmt;
   extern __shared__ float y[];            // [D] entry values, then [kThreads/64] partials
   float* red = y + D;
   const int tid = threadIdx.x;
@@ -78,7 +84,7 @@ compress_kernel(const void* __restrict__ x, csa_fmt x_fmt, const float* __restri
     if (R > 0) {
       for (int i = tid; i < R / 2; i += kThreads) {
         float sn, cs;
-        rope_sincos(pos, i, R, base, &sn, &cs);
+        rope_sincos(pos, a.rope_theta[i], &sn, &cs);
         const int d = D - R + 2 * i;
         const float a = y[d], b = y[d + 1];
         y[d] = a * cs - b * sn;
@@ -144,9 +150,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   const int64_t grid = n_blocks < 65536 ? n_blocks : 65536;
   const size_t shm = (static_cast<size_t>(a.D) + kThreads / kWave) * sizeof(float);
   hipLaunchKernelGGL(compress_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), shm,
-                     stream, a.x, a.x_fmt, a.gate, a.gate_cols, n_blocks, a.D, a.m, a.nseg,
-                     a.seg_tok_off, a.seg_pos0, a.seg_out_row, a.normalize, a.norm_w, a.eps,
-                     a.rope_dim, a.rope_base, static_cast<uint8_t*>(a.out), a.out_fmt);
+                     stream, a, n_blocks);
   return hipGetLastError();
 }
 

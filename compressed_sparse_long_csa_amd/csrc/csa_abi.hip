@@ -81,8 +81,10 @@ csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gat
   if (!fmt_ok(out_fmt)) return fail(CSA_ERR_INVALID_ARG, "csa_compress: bad out_fmt");
   if (gate_cols != 1 && gate_cols != D)
     return fail(CSA_ERR_INVALID_ARG, "csa_compress: gate_cols must be 1 or D");
-  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_dim must be even and in [0, D]");
+  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D || rope_dim > 2 * kMaxRopePairs)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_dim must be even, <= D and <= 128");
+  if (rope_dim > 0 && !(rope_base > 0.0f))
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_base must be > 0");
   if (out_fmt == CSA_MXFP4 && D % 32 != 0)
     return fail(CSA_ERR_INVALID_ARG, "csa_compress: MXFP4 needs D %% 32 == 0");
   if (out_fmt == CSA_SPLIT && (rope_dim == 0 || D - rope_dim < 1))
@@ -93,7 +95,8 @@ csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gat
   if (!x || !gate || !seg_tok_off || !seg_pos0 || !seg_out_row || !out)
     return fail(CSA_ERR_INVALID_ARG, "csa_compress: null pointer");
   CompressArgs a{x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0, seg_out_row,
-                 normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt};
+                 normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt, {}};
+  fill_rope_theta(a.rope_theta, rope_dim, rope_base);
   return launched(launch_compress(a, stream), "csa_compress");
 }
 
@@ -134,14 +137,16 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
   return launched(launch_topk(a, stream), "topk_select");
 }
 
-static csa_status attn_common(const char* name, const AttnArgs& a, hipStream_t stream) {
+static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream) {
   if (a.nq < 0) return fail(CSA_ERR_INVALID_ARG, "%s: query count < 0", name);
   if (a.H < 1 || a.D < 2) return fail(CSA_ERR_INVALID_ARG, "%s: H, D must be positive", name);
   if (a.m < 1) return fail(CSA_ERR_INVALID_ARG, "%s: m must be >= 1", name);
   if (a.n_win < 0) return fail(CSA_ERR_INVALID_ARG, "%s: n_win < 0", name);
   if (a.idx != nullptr && a.k < 1) return fail(CSA_ERR_INVALID_ARG, "%s: k must be >= 1 with idx", name);
-  if (a.rope_dim < 0 || a.rope_dim % 2 != 0 || a.rope_dim > a.D)
-    return fail(CSA_ERR_INVALID_ARG, "%s: rope_dim must be even and in [0, D]", name);
+  if (a.rope_dim < 0 || a.rope_dim % 2 != 0 || a.rope_dim > a.D || a.rope_dim > 2 * kMaxRopePairs)
+    return fail(CSA_ERR_INVALID_ARG, "%s: rope_dim must be even, <= D and <= 128", name);
+  if (a.rope_dim > 0 && !(a.rope_base > 0.0f))
+    return fail(CSA_ERR_INVALID_ARG, "%s: rope_base must be > 0", name);
   if (!(a.eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
   if (a.variant < CSA_VARIANT_AUTO || a.variant > CSA_VARIANT_LOW_OCC)
     return fail(CSA_ERR_INVALID_ARG, "%s: bad variant", name);
@@ -168,6 +173,7 @@ static csa_status attn_common(const char* name, const AttnArgs& a, hipStream_t s
   if (!a.q || !a.q_pos || !a.kv || !a.kv_off || !a.sinks || !a.out)
     return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", name);
   if (a.n_win > 0 && !a.win) return fail(CSA_ERR_INVALID_ARG, "%s: null window pointer", name);
+  fill_rope_theta(a.rope_theta, a.rope_dim, a.rope_base);
   return launched(launch_attn(a, stream), name);
 }
 
@@ -183,7 +189,7 @@ csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
     return fail(CSA_ERR_INVALID_ARG, "hybrid_attn_decode: null win_len");
   AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt, kv_off, m,
              idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
-             scale, out, out_fmt, static_cast<int>(variant)};
+             scale, out, out_fmt, static_cast<int>(variant), {}};
   return attn_common("hybrid_attn_decode", a, stream);
 }
 
@@ -199,8 +205,7 @@ csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int 
     return fail(CSA_ERR_INVALID_ARG, "hybrid_attn_prefill: null tok_off / tok_pos0");
   AttnArgs a{q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt, kv_off, m,
              idx, k, tok, tok_fmt, n_win, n_win > 0 ? 2 : 0, nullptr, tok_off, tok_pos0, sinks,
-             scale, out, out_fmt,
-             static_cast<int>(variant)};
+             scale, out, out_fmt, static_cast<int>(variant), {}};
   return attn_common("hybrid_attn_prefill", a, stream);
 }
 

@@ -22,6 +22,7 @@ struct CompressArgs {
   const int64_t* seg_tok_off; const int64_t* seg_pos0; const int64_t* seg_out_row;
   int normalize; const float* norm_w; float eps; int rope_dim; float rope_base;
   void* out; csa_fmt out_fmt;
+  double rope_theta[kMaxRopePairs];
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
 
@@ -51,6 +52,7 @@ struct AttnArgs {
   const int32_t* win_len;                               // decode
   const int64_t* tok_off; const int64_t* tok_pos0;      // prefill
   const float* sinks; float scale; void* out; csa_fmt out_fmt; int variant;
+  double rope_theta[kMaxRopePairs];
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

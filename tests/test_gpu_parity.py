@@ -176,6 +176,32 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
         assert np.all(np.isneginf(gs[i, c:]))
 
 
+@pytest.mark.parametrize("case", ["all_equal", "two_levels", "with_inf", "huge_range", "negatives"])
+def test_topk_edge_rows(case):
+    rng = np.random.default_rng(5)
+    nq, ld, k = 3, 20000, 512
+    if case == "all_equal":
+        s = np.full((nq, ld), 1.5, np.float32)
+    elif case == "two_levels":
+        s = np.where(rng.random((nq, ld)) < 0.01, 2.0, 1.0).astype(np.float32)
+    elif case == "with_inf":
+        s = rng.standard_normal((nq, ld)).astype(np.float32)
+        s[:, ::97] = -np.inf
+        s[0, 5:300] = np.inf
+    elif case == "huge_range":
+        s = (rng.standard_normal((nq, ld)) * 10.0 ** rng.integers(-30, 30, (nq, ld))).astype(np.float32)
+    else:
+        s = -np.abs(rng.standard_normal((nq, ld))).astype(np.float32)
+    nv = np.array([ld, 777, 513], np.int64)
+    idx = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(dev(s), ld, nq, dev(nv), k, idx)
+    got = idx.cpu().numpy()
+    for i in range(nq):
+        want = OM.top_k(s[i, : nv[i]].astype(np.float64), k)
+        assert np.array_equal(got[i, : len(want)], want), f"{case} row {i}"
+        assert np.all(got[i, len(want):] == -1)
+
+
 # ------------------------------------------------------------------ attention
 def _decode_case(cfg, lengths, seed, csa_mode):
     c = synth.CONFIGS[cfg]
