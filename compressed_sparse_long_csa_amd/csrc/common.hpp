@@ -85,6 +85,19 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
   return (c & 8u) ? -v : v;
 }
 
+// ------------------------------------------------------------------ raw buffer loads
+// A buffer descriptor over [base, base + bytes): a load whose byte offset is
+// at or past `bytes` returns 0 without touching memory (the buffer range
+// check), so ragged tails need neither a branch nor a clamped address.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_load_u32(buf_rsrc r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0);
+}
+
 // ------------------------------------------------------------------ wave reductions
 // Butterfly over the 64 lanes; the order of operations is fixed by the lane
 // pattern, so every lane ends with the same bits on every run.

@@ -130,7 +130,8 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
                        int32_t* idx, float* top_scores, hipStream_t stream) {
   if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "topk_select: nq < 0");
   if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "topk_select: k must be in [1, 4096]");
-  if (ld < 1) return fail(CSA_ERR_INVALID_ARG, "topk_select: ld must be >= 1");
+  if (ld < 1 || ld > (int64_t{1} << 28))
+    return fail(CSA_ERR_INVALID_ARG, "topk_select: ld must be in [1, 2^28]");
   if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
   if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "topk_select: null pointer");
   TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};

@@ -8,24 +8,27 @@
 //
 // One workgroup of 1024 threads (16 waves) per row.  Wave w owns the contiguous
 // range [w*C, (w+1)*C) of the row and reads it 64 consecutive scores at a time
-// (coalesced).  Scores map to order-preserving 32-bit keys.
-//  1. min / max of the finite scores;
-//  2. a 2048-bin histogram linear in the score value over [min, max]
-//     (monotone float binning; LDS integer atomics are order-free) gives the
-//     bin b* holding the k-th largest score and `need`, the number of its
-//     elements that are selected;
-//  3. one pass collects the elements of b* (key, index) into LDS and counts,
-//     per wave, the elements of higher bins;
-//  4. among the candidates the threshold key T and the number of elements
-//     equal to T to take (lowest indices first) are found exactly: by direct
+// (coalesced).  Scores are canonicalised on load (-0 -> +0, NaN -> -inf); slots
+// past the end of the row hold NaN, which no comparison selects.
+//  1. the first pass finds min / max of the finite scores (and, for rows of
+//     up to kStageMax scores, keeps the row in LDS for the later passes);
+//  2. a 2048-bin histogram linear in the score over [min, max] (monotone
+//     float binning; LDS integer atomics are order-free) gives the bin b*
+//     holding the k-th largest score and `need`, the number of its elements
+//     that are selected;
+//  3. one pass appends the elements of b* (order key, index) to an LDS list
+//     and counts, per wave, the elements of higher bins;
+//  4. among the candidates the threshold T and the number of elements equal
+//     to T to take (lowest indices first) are found exactly: by direct
 //     ranking for few candidates, else by key-space histograms over the LDS
-//     list (bins of power-of-two width) -- rows whose b* is too large to keep
-//     refine over the row itself;
-//  5. per-wave counts give each wave its output offset and every wave writes
-//     its indices in order with ballot prefix counts.
-// The result is the exact set, ascending, whatever the batch or launch.
-// Rows of up to 16384 scores stay in registers; longer rows are re-read from
-// memory (L2), in batches of independent loads.
+//     list (bins of power-of-two width) -- a b* too large to keep refines
+//     over the row itself;
+//  5. every wave writes its selected indices in order: a running count plus
+//     the ballot prefix count of each 64-score step.
+// Wave reductions and scans use DPP row operations and lane reads, so a block
+// reduction costs one barrier.  The result is the exact set, ascending,
+// whatever the batch or launch.  Loads and stores go through buffer
+// descriptors, so slots past a row's end need neither branches nor clamps.
 #include "kernels.hpp"
 
 namespace csa {
@@ -35,11 +38,14 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
-constexpr int kMaxJ = 16;                  // 64-element steps per wave kept in registers
-constexpr int kBinsPerThread = kBins / kThreads;
-constexpr int kMaxCand = 4096;             // candidates kept in LDS
-constexpr int kRankDirect = 512;           // candidates ranked by direct counting
+constexpr int kStreamJ = 8;                // independent loads per streamed step
+constexpr int kLdsJ = 4;                   // LDS reads per staged step
+constexpr int kMaxCand = 2048;             // candidates kept in LDS
+constexpr int kRankDirect = 96;            // candidates ranked by direct counting
+constexpr uint32_t kStageMax = 33 * 1024;  // rows staged in LDS (wave ranges included)
+constexpr uint32_t kStageSlack = 64 * (kLdsJ - 1);
 
+// Order-preserving key of a canonical (non-NaN, no -0) float, and back.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -47,199 +53,241 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
+__device__ __forceinline__ float canon(float v) { return v == v ? v + 0.0f : -INFINITY; }
+
+// ---------------------------------------------------------------- DPP wave ops
+// update_dpp with old = identity: lanes whose source lies outside the row (or
+// whose row is masked off) receive the identity.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ uint32_t dpp(uint32_t v, uint32_t identity) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(identity),
+                                                           static_cast<int>(v), Ctrl, RowMask,
+                                                           0xf, false));
+}
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele shifts inside each
+// 16-lane row, then the row totals carried by the row broadcasts.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<0x111, 0xf>(v, 0u);      // row_shr:1
+  v += dpp<0x112, 0xf>(v, 0u);      // row_shr:2
+  v += dpp<0x114, 0xf>(v, 0u);      // row_shr:4
+  v += dpp<0x118, 0xf>(v, 0u);      // row_shr:8
+  v += dpp<0x142, 0xa>(v, 0u);      // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xc>(v, 0u);      // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_total(uint32_t v) {
+  return lane_read(wave_incl_scan(v), 63);
+}
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = umin(v, dpp<0x111, 0xf>(v, 0xffffffffu));
+  v = umin(v, dpp<0x112, 0xf>(v, 0xffffffffu));
+  v = umin(v, dpp<0x114, 0xf>(v, 0xffffffffu));
+  v = umin(v, dpp<0x118, 0xf>(v, 0xffffffffu));
+  return umin(umin(lane_read(v, 15), lane_read(v, 31)), umin(lane_read(v, 47), lane_read(v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = umax(v, dpp<0x111, 0xf>(v, 0u));
+  v = umax(v, dpp<0x112, 0xf>(v, 0u));
+  v = umax(v, dpp<0x114, 0xf>(v, 0u));
+  v = umax(v, dpp<0x118, 0xf>(v, 0u));
+  return umax(umax(lane_read(v, 15), lane_read(v, 31)), umax(lane_read(v, 47), lane_read(v, 63)));
+}
+// Position of this lane among the set lanes of `mask` below it.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
 
 struct TopkSmem {
   uint32_t hist[kBins];
   uint32_t cand_key[kMaxCand];
   uint32_t cand_idx[kMaxCand];
-  uint32_t wgt[kWaves];            // per wave: selected elements with key > T
-  uint32_t weq[kWaves];            // per wave: elements with key == T
-  uint32_t wred[kWaves];
-  uint32_t wred2[kWaves];
-  uint32_t sh[8];
+  uint32_t wa[kWaves];             // per wave: elements with key > T
+  uint32_t wb[kWaves];             // per wave: elements with key == T
+  uint32_t wlo[kWaves];
+  uint32_t whi[kWaves];
+  uint32_t sh[4];                  // 0 bin, 1 above, 2 n_cand, 3 T
 };
 
+// Block min / max of per-thread keys (one barrier; the caller's next barrier
+// must precede any reuse of wlo / whi).
 __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, TopkSmem& sm) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t a = __shfl_xor(lo, o, 64), b = __shfl_xor(hi, o, 64);
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    sm.wred[threadIdx.x >> 6] = lo;
-    sm.wred2[threadIdx.x >> 6] = hi;
-  }
+  const int wv = threadIdx.x >> 6;
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if ((threadIdx.x & 63) == 0) { sm.wlo[wv] = lo; sm.whi[wv] = hi; }
   __syncthreads();
   lo = 0xffffffffu;
   hi = 0u;
-  for (int w = 0; w < kWaves; ++w) {
-    lo = sm.wred[w] < lo ? sm.wred[w] : lo;
-    hi = sm.wred2[w] > hi ? sm.wred2[w] : hi;
-  }
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) { lo = umin(lo, sm.wlo[w]); hi = umax(hi, sm.whi[w]); }
 }
 
-// Bin b with above(b) < need <= above(b) + hist[b], counting from the top bin.
-// Thread t owns the kBinsPerThread bins just below 2047 - kBinsPerThread * t.
+// Bin b with above(b) < need <= above(b) + hist[b], counting from the top
+// bin; needs the histogram published by a barrier and need <= its total.
+// Thread t owns bins 2047 - 2t and 2046 - 2t.
 __device__ __forceinline__ void find_bin(TopkSmem& sm, uint32_t need, uint32_t* bin,
                                          uint32_t* above) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int top = kBins - 1 - kBinsPerThread * tid;
-  uint32_t c[kBinsPerThread], own = 0u;
-#pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) { c[i] = sm.hist[top - i]; own += c[i]; }
-  uint32_t incl = own;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int top = kBins - 1 - 2 * tid;
+  const uint32_t c0 = sm.hist[top], c1 = sm.hist[top - 1];
+  const uint32_t incl = wave_incl_scan(c0 + c1);
+  if (lane == 63) sm.wlo[wv] = incl;
   __syncthreads();
-  if (lane == 63) sm.wred[wv] = incl;
-  __syncthreads();
-  uint32_t run = incl - own;
-  for (int w = 0; w < wv; ++w) run += sm.wred[w];
+  uint32_t run = incl - c0 - c1;
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) {
-    if (run < need && need <= run + c[i]) { sm.sh[0] = top - i; sm.sh[1] = run; }
-    run += c[i];
-  }
+  for (int w = 0; w < kWaves; ++w) run += w < wv ? sm.wlo[w] : 0u;
+  if (run < need && need <= run + c0) { sm.sh[0] = top; sm.sh[1] = run; }
+  if (run + c0 < need && need <= run + c0 + c1) { sm.sh[0] = top - 1; sm.sh[1] = run + c0; }
   __syncthreads();
   *bin = sm.sh[0];
   *above = sm.sh[1];
 }
 
-// Key-space refinement of [lo, hi] (all keys inside are candidates) over a
-// list of candidate keys: returns T and need (elements equal to T to take).
-template <typename KeyFn>
-__device__ __forceinline__ void refine(TopkSmem& sm, uint32_t lo, uint32_t hi, uint32_t need,
-                                       int count, KeyFn key_of, uint32_t* T, uint32_t* need_eq) {
-  const int tid = threadIdx.x;
-  while (lo != hi) {
-    const uint32_t span = hi - lo;
-    const int shift = span < kBins ? 0 : (32 - __clz(span)) - 11;
-    for (int b = tid; b < kBins; b += kThreads) sm.hist[b] = 0u;
-    __syncthreads();
-    for (int i = tid; i < count; i += kThreads) {
-      const uint32_t key = key_of(i);
-      if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> shift], 1u);
-    }
-    __syncthreads();
-    uint32_t b2, ab2;
-    find_bin(sm, need, &b2, &ab2);
-    need -= ab2;
-    const uint32_t nlo = lo + (b2 << shift);
-    const uint32_t nhi = (span >> shift) == b2 ? hi : nlo + ((1u << shift) - 1u);
-    lo = nlo;
-    hi = nhi;
-    __syncthreads();
-  }
-  *T = lo;
-  *need_eq = need;
-}
+// Row access.  Staged rows: the first pass copies the canonical scores into
+// LDS (vals[e] for element e) and every later pass reads them there.
+// Streamed rows: every pass re-reads the scores, kStreamJ steps at a time.
+template <bool kStaged>
+struct Row {
+  buf_rsrc rs;      // the row's n scores
+  uint32_t n;       // valid scores
+  uint32_t w0;      // first element of this wave
+  uint32_t nj;      // 64-element steps per wave
+  uint32_t lane;
+  float* vals;      // LDS copy of the row (staged rows)
 
-template <bool kInRegs>
-__device__ void topk_row(const TopkArgs& a, int row, int64_t n, TopkSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float* s = a.scores + static_cast<int64_t>(row) * a.ld;
-  int32_t* out = a.idx + static_cast<int64_t>(row) * a.k;
-  float* out_s = a.top_scores ? a.top_scores + static_cast<int64_t>(row) * a.k : nullptr;
-  const uint32_t k = static_cast<uint32_t>(a.k);
-  // wave range: C elements, a multiple of 64
-  const int64_t C = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;
-  const int64_t w0 = wv * C;
-  const int nj = kInRegs ? kMaxJ : static_cast<int>(C / 64);
-  auto elem = [&](int j) -> int64_t { return w0 + static_cast<int64_t>(j) * 64 + lane; };
-  auto valid = [&](int j) -> bool { return static_cast<int64_t>(j) * 64 < C && elem(j) < n; };
-
-  // Visits every element of this lane: f(j, key).  In-register rows loop over a
-  // compile-time count; streamed rows load 8 independent scores per step.
-  uint32_t reg[kInRegs ? kMaxJ : 1];
-  if (kInRegs) {
-#pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) reg[j] = valid(j) ? order_key(s[elem(j)]) : 0u;
+  __device__ __forceinline__ uint32_t elem(uint32_t j) const { return w0 + 64u * j + lane; }
+  __device__ __forceinline__ float load(uint32_t j) const {
+    const uint32_t e = elem(j);
+    const float v = canon(__uint_as_float(buf_load_u32(rs, 4u * e)));
+    return (j < nj && e < n) ? v : __builtin_nanf("");
   }
-  auto for_each = [&](auto&& f) {
-    if (kInRegs) {
+  // First pass: f(j, v) for every slot of this lane; staged rows also keep the
+  // scores in LDS.
+  template <typename F>
+  __device__ __forceinline__ void stage(F&& f) const {
+#pragma unroll 1
+    for (uint32_t j0 = 0; j0 < nj; j0 += kStreamJ) {
+      float vb[kStreamJ];
 #pragma unroll
-      for (int j = 0; j < kMaxJ; ++j)
-        if (valid(j)) f(j, reg[j]);
-    } else {
-      for (int j0 = 0; j0 < nj; j0 += 8) {
-        uint32_t kb[8];
+      for (int u = 0; u < kStreamJ; ++u) vb[u] = load(j0 + u);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kb[u] = valid(j0 + u) ? order_key(s[elem(j0 + u)]) : 0u;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (valid(j0 + u)) f(j0 + u, kb[u]);
+      for (int u = 0; u < kStreamJ; ++u) {
+        if (kStaged && j0 + u < nj) vals[elem(j0 + u)] = vb[u];
+        f(j0 + u, vb[u]);
       }
     }
-  };
+  }
+  // Later passes: f(j, v) for every slot of this lane.
+  template <typename F>
+  __device__ __forceinline__ void visit(F&& f) const {
+    if (kStaged) {
+#pragma unroll 1
+      for (uint32_t j0 = 0; j0 < nj; j0 += kLdsJ) {
+        float vb[kLdsJ];
+#pragma unroll
+        for (int u = 0; u < kLdsJ; ++u) vb[u] = vals[elem(j0 + u)];   // slack covers the overrun
+#pragma unroll
+        for (int u = 0; u < kLdsJ; ++u) f(j0 + u, j0 + u < nj ? vb[u] : __builtin_nanf(""));
+      }
+    } else {
+      stage(f);
+    }
+  }
+};
 
-  uint32_t T = 0u, need_eq = 0u;
-  const bool take_all = n <= static_cast<int64_t>(k);
+template <bool kStaged>
+__device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n, uint32_t C,
+                                         TopkSmem& sm, float* vals) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const buf_rsrc out_rs = make_rsrc(a.idx + static_cast<int64_t>(row) * a.k, 4u * k);
+  const bool want_s = a.top_scores != nullptr;
+  const buf_rsrc outs_rs =
+      make_rsrc(want_s ? a.top_scores + static_cast<int64_t>(row) * a.k : nullptr, want_s ? 4u * k : 0u);
+
+  Row<kStaged> r;
+  r.rs = make_rsrc(a.scores + static_cast<int64_t>(row) * a.ld, 4u * n);
+  r.n = n;
+  r.w0 = static_cast<uint32_t>(wv) * C;
+  r.nj = C / 64u;
+  r.lane = static_cast<uint32_t>(lane);
+  r.vals = vals;
+  for (int b = tid; b < kBins; b += kThreads) sm.hist[b] = 0u;
+  if (tid == 0) sm.sh[2] = 0u;
+
+  const bool take_all = n <= k;
+  float Tv = -INFINITY;             // selected: v > Tv, plus the first need_eq with v == Tv
+  uint32_t need_eq = 0u;
   if (take_all) {
-    uint32_t cnt = 0u;
-    for_each([&](int, uint32_t) { ++cnt; });
-    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-    if (lane == 0) { sm.wgt[wv] = cnt; sm.weq[wv] = 0u; }
+    r.stage([&](uint32_t, float) __attribute__((always_inline)) {});
+    if (lane == 0) {
+      sm.wa[wv] = umin(r.w0 + C, n) - umin(r.w0, n);
+      sm.wb[wv] = 0u;
+    }
     __syncthreads();
   } else {
-    // ---- 1. value range of the finite scores
-    const uint32_t kNegInf = order_key(-INFINITY), kPosInf = order_key(INFINITY);
+    // ---- 1. value range of the finite scores (its barrier also publishes the zeroed histogram)
     uint32_t lo = 0xffffffffu, hi = 0u;
-    for_each([&](int, uint32_t key) {
-      if (key != kNegInf && key != kPosInf) {
-        lo = key < lo ? key : lo;
-        hi = key > hi ? key : hi;
-      }
+    r.stage([&](uint32_t, float v) __attribute__((always_inline)) {
+      const bool fin = __builtin_isfinite(v);
+      const uint32_t key = order_key(v);
+      lo = fin ? umin(lo, key) : lo;
+      hi = fin ? umax(hi, key) : hi;
     });
     block_minmax(lo, hi, sm);
-    float vlo = 0.0f, sc = 0.0f;
+    // bin(v) = floor((v - vlo) * sc) clamped to [0, 2047]: monotone in v, never NaN
+    // for a valid v (v - vlo is finite or +-inf; 0 < sc <= FLT_MAX)
+    float vlo = 0.0f, sc = 1.0f;
     if (lo <= hi) {
       vlo = key_value(lo);
       const float width = key_value(hi) - vlo;
-      sc = (width > 0.0f && width < INFINITY) ? static_cast<float>(kBins) / width : 0.0f;
+      sc = width > 0.0f ? fminf(static_cast<float>(kBins) / width, 3.4028234663852886e38f) : 1.0f;
+      if (width == INFINITY) sc = static_cast<float>(kBins) / 3.4028234663852886e38f;
     }
-    // monotone in the key: -inf -> 0, +inf -> top bin, finite values linear in value
-    auto bin1 = [&](uint32_t key) -> uint32_t {
-      if (key <= kNegInf) return 0u;
-      if (key >= kPosInf) return kBins - 1;
-      const int b = static_cast<int>((key_value(key) - vlo) * sc);
-      return static_cast<uint32_t>(b < 0 ? 0 : (b > kBins - 1 ? kBins - 1 : b));
+    auto bin_of = [&](float v) __attribute__((always_inline)) -> uint32_t {
+      return static_cast<uint32_t>(__builtin_amdgcn_fmed3f((v - vlo) * sc, 0.0f, kBins - 1.0f));
     };
     // ---- 2. value histogram
-    for (int b = tid; b < kBins; b += kThreads) sm.hist[b] = 0u;
-    if (tid == 0) sm.sh[2] = 0u;
-    __syncthreads();
-    for_each([&](int, uint32_t key) { atomicAdd(&sm.hist[bin1(key)], 1u); });
+    r.visit([&](uint32_t, float v) __attribute__((always_inline)) {
+      if (v == v) atomicAdd(&sm.hist[bin_of(v)], 1u);
+    });
     __syncthreads();
     uint32_t bstar, above;
     find_bin(sm, k, &bstar, &above);
     const uint32_t need = k - above;
     const uint32_t cnt = sm.hist[bstar];
     // ---- 3. candidates of b* to LDS, per-wave counts of higher bins
-    uint32_t c_above = 0u;
-    lo = 0xffffffffu;
-    hi = 0u;
     const bool keep = cnt <= kMaxCand;
-    for_each([&](int j, uint32_t key) {
-      const uint32_t b = bin1(key);
-      c_above += b > bstar ? 1u : 0u;
-      if (b == bstar) {
-        lo = key < lo ? key : lo;
-        hi = key > hi ? key : hi;
-        if (keep) {
-          const uint32_t slot = atomicAdd(&sm.sh[2], 1u);
-          sm.cand_key[slot] = key;
-          sm.cand_idx[slot] = static_cast<uint32_t>(elem(j));
+    uint32_t c_above = 0u;
+    r.visit([&](uint32_t j, float v) __attribute__((always_inline)) {
+      const bool ok = v == v;
+      const uint32_t b = bin_of(v);
+      c_above += (ok && b > bstar) ? 1u : 0u;
+      const uint64_t mc = __ballot(ok && b == bstar);
+      if (keep && mc != 0ull) {
+        uint32_t base = 0u;
+        if (lanes_below(mc) == 0u && ((mc >> lane) & 1ull))
+          base = atomicAdd(&sm.sh[2], static_cast<uint32_t>(__popcll(mc)));
+        base = lane_read(base, __builtin_ctzll(mc));
+        if ((mc >> lane) & 1ull) {
+          const uint32_t slot = base + lanes_below(mc);
+          sm.cand_key[slot] = order_key(v);
+          sm.cand_idx[slot] = r.elem(j);
         }
       }
     });
-    for (int o = 32; o >= 1; o >>= 1) c_above += __shfl_xor(c_above, o, 64);
-    if (lane == 0) { sm.wgt[wv] = c_above; sm.weq[wv] = 0u; }
-    block_minmax(lo, hi, sm);              // key range of b*; its barriers publish the lists
+    c_above = wave_total(c_above);
+    if (lane == 0) { sm.wa[wv] = c_above; sm.wb[wv] = 0u; }
+    __syncthreads();
     // ---- 4. exact threshold among the candidates
+    uint32_t T;
     if (keep && cnt <= kRankDirect) {
       if (tid < static_cast<int>(cnt)) {
         const uint32_t ck = sm.cand_key[tid], ci = sm.cand_idx[tid];
@@ -252,24 +300,46 @@ __device__ void topk_row(const TopkArgs& a, int row, int64_t n, TopkSmem& sm) {
       }
       __syncthreads();
       T = sm.sh[3];
-      // elements equal to T ranked above the threshold candidate are selected
       uint32_t gt = 0u;
       for (uint32_t j = 0; j < cnt; ++j) gt += sm.cand_key[j] > T ? 1u : 0u;
       need_eq = need - gt;
-    } else if (keep) {
-      refine(sm, lo, hi, need, static_cast<int>(cnt), [&](int i) { return sm.cand_key[i]; }, &T,
-             &need_eq);
     } else {
-      // a huge b* (e.g. massive ties): refine over the row itself
+      // key range of b*, then key-space refinement of it over the LDS list or,
+      // for a b* too large to keep, over the row itself
+      lo = 0xffffffffu;
+      hi = 0u;
+      if (keep) {
+        for (int i = tid; i < static_cast<int>(cnt); i += kThreads) {
+          lo = umin(lo, sm.cand_key[i]);
+          hi = umax(hi, sm.cand_key[i]);
+        }
+      } else {
+        r.visit([&](uint32_t, float v) __attribute__((always_inline)) {
+          const bool in = v == v && bin_of(v) == bstar;
+          lo = in ? umin(lo, order_key(v)) : lo;
+          hi = in ? umax(hi, order_key(v)) : hi;
+        });
+      }
+      block_minmax(lo, hi, sm);
+      // (each pass narrows the span by 2^11, so three passes reach one key)
       uint32_t l2 = lo, h2 = hi, nd = need;
-      while (l2 != h2) {
+      for (int pass = 0; pass < 4 && l2 != h2; ++pass) {
         const uint32_t span = h2 - l2;
         const int shift = span < kBins ? 0 : (32 - __clz(span)) - 11;
+        __syncthreads();
         for (int b = tid; b < kBins; b += kThreads) sm.hist[b] = 0u;
         __syncthreads();
-        for_each([&](int, uint32_t key) {
-          if (key >= l2 && key <= h2) atomicAdd(&sm.hist[(key - l2) >> shift], 1u);
-        });
+        if (keep) {
+          for (int i = tid; i < static_cast<int>(cnt); i += kThreads) {
+            const uint32_t key = sm.cand_key[i];
+            if (key >= l2 && key <= h2) atomicAdd(&sm.hist[(key - l2) >> shift], 1u);
+          }
+        } else {
+          r.visit([&](uint32_t, float v) __attribute__((always_inline)) {
+            const uint32_t key = order_key(v);
+            if (v == v && key >= l2 && key <= h2) atomicAdd(&sm.hist[(key - l2) >> shift], 1u);
+          });
+        }
         __syncthreads();
         uint32_t b2, ab2;
         find_bin(sm, nd, &b2, &ab2);
@@ -278,94 +348,111 @@ __device__ void topk_row(const TopkArgs& a, int row, int64_t n, TopkSmem& sm) {
         const uint32_t nhi = (span >> shift) == b2 ? h2 : nlo + ((1u << shift) - 1u);
         l2 = nlo;
         h2 = nhi;
-        __syncthreads();
       }
       T = l2;
       need_eq = nd;
+      // per-wave counts of b*'s elements above / equal to T
+      if (!keep) {
+        uint32_t g = 0u, e = 0u;
+        r.visit([&](uint32_t, float v) __attribute__((always_inline)) {
+          const uint32_t key = order_key(v);
+          const bool in = v == v && key >= lo && key <= hi;
+          g += (in && key > T) ? 1u : 0u;
+          e += (in && key == T) ? 1u : 0u;
+        });
+        g = wave_total(g);
+        e = wave_total(e);
+        if (lane == 0) { sm.wa[wv] += g; sm.wb[wv] += e; }
+      }
     }
-    // per-wave counts of b*'s elements above / equal to T
     if (keep) {
       for (int i = tid; i < static_cast<int>(cnt); i += kThreads) {
         const uint32_t key = sm.cand_key[i];
-        const int w = static_cast<int>(static_cast<int64_t>(sm.cand_idx[i]) / C);
-        if (key > T) atomicAdd(&sm.wgt[w], 1u);
-        else if (key == T) atomicAdd(&sm.weq[w], 1u);
+        const uint32_t w = sm.cand_idx[i] / C;
+        if (key > T) atomicAdd(&sm.wa[w], 1u);
+        else if (key == T) atomicAdd(&sm.wb[w], 1u);
       }
-    } else {
-      uint32_t g = 0u, e = 0u;
-      for_each([&](int, uint32_t key) {
-        if (key >= lo && key <= hi) { g += key > T ? 1u : 0u; e += key == T ? 1u : 0u; }
-      });
-      for (int o = 32; o >= 1; o >>= 1) { g += __shfl_xor(g, o, 64); e += __shfl_xor(e, o, 64); }
-      if (lane == 0) { atomicAdd(&sm.wgt[wv], g); atomicAdd(&sm.weq[wv], e); }
     }
+    Tv = key_value(T);
     __syncthreads();
   }
 
   // ---- 5. ordered writes
   uint32_t gt_before = 0u, eq_before = 0u, total_gt = 0u, total_eq = 0u;
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    if (w < wv) { gt_before += sm.wgt[w]; eq_before += sm.weq[w]; }
-    total_gt += sm.wgt[w];
-    total_eq += sm.weq[w];
+    const uint32_t ga = sm.wa[w], gb = sm.wb[w];
+    gt_before += w < wv ? ga : 0u;
+    eq_before += w < wv ? gb : 0u;
+    total_gt += ga;
+    total_eq += gb;
   }
-  const unsigned long long lm = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  auto emit = [&](int j, bool gt, bool eq) {
-    const unsigned long long mg = __ballot(gt), me = __ballot(eq);
-    const uint32_t gp = gt_before + static_cast<uint32_t>(__popcll(mg & lm));
-    const uint32_t ep = eq_before + static_cast<uint32_t>(__popcll(me & lm));
-    if (gt || (eq && ep < need_eq)) {
-      const uint32_t pos = gp + (ep < need_eq ? ep : need_eq);
-      if (pos < k) {
-        const int64_t e = elem(j);
-        out[pos] = static_cast<int32_t>(e);
-        if (out_s) out_s[pos] = s[e];
+  uint32_t sel_before = gt_before + umin(eq_before, need_eq);
+  r.visit([&](uint32_t j, float v) __attribute__((always_inline)) {
+    const bool gt = take_all ? v == v : v > Tv;
+    uint64_t ms = __ballot(gt);
+    bool sel = gt;
+    if (!take_all) {
+      const uint64_t me = __ballot(v == Tv);
+      if (me != 0ull) {                       // rare: scores equal to the threshold
+        const bool eq_take = v == Tv && eq_before + lanes_below(me) < need_eq;
+        ms |= __ballot(eq_take);
+        sel = sel || eq_take;
+        eq_before += static_cast<uint32_t>(__popcll(me));
       }
     }
-    gt_before += static_cast<uint32_t>(__popcll(mg));
-    eq_before += static_cast<uint32_t>(__popcll(me));
-  };
-  if (kInRegs) {
-#pragma unroll
-    for (int j = 0; j < kMaxJ; ++j) {
-      const bool v = valid(j);
-      const uint32_t key = reg[j];
-      emit(j, v && (take_all || key > T), v && !take_all && key == T);
-    }
-  } else {
-    for (int j0 = 0; j0 < nj; j0 += 8) {
-      uint32_t kb[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) kb[u] = valid(j0 + u) ? order_key(s[elem(j0 + u)]) : 0u;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool v = valid(j0 + u);
-        emit(j0 + u, v && (take_all || kb[u] > T), v && !take_all && kb[u] == T);
+    if (ms != 0ull) {
+      const uint32_t pos = sel_before + lanes_below(ms);
+      if (sel) {
+        __builtin_amdgcn_raw_buffer_store_b32(r.elem(j), out_rs, static_cast<int>(4u * pos), 0, 0);
+        if (want_s)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outs_rs,
+                                                static_cast<int>(4u * pos), 0, 0);
       }
+      sel_before += static_cast<uint32_t>(__popcll(ms));
     }
-  }
-  const uint32_t sel = total_gt + (total_eq < need_eq ? total_eq : need_eq);
-  const uint32_t total = sel < k ? sel : k;
+  });
+  const uint32_t total = umin(total_gt + umin(total_eq, need_eq), k);
   for (uint32_t j = total + tid; j < k; j += kThreads) {
-    out[j] = -1;
-    if (out_s) out_s[j] = -INFINITY;
+    __builtin_amdgcn_raw_buffer_store_b32(0xffffffffu, out_rs, static_cast<int>(4u * j), 0, 0);
+    if (want_s)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), outs_rs,
+                                            static_cast<int>(4u * j), 0, 0);
   }
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, uint32_t cap) {
   __shared__ TopkSmem sm;
+  extern __shared__ float vals[];            // cap + kStageSlack scores
   const int row = blockIdx.x;
   int64_t n = a.n_valid ? a.n_valid[row] : a.ld;
   n = n < 0 ? 0 : (n > a.ld ? a.ld : n);
-  if (n <= static_cast<int64_t>(kWaves) * 64 * kMaxJ) topk_row<true>(a, row, n, sm);
-  else topk_row<false>(a, row, n, sm);
+  const uint32_t nn = static_cast<uint32_t>(n);
+  const uint32_t C = ((nn + kWaves - 1) / kWaves + 63u) / 64u * 64u;
+  if (kWaves * C <= cap) topk_row<true>(a, row, nn, C, sm, vals);
+  else topk_row<false>(a, row, nn, C, sm, vals);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), 0, stream, a);
+  const uint64_t cmax = (static_cast<uint64_t>(a.ld) + kWaves - 1) / kWaves;
+  const uint64_t need = kWaves * ((cmax + 63) / 64 * 64);
+  const uint32_t cap = need <= kStageMax ? static_cast<uint32_t>(need) : 0u;
+  const size_t shm = cap ? (static_cast<size_t>(cap) + kStageSlack) * sizeof(float) : 0;
+  static thread_local int configured_dev = -1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (configured_dev != dev) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>((kStageMax + kStageSlack) * sizeof(float)));
+    if (e != hipSuccess) return e;
+    configured_dev = dev;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), shm, stream, a, cap);
   return hipGetLastError();
 }
 

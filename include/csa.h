@@ -168,7 +168,8 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
  * not be NaN.  n_valid is clamped to [0, ld] on the device.
  *
  *   scores  [nq, ld] float32;  idx [nq, k] int32;  top_scores [nq, k] or NULL
- * Errors: INVALID_ARG for k < 1, k > 4096, ld < 1, nq < 0, null pointers.
+ * Errors: INVALID_ARG for k < 1, k > 4096, ld < 1, ld > 2^28, nq < 0,
+ * null pointers.
  */
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
                        int32_t* idx, float* top_scores, hipStream_t stream);

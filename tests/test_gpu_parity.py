@@ -155,6 +155,7 @@ def test_indexer_matches_oracle(fmt, H_I, d_I, lengths):
 @pytest.mark.parametrize("ld,k,tie_levels,n_valid", [
     (16384, 512, 0, None), (16384, 512, 5, None), (5000, 1024, 0, [5000, 4999, 1024, 1000, 1, 0]),
     (262144, 1024, 0, [262144, 100000]), (3000, 64, 3, [3000, 64, 65, 2]), (70000, 2048, 0, None),
+    (33792, 1024, 0, [33792, 33000, 20000]), (34000, 1024, 2, [34000, 33792, 4097]),
 ])
 def test_topk_exact(ld, k, tie_levels, n_valid):
     nq = len(n_valid) if n_valid else 4
@@ -176,10 +177,11 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
         assert np.all(np.isneginf(gs[i, c:]))
 
 
+@pytest.mark.parametrize("ld", [20000, 40000])
 @pytest.mark.parametrize("case", ["all_equal", "two_levels", "with_inf", "huge_range", "negatives"])
-def test_topk_edge_rows(case):
+def test_topk_edge_rows(case, ld):
     rng = np.random.default_rng(5)
-    nq, ld, k = 3, 20000, 512
+    nq, k = 3, 512
     if case == "all_equal":
         s = np.full((nq, ld), 1.5, np.float32)
     elif case == "two_levels":
