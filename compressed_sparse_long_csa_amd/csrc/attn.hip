@@ -138,34 +138,35 @@ constexpr int kRowBf16 = 2 * kD;                        // 1024 bytes per window
 constexpr int kChunksSplit = kRowSplit / 16;            // 36 chunks of 16 bytes
 constexpr int kPitchSplit = kRowSplit + 16;             // LDS row pitch: rows land on distinct banks
 constexpr int kPitchWin = kRowBf16 + 16;
-constexpr int kTile = 64;                               // entries per tile
 constexpr int kThreads = 256;
-constexpr int kBufBytes = kTile * kPitchWin;            // raw tile buffer (largest row format)
-constexpr int kMaxK = 2048;                             // longest selected list kept in LDS
-constexpr int kPPitch8 = 72;                            // padded rows of the fp8 P arrays
-constexpr int kPPitch16 = 72;                           // padded rows (elements) of the bf16 P array
+constexpr int kWaves = kThreads / 64;
+constexpr int kStepE = 32;                              // compressed entries per wave step
+constexpr int kStepW = 16;                              // window rows per wave step
+constexpr int kBufBytes = kStepE * kPitchSplit;         // one step's rows (>= kStepW * kPitchWin)
+constexpr int kPPitch = 40;                             // padded rows of the P arrays
 constexpr float kPScale = 256.0f;                       // probabilities are stored x 2^8
+static_assert(kStepW * kPitchWin <= kBufBytes, "window step must fit a buffer");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-// Raw rows land in LDS as stored (split: 576-byte rows, window: 1024-byte rows)
-// through direct global->LDS loads, one wave instruction per row, at a pitch
-// padded by 16 bytes so that neighbouring rows start on different banks.  Every
-// operand address is then a per-lane base plus a compile-time offset.
+// Each wave owns its LDS: two step buffers that receive raw stored rows by
+// direct global->LDS loads (one wave instruction per row, pitch padded by 16
+// bytes), and its probability arrays.  No wave reads another wave's buffers,
+// so the entry loop has no workgroup barrier.
+struct __align__(16) WaveSmem {
+  uint8_t buf[2][kBufBytes];
+  uint8_t phi[16][kPPitch];        // fp8 high part of p * 2^8   [head][entry]
+  uint8_t plo[16][kPPitch];        // fp8 residual
+  uint16_t pbf[16][kPPitch];       // bf16(p * 2^8)
+};
 struct __align__(16) AttnSmem {
-  uint8_t raw[2][kBufBytes];       // double-buffered tiles
-  int32_t sel[kMaxK];              // selected entry list (CSA), -1 where dropped
-  uint8_t phi[16][kPPitch8];       // fp8 high part of p * 2^8   [head][entry]
-  uint8_t plo[16][kPPitch8];       // fp8 residual
-  uint16_t pbf[16][kPPitch16];     // bf16(p * 2^8)
-  float red_max[4][16];
-  float red_sum[4][16];
+  WaveSmem wave[kWaves];
   float rope_cs[kR / 2][2];        // cos, sin of the query's RoPE angles
-  int valid[2][kTile];
+  float ml[kWaves][2][16];         // per wave: running max and sum of each head
 };
 
 __device__ __forceinline__ const lds_u8* lds_ptr(const uint8_t* p) {
-  // the tile lives in LDS; a C-style cast changes the address space
+  // the buffers live in LDS; a C-style cast changes the address space
   return (const lds_u8*)(p);
 }
 
@@ -206,73 +207,261 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(long v) {
   return bf16x8{c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
 }
 
-// Per-query description of the attended list: n_ct tiles of compressed
-// entries (list positions [0, n_list)), then n_wt tiles of window rows.
+// Combine a value with the same lane of the other 16-lane rows of its half
+// (xor 16) and then of the other half (xor 32), in one fixed order.
+__device__ __forceinline__ float row_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Per-query description of the attended list.  Wave w takes, in step s < ns,
+// list positions [128 s + 32 w, +32) of the compressed entries, then in step
+// ns + t window rows [64 t + 16 w, +16).  Rows are read through buffer
+// descriptors over the query's own cache rows and window rows, so a row
+// address is a scalar byte offset.
 struct Work {
-  int b;
-  int64_t p, N, kv0, win_row0;
-  int n_list, n_ct, n_wt, win_count;
+  int64_t p, N;
+  int n_list, win_count, ns, n_steps;
+  const int32_t* idx;              // this query's selected list (CSA) or nullptr
+  buf_rsrc kv_rs, win_rs;
 };
 
-// Issue the direct global->LDS loads of tile `tile` into buffer `buf` and
-// write its per-row validity.  One wave instruction moves one row (36 lanes x
-// 16 bytes for a split row, 64 lanes for a window row) to the row's padded LDS
-// slot.  Rows without an entry load a real row (entry 0 / window row 0) and
-// are masked by `valid`, so no stale bits reach P.V.
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Work& w, int tile, int buf,
-                                           AttnSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint8_t* dst = sm.raw[buf];
-  if (tile < w.n_ct) {
-    const uint8_t* kv = static_cast<const uint8_t*>(a.kv) + w.kv0 * kRowSplit + lane * 16;
-    // lane l < 16 looks up the entry of this wave's row 4l + wv; readlane makes it scalar
-    int my_e = 0;
-    if (lane < kTile / 4) {
-      const int pos = tile * kTile + lane * 4 + wv;
-      if (pos < w.n_list) {
-        const int e = a.idx != nullptr ? sm.sel[pos] : pos;
-        my_e = e < 0 ? 0 : e;
-      }
-    }
+// Lane-held entry of the compressed step `step` (lanes < 32) and its validity.
+__device__ __forceinline__ int step_entry(const Work& w, int step, int wv, bool* ok) {
+  const int lane = threadIdx.x & 63;
+  *ok = false;
+  if (step >= w.ns || lane >= kStepE) return 0;
+  const int pos = step * (kWaves * kStepE) + wv * kStepE + lane;
+  int e = pos;
+  bool v = pos < w.n_list;
+  if (w.idx != nullptr) {
+    e = v ? w.idx[pos] : 0;
+    v = v && e >= 0 && e < w.N;
+  }
+  *ok = v;
+  return v ? e : 0;
+}
+
+// Direct buffer->LDS loads of one wave step into `dst`; returns the step's
+// row-validity mask (bit r = row r holds a real entry).  Rows without an
+// entry load entry 0 / window row 0 and stay masked.
+__device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, int my_e,
+                                               bool my_ok, uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+  typedef __attribute__((address_space(3))) void lds_void;
+  if (step < w.ns) {
     if (lane < kChunksSplit) {
 #pragma unroll
-      for (int i = 0; i < kTile / 4; ++i) {                             // 16 rows per wave
-        const int row = i * 4 + wv;
-        const int e = __builtin_amdgcn_readlane(my_e, i);
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(kv + static_cast<int64_t>(e) * kRowSplit),
-            (__attribute__((address_space(3))) void*)(lds_ptr(dst + row * kPitchSplit)), 16, 0, 0);
+      for (int r = 0; r < kStepE; ++r) {
+        const int e = __builtin_amdgcn_readlane(my_e, r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w.kv_rs, (lds_void*)(lds_ptr(dst + r * kPitchSplit)),
+                                                 16, lane * 16, e * kRowSplit, 0, 0);
       }
     }
-    if (tid < kTile) {
-      const int pos = tile * kTile + tid;
-      int ok = 0;
-      if (pos < w.n_list) ok = a.idx != nullptr ? (sm.sel[pos] >= 0) : 1;
-      sm.valid[buf][tid] = ok;
-    }
-  } else {
-    const uint8_t* win = static_cast<const uint8_t*>(a.win) + w.win_row0 * kRowBf16 + lane * 16;
-    const int wt = tile - w.n_ct;
+    return static_cast<uint32_t>(__ballot(lane < kStepE && my_ok));
+  }
+  const int j0 = (step - w.ns) * (kWaves * kStepW) + wv * kStepW;
 #pragma unroll
-    for (int i = 0; i < kTile / 4; ++i) {                               // 16 rows per wave
-      const int row = i * 4 + wv;
-      const int j = wt * kTile + row;
-      const int src = j < w.win_count ? j : 0;
-      __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(win + static_cast<int64_t>(src) * kRowBf16),
-          (__attribute__((address_space(3))) void*)(lds_ptr(dst + row * kPitchWin)), 16, 0, 0);
+  for (int r = 0; r < kStepW; ++r) {
+    const int src = j0 + r < w.win_count ? j0 + r : 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w.win_rs, (lds_void*)(lds_ptr(dst + r * kPitchWin)),
+                                             16, lane * 16, src * kRowBf16, 0, 0);
+  }
+  const int nv = w.win_count - j0;
+  return nv >= kStepW ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+}
+
+// Online-softmax update of head j16 from this lane's logits t (log2 domain):
+// returns alpha and writes the probabilities p = 2^(t - m_new).
+template <int NV>
+__device__ __forceinline__ float softmax_step(const float (&t)[NV], float (&pv)[NV], float& m_run,
+                                              float& l_run) {
+  float mx = t[0];
+#pragma unroll
+  for (int r = 1; r < NV; ++r) mx = fmaxf(mx, t[r]);
+  const float m_new = fmaxf(m_run, row_max4(mx));
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  float ps = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NV; ++r) {
+    pv[r] = __builtin_amdgcn_exp2f(t[r] - m_new);
+    ps += pv[r];
+  }
+  l_run = l_run * alpha + row_sum4(ps);
+  m_run = m_new;
+  return alpha;
+}
+
+// The entry loop of one wave.  NB output blocks of 16 dims starting at dbase,
+// the first NF of them FP8 dims (the rest the BF16 RoPE dims).
+template <int NB, int NF>
+__device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, const bf16x8 (&qb)[kD / 32],
+                                           float ch, int dbase, float& m_run, float& l_run,
+                                           f32x4 (&acc)[NB], int e_next, bool ok_next,
+                                           uint32_t vmask_cur) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, j16 = lane & 15;
+  for (int step = 0; step < w.n_steps; ++step) {
+    const int bi = step & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this step's rows landed
+    const uint32_t vmask = vmask_cur;
+    if (step + 1 < w.n_steps) {
+      vmask_cur = issue_step(w, step + 1, wv, e_next, ok_next, ws.buf[bi ^ 1]);
+      e_next = step_entry(w, step + 2, wv, &ok_next);
     }
-    if (tid < kTile) sm.valid[buf][tid] = wt * kTile + tid < w.win_count;
+    const uint8_t* T = ws.buf[bi];
+    float alpha;
+    if (step < w.ns) {
+      // -------- logits of the step's 32 entries (two 16-row blocks) x 16 heads.
+      // Every operand read is issued before the math so the LDS latency
+      // overlaps, and the two blocks' MFMA chains interleave.
+      long ka[2][kDF8 / 32];
+      bf16x8 kr[2][kR / 32];
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        const uint8_t* rowp = T + (bk * 16 + j16) * kPitchSplit + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < kDF8 / 32; ++ks) ka[bk][ks] = lds_read_b64(rowp + ks * 32);
+#pragma unroll
+        for (int ks = 0; ks < kR / 32; ++ks)
+          kr[bk][ks] = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + g * 8 + ks * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int ks = 0; ks < kDF8 / 32; ++ks)
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(ka[bk][ks]), qb[ks], s[bk], 0, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kR / 32; ++ks)
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[bk][ks], qb[kDF8 / 32 + ks], s[bk], 0, 0, 0);
+      // lane holds head j16, entries 16 bk + 4 g + r
+      float t[8], pv[8];
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (vmask >> (bk * 16 + g * 4 + r)) & 1u;
+          t[bk * 4 + r] = ok ? s[bk][r] * ch : -INFINITY;
+        }
+      alpha = softmax_step<8>(t, pv, m_run, l_run);
+      // probabilities to this wave's LDS in the P^T operand layout [head][entry]
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+        const int e0 = bk * 16 + g * 4;
+        const float v0 = pv[bk * 4] * kPScale, v1 = pv[bk * 4 + 1] * kPScale;
+        const float v2 = pv[bk * 4 + 2] * kPScale, v3 = pv[bk * 4 + 3] * kPScale;
+        if (NF > 0) {
+          const uint32_t h01 = fp8x2(v0, v1), h23 = fp8x2(v2, v3);
+          const f32x2 d01 = fp8x2_to_f32(h01), d23 = fp8x2_to_f32(h23);
+          const uint32_t l01 = fp8x2(v0 - d01[0], v1 - d01[1]), l23 = fp8x2(v2 - d23[0], v3 - d23[1]);
+          *reinterpret_cast<uint32_t*>(&ws.phi[j16][e0]) = h01 | (h23 << 16);
+          *reinterpret_cast<uint32_t*>(&ws.plo[j16][e0]) = l01 | (l23 << 16);
+        }
+        if (NF < NB) {
+          uint2 bb;
+          bb.x = bf16x2_rne(v0, v1);
+          bb.y = bf16x2_rne(v2, v3);
+          *reinterpret_cast<uint2*>(&ws.pbf[j16][e0]) = bb;
+        }
+      }
+    } else {
+      // -------- window step: 16 BF16 rows x 16 heads
+      const uint8_t* rowp = T + j16 * kPitchWin + g * 16;
+      bf16x8 kw[kD / 32];
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) kw[ks] = *reinterpret_cast<const bf16x8*>(rowp + ks * 64);
+      __builtin_amdgcn_sched_barrier(0);
+      // two partial chains (even / odd k-steps), added once at the end
+      f32x4 s2[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks)
+        s2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[ks], qb[ks], s2[ks & 1], 0, 0, 0);
+      const f32x4 s = s2[0] + s2[1];
+      float t[4], pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (vmask >> (g * 4 + r)) & 1u;
+        t[r] = ok ? s[r] * ch : -INFINITY;
+      }
+      alpha = softmax_step<4>(t, pv, m_run, l_run);
+      uint2 bb;
+      bb.x = bf16x2_rne(pv[0] * kPScale, pv[1] * kPScale);
+      bb.y = bf16x2_rne(pv[2] * kPScale, pv[3] * kPScale);
+      *reinterpret_cast<uint2*>(&ws.pbf[j16][g * 4]) = bb;
+    }
+    if (__ballot(alpha != 1.0f) != 0ull) {              // the running max moved for some head
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] *= alpha;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (step < w.ns) {
+      // -------- P.V over the 32 entries: rows = dims, cols = heads
+      const int ebase = g * 8;
+      long phv = 0, plv = 0;
+      bf16x8 pbv = {};
+      if (NF > 0) {
+        phv = lds_read_b64(&ws.phi[j16][ebase]);
+        plv = lds_read_b64(&ws.plo[j16][ebase]);
+      }
+      if (NF < NB) pbv = *reinterpret_cast<const bf16x8*>(&ws.pbf[j16][ebase]);
+      // fp8 dims: lane j of group g supplies row (ebase + j/2), bytes d0 + 8*(j%2)
+      const uint8_t* b8 = T + (ebase + (j16 >> 1)) * kPitchSplit + dbase + 8 * (j16 & 1);
+      // bf16 RoPE dims: lane j supplies row (ebase + j/4), dims d0 + 4*(j%4)
+      const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchSplit + kDF8 +
+                           (dbase + NF * 16 - kDF8) * 2 + 8 * (j16 & 3);
+      long v8[NF > 0 ? NF : 1];
+      bf16x8 v16[NB - NF > 0 ? NB - NF : 1];
+#pragma unroll
+      for (int i = 0; i < NF; ++i) v8[i] = tr8(b8 + i * 16);
+#pragma unroll
+      for (int i = 0; i < NB - NF; ++i) {
+        const bf16x4 lo4 = tr16(b16 + i * 32);
+        const bf16x4 hi4 = tr16(b16 + i * 32 + 4 * kPitchSplit);
+        v16[i] = bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], phv, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], plv, acc[i], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NB - NF; ++i)
+        acc[NF + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v16[i], pbv, acc[NF + i], 0, 0, 0);
+    } else {
+      const bf16x4 pbw = *reinterpret_cast<const bf16x4*>(&ws.pbf[j16][g * 4]);
+      // lane j of group g supplies row (4 g + j/4), dims d0 + 4*(j%4)
+      const uint8_t* b16 = T + (g * 4 + (j16 >> 2)) * kPitchWin + dbase * 2 + 8 * (j16 & 3);
+      bf16x4 vw[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) vw[i] = tr16(b16 + i * 32);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vw[i], pbw, acc[i], 0, 0, 0);
+    }
   }
 }
 
 // DVS = number of workgroups sharing one (query, 16-head tile): each owns
-// 512 / DVS output dims, i.e. DW = 128 / DVS per wave.
+// 512 / DVS output dims; every wave of it accumulates all of them over its
+// own entries, and the four partial states are merged at the end in wave order.
 template <int DVS>
 __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_units,
                                                              int n_pad) {
-  constexpr int DW = 128 / DVS;        // output dims per wave
-  constexpr int NB = DW / 16;          // 16-dim MFMA blocks per wave
+  constexpr int DWG = kD / DVS;        // output dims of this workgroup
+  constexpr int NB = DWG / 16;         // 16-dim MFMA blocks
+  // the last slice holds the BF16 RoPE dims: its first NFR blocks are FP8 dims
+  constexpr int NFR = (kDF8 - (kD - DWG)) / 16;
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
 
@@ -286,44 +475,50 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const int dvs = unit % DVS;
   const int ht = (unit / DVS) % n_ht;
   const int b = unit / (DVS * n_ht);
+  const int dbase = dvs * DWG;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j16 = lane & 15;
+  WaveSmem& ws = sm.wave[wv];
 
   Work w;
-  w.b = b;
   w.p = a.q_pos[b];
   w.N = (w.p + 1) / a.m;
-  w.kv0 = a.kv_off[b];
-  window_of(a, b, w.p, &w.win_row0, &w.win_count);
-  if (a.idx != nullptr) {
-    w.n_list = w.N > 0 ? a.k : 0;
-    for (int j = tid; j < a.k; j += kThreads) {
-      const int32_t e = a.idx[static_cast<int64_t>(b) * a.k + j];
-      sm.sel[j] = (e >= 0 && e < w.N) ? e : -1;
-    }
-  } else {
-    w.n_list = static_cast<int>(w.N);
-  }
-  w.n_ct = (w.n_list + kTile - 1) / kTile;
-  w.n_wt = (w.win_count + kTile - 1) / kTile;
-  const int n_tiles = w.n_ct + w.n_wt;
+  const int64_t kv0 = a.kv_off[b];
+  int64_t win_row0;
+  window_of(a, b, w.p, &win_row0, &w.win_count);
+  w.idx = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
+  w.n_list = a.idx != nullptr ? (w.N > 0 ? a.k : 0) : static_cast<int>(w.N);
+  w.ns = (w.n_list + kWaves * kStepE - 1) / (kWaves * kStepE);
+  w.n_steps = w.ns + (w.win_count + kWaves * kStepW - 1) / (kWaves * kStepW);
+  const uint64_t kv_bytes = static_cast<uint64_t>(w.N) * kRowSplit;
+  w.kv_rs = make_rsrc(static_cast<const uint8_t*>(a.kv) + kv0 * kRowSplit,
+                      kv_bytes < 0xffffffffull ? static_cast<uint32_t>(kv_bytes) : 0xffffffffu);
+  w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
+                       static_cast<uint32_t>(w.win_count) * kRowBf16);
+
+  // first step's rows go out before anything else
+  bool ok0, ok1;
+  const int e0 = step_entry(w, 0, wv, &ok0);
+  const int e1 = step_entry(w, 1, wv, &ok1);
+  const uint32_t vmask0 = w.n_steps > 0 ? issue_step(w, 0, wv, e0, ok0, ws.buf[0]) : 0u;
+
   if (tid < kR / 2) {
     float sn, cs;
     rope_sincos(w.p, a.rope_theta[tid], &sn, &cs);
     sm.rope_cs[tid][0] = cs;
     sm.rope_cs[tid][1] = sn;
   }
-  __syncthreads();                                      // sel[] and rope_cs ready
 
-  if (n_tiles > 0) issue_tile(a, w, 0, 0, sm);
-
-  // ---------------- prologue: qhat = RoPE(RMSNorm(q)) for 16 heads, staged in raw[1]
-  uint16_t(*qbf)[kD] = reinterpret_cast<uint16_t(*)[kD]>(sm.raw[1]);
+  // ---------------- prologue: qhat = RoPE(RMSNorm(q)); wave w prepares heads
+  // 4w .. 4w+3 into a bf16 staging copy (in wave 0's second buffer, free until
+  // its first DMA of step 1), then every lane takes its QK operand from it.
+  uint16_t(*qbf)[kD] = reinterpret_cast<uint16_t(*)[kD]>(sm.wave[0].buf[1]);
   {
-    const int h = tid >> 4, c = tid & 15;          // head in tile, 32-dim chunk
-    const int hg = ht * 16 + h;
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(b) * a.H + hg) * kD + c * 32;
+    const int h = wv * 4 + (lane >> 4), c = lane & 15;  // head in tile, 32-dim chunk
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
+                        (static_cast<int64_t>(b) * a.H + ht * 16 + h) * kD + c * 32;
     float x[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -343,6 +538,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     const float r = static_cast<float>(1.0 / sqrt(static_cast<double>(ss) / kD + a.eps));
 #pragma unroll
     for (int t = 0; t < 32; ++t) x[t] = x[t] * r * (a.q_norm_w ? a.q_norm_w[c * 32 + t] : 1.0f);
+    __syncthreads();                                    // rope_cs ready
     if (c * 32 >= kD - kR) {
       const int p0 = (c * 32 - (kD - kR)) / 2;
 #pragma unroll
@@ -369,157 +565,53 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 #pragma unroll
   for (int ks = 0; ks < kD / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(&qbf[j16][ks * 32 + g * 8]);
   const float ch = a.scale * kLog2e;
-  __syncthreads();                                      // raw[1] free again
+  __syncthreads();                                      // the staging copy is free again
 
-  // softmax state for head j16 (identical in all lanes of that head)
+  // softmax state of head j16 (the same in the four lanes of that head); the
+  // sink enters once, through wave 0
   float m_run = a.sinks[ht * 16 + j16] * kLog2e;
-  float l_run = 1.0f;
+  float l_run = wv == 0 ? 1.0f : 0.0f;
   f32x4 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int dbase = dvs * (kD / DVS) + wv * DW;         // first output dim of this wave
+  if (dbase + DWG <= kDF8)
+    entry_loop<NB, NB>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, e1, ok1, vmask0);
+  else
+    entry_loop<NB, NFR>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, e1, ok1, vmask0);
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    const bool is_win = tile >= w.n_ct;
-    __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this tile's loads landed
-    __syncthreads();                                    // ... in every wave; previous P.V done
-    if (tile + 1 < n_tiles) issue_tile(a, w, tile + 1, buf ^ 1, sm);
-    const uint8_t* T = sm.raw[buf];
-
-    // -------- logits for entries 16*wv .. 16*wv+15 (rows), heads (cols)
-    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int erow = wv * 16 + j16;
-    if (!is_win) {
-      const uint8_t* rowp = T + erow * kPitchSplit + g * 8;
-      long ka[kDF8 / 32];
-#pragma unroll
-      for (int ks = 0; ks < kDF8 / 32; ++ks) ka[ks] = lds_read_b64(rowp + ks * 32);
-      bf16x8 kr[kR / 32];
-#pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks)
-        kr[ks] = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + g * 8 + ks * 64);
-#pragma unroll
-      for (int ks = 0; ks < kDF8 / 32; ++ks)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(ka[ks]), qb[ks], s, 0, 0, 0);
-#pragma unroll
-      for (int ks = 0; ks < kR / 32; ++ks)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[kDF8 / 32 + ks], s, 0, 0, 0);
-    } else {
-      const uint8_t* rowp = T + erow * kPitchWin + g * 16;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 kw[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          kw[ks] = *reinterpret_cast<const bf16x8*>(rowp + (half * 8 + ks) * 64);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[ks], qb[half * 8 + ks], s, 0, 0, 0);
-      }
-    }
-    // lane holds head j16, entries 16*wv + 4*g + r
-    float t[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = sm.valid[buf][wv * 16 + g * 4 + r] != 0;
-      t[r] = ok ? s[r] * ch : -INFINITY;
-      mx = fmaxf(mx, t[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lane < 16) sm.red_max[wv][j16] = mx;
-    __syncthreads();
-    const float tmax = fmaxf(fmaxf(sm.red_max[0][j16], sm.red_max[1][j16]),
-                             fmaxf(sm.red_max[2][j16], sm.red_max[3][j16]));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float pv[4];
-    float ps = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = exp2f(t[r] - m_new);
-      ps += pv[r];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    if (lane < 16) sm.red_sum[wv][j16] = ps;
-    // probabilities to LDS in the P^T operand layout [head][entry]
-    {
-      const int e0 = wv * 16 + g * 4;
-      const float v0 = pv[0] * kPScale, v1 = pv[1] * kPScale, v2 = pv[2] * kPScale, v3 = pv[3] * kPScale;
-      const uint32_t h01 = fp8x2(v0, v1), h23 = fp8x2(v2, v3);
-      const f32x2 d01 = fp8x2_to_f32(h01), d23 = fp8x2_to_f32(h23);
-      const uint32_t l01 = fp8x2(v0 - d01[0], v1 - d01[1]), l23 = fp8x2(v2 - d23[0], v3 - d23[1]);
-      *reinterpret_cast<uint32_t*>(&sm.phi[j16][e0]) = h01 | (h23 << 16);
-      *reinterpret_cast<uint32_t*>(&sm.plo[j16][e0]) = l01 | (l23 << 16);
-      uint2 bb;
-      bb.x = bf16x2_rne(v0, v1);
-      bb.y = bf16x2_rne(v2, v3);
-      *reinterpret_cast<uint2*>(&sm.pbf[j16][e0]) = bb;
-    }
-    __syncthreads();
-    const float tsum = ((sm.red_sum[0][j16] + sm.red_sum[1][j16]) + sm.red_sum[2][j16]) + sm.red_sum[3][j16];
-    l_run = l_run * alpha + tsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i] *= alpha;
-
-    // -------- P.V for dims [dbase, dbase + DW): rows = dims, cols = heads
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {                     // entries [32*ks, 32*ks + 32)
-      const int ebase = ks * 32 + g * 8;
-      const long phv = lds_read_b64(&sm.phi[j16][ebase]);
-      const long plv = lds_read_b64(&sm.plo[j16][ebase]);
-      const bf16x8 pbv = *reinterpret_cast<const bf16x8*>(&sm.pbf[j16][ebase]);
-      if (!is_win) {
-        // fp8 dims: lane j of group g supplies row (ebase + j/2), bytes d0 + 8*(j%2)
-        const uint8_t* b8 = T + (ebase + (j16 >> 1)) * kPitchSplit + dbase + 8 * (j16 & 1);
-        // bf16 RoPE dims: lane j supplies row (ebase + j/4), dims d0 + 4*(j%4)
-        const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchSplit + kDF8 + (dbase - kDF8) * 2 + 8 * (j16 & 3);
-        long v8[NB];
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          if (dbase + i * 16 < kDF8) v8[i] = tr8(b8 + i * 16);
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          if (dbase + i * 16 < kDF8) {
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], phv, acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(v8[i], plv, acc[i], 0, 0, 0);
-          } else {
-            const bf16x4 lo4 = tr16(b16 + i * 32);
-            const bf16x4 hi4 = tr16(b16 + i * 32 + 4 * kPitchSplit);
-            const bf16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pbv, acc[i], 0, 0, 0);
-          }
-        }
-      } else {
-        const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchWin + dbase * 2 + 8 * (j16 & 3);
-        bf16x8 vw[NB];
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const bf16x4 lo4 = tr16(b16 + i * 32);
-          const bf16x4 hi4 = tr16(b16 + i * 32 + 4 * kPitchWin);
-          vw[i] = bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[i], pbv, acc[i], 0, 0, 0);
-      }
-    }
+  // -------- merge the four waves' states in wave order, then out = acc / (2^8 * l)
+  __syncthreads();                                      // every wave is done with its buffers
+  if (lane < 16) {
+    sm.ml[wv][0][j16] = m_run;
+    sm.ml[wv][1][j16] = l_run;
   }
-
-  // -------- epilogue: out = acc / (2^8 * l)
-  const float inv = 1.0f / (l_run * kPScale);
+  f32x4* part = reinterpret_cast<f32x4*>(&ws.buf[0][0]);   // [NB][64 lanes]
+#pragma unroll
+  for (int i = 0; i < NB; ++i) part[i * 64 + lane] = acc[i];
+  __syncthreads();
+  float f[kWaves];
+  float mm = sm.ml[0][0][j16];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) mm = fmaxf(mm, sm.ml[v][0][j16]);
+  float L = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    f[v] = __builtin_amdgcn_exp2f(sm.ml[v][0][j16] - mm);
+    L += sm.ml[v][1][j16] * f[v];
+  }
+  const float inv = 1.0f / (L * kPScale);
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * a.H + ht * 16 + j16) * kD;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int i = wv * (NB / kWaves); i < (wv + 1) * (NB / kWaves); ++i) {
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+      o += reinterpret_cast<const f32x4*>(&sm.wave[v].buf[0][0])[i * 64 + lane] * f[v];
     const int d = dbase + i * 16 + g * 4;
-    uint2 v;
-    v.x = static_cast<uint32_t>(f32_to_bf16(acc[i][0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc[i][1] * inv)) << 16);
-    v.y = static_cast<uint32_t>(f32_to_bf16(acc[i][2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(acc[i][3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(out + d) = v;
+    uint2 st;
+    st.x = static_cast<uint32_t>(f32_to_bf16(o[0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[1] * inv)) << 16);
+    st.y = static_cast<uint32_t>(f32_to_bf16(o[2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(o[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(out + d) = st;
   }
 }
 

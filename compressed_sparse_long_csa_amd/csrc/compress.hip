@@ -10,6 +10,12 @@
 // One workgroup per output entry.  The block sum runs over the m tokens in
 // order, the mean square over D in a fixed tree, so an entry's bits depend
 // only on its own tokens.
+//
+// Latency: a decode step writes a handful of entries, so the kernel is a
+// chain of memory round trips, and it keeps that chain short.  The block's
+// tokens and gate logits depend only on the entry number and are loaded
+// first (into registers when m * ceil(D / 256) <= 16); the segment of the
+// block is found in the same round trip, every thread testing one segment.
 #include "kernels.hpp"
 
 namespace csa {
@@ -17,128 +23,210 @@ namespace csa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxSegParallel = kThreads;   // segments tested in parallel
 
 __device__ __forceinline__ float load_x(const void* x, csa_fmt fmt, int64_t i) {
   return fmt == CSA_F32 ? static_cast<const float*>(x)[i]
                         : bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
-__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int64_t n_blocks) {
-  const void* __restrict__ x = a.x;
-  const csa_fmt x_fmt = a.x_fmt;
-  const float* __restrict__ gate = a.gate;
-  const int gate_cols = a.gate_cols, D = a.D, m = a.m, nseg = a.nseg, normalize = a.normalize;
-  const int64_t* __restrict__ seg_tok_off = a.seg_tok_off;
-  const int64_t* __restrict__ seg_pos0 = a.seg_pos0;
-  const int64_t* __restrict__ seg_out_row = a.seg_out_row;
-  const float* __restrict__ norm_w = a.norm_w;
-  const float eps = a.eps;
-  const int R = a.rope_dim;
-  uint8_t* __restrict__ out = static_cast<uint8_t*>(a.out);
-  const csa_fmt out_fmt = a.out_fmt;
-  extern __shared__ float y[];            // [D] entry values, then [kThreads/64] partials
-  float* red = y + D;
+struct EntrySlot {
+  int64_t row;
+  int64_t pos;
+  int ok;
+};
+
+// Segment of the block starting at token t0, its output row and position.
+// ok = 0 for a block that straddles a segment boundary.  Ends with a barrier.
+__device__ __forceinline__ void locate(const CompressArgs& a, int64_t t0, EntrySlot* slot) {
   const int tid = threadIdx.x;
-  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-    const int64_t t0 = blk * m;
-    // segment holding token t0: the last s with seg_tok_off[s] <= t0
+  const int m = a.m, nseg = a.nseg;
+  if (nseg <= kMaxSegParallel) {
+    if (tid == 0) slot->ok = 0;
+    __syncthreads();
+    if (tid < nseg) {
+      const int64_t lo = a.seg_tok_off[tid], hi = a.seg_tok_off[tid + 1];
+      const int64_t p0 = a.seg_pos0[tid], r0 = a.seg_out_row[tid];
+      if (lo <= t0 && t0 < hi && (t0 - lo) % m == 0 && t0 + m <= hi) {
+        const int64_t j = (t0 - lo) / m;
+        slot->row = r0 + j;
+        slot->pos = p0 + j * m;
+        slot->ok = 1;
+      }
+    }
+  } else if (tid == 0) {
+    // the last s with seg_tok_off[s] <= t0
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (seg_tok_off[mid] <= t0) lo = mid; else hi = mid - 1;
+      if (a.seg_tok_off[mid] <= t0) lo = mid; else hi = mid - 1;
     }
-    const int s = lo;
-    const int64_t off = seg_tok_off[s];
-    if ((t0 - off) % m != 0 || t0 + m > seg_tok_off[s + 1]) continue;   // straddling block
+    const int64_t off = a.seg_tok_off[lo];
+    const int ok = (t0 - off) % m == 0 && t0 + m <= a.seg_tok_off[lo + 1];
     const int64_t j = (t0 - off) / m;
-    const int64_t row = seg_out_row[s] + j;
-    const int64_t pos = seg_pos0[s] + j * m;
+    slot->row = a.seg_out_row[lo] + j;
+    slot->pos = a.seg_pos0[lo] + j * m;
+    slot->ok = ok;
+  }
+  __syncthreads();
+}
 
-    // softmax-gated block sum
+// Softmax-gated block sum of channel c (tokens t0 .. t0+m-1 in order).
+// xv / gv hold the values already loaded, or nullptr to read them here.
+__device__ __forceinline__ float gated_sum(int m, const float* xv, const float* gv) {
+  float gmax = -INFINITY;
+  for (int t = 0; t < m; ++t) gmax = fmaxf(gmax, gv[t]);
+  float den = 0.0f, acc = 0.0f;
+  for (int t = 0; t < m; ++t) {
+    const float e = expf(gv[t] - gmax);
+    den += e;
+    acc = fmaf(e, xv[t], acc);
+  }
+  return acc / den;
+}
+
+// Normalise, rotate and store the entry held in y[0 .. D); sq is this
+// thread's partial sum of squares.
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, float* y, float* red, float sq,
+                                             const EntrySlot& slot) {
+  const int tid = threadIdx.x;
+  const int D = a.D, R = a.rope_dim;
+  if (a.normalize) {
+    sq = wave_sum(sq);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sq;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += red[w];
+    const float r = static_cast<float>(1.0 / sqrt(static_cast<double>(tot) / D + a.eps));
+    for (int c = tid; c < D; c += kThreads)
+      y[c] = y[c] * r * (a.norm_w ? a.norm_w[c] : 1.0f);
+  }
+  __syncthreads();
+  if (R > 0) {
+    for (int i = tid; i < R / 2; i += kThreads) {
+      float sn, cs;
+      rope_sincos(slot.pos, a.rope_theta[i], &sn, &cs);
+      const int d = D - R + 2 * i;
+      const float u = y[d], v = y[d + 1];
+      y[d] = u * cs - v * sn;
+      y[d + 1] = u * sn + v * cs;
+    }
+    __syncthreads();
+  }
+  // quantised store
+  const size_t rb = row_bytes(a.out_fmt, D, R);
+  uint8_t* dst = static_cast<uint8_t*>(a.out) + slot.row * rb;
+  switch (a.out_fmt) {
+    case CSA_F32:
+      for (int c = tid; c < D; c += kThreads) reinterpret_cast<float*>(dst)[c] = y[c];
+      break;
+    case CSA_BF16:
+      for (int c = tid; c < D; c += kThreads) reinterpret_cast<uint16_t*>(dst)[c] = f32_to_bf16(y[c]);
+      break;
+    case CSA_FP8:
+      for (int c = tid; c < D; c += kThreads) dst[c] = static_cast<uint8_t>(f32_to_e4m3(y[c]));
+      break;
+    case CSA_SPLIT:
+      for (int c = tid; c < D; c += kThreads) {
+        if (c < D - R) dst[c] = static_cast<uint8_t>(f32_to_e4m3(y[c]));
+        else reinterpret_cast<uint16_t*>(dst + (D - R))[c - (D - R)] = f32_to_bf16(y[c]);
+      }
+      break;
+    case CSA_MXFP4:
+      for (int b = tid; b < D / 32; b += kThreads) {
+        float amax = 0.0f;
+        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[b * 32 + e]));
+        uint32_t sbyte = 0;
+        int shared = 0;
+        if (amax > 0.0f) {
+          int ex;
+          frexpf(amax, &ex);
+          shared = ex - 1 - 2;
+          shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
+          sbyte = static_cast<uint32_t>(shared + 127);
+        }
+        for (int e = 0; e < 32; e += 2) {
+          uint32_t c0 = 0, c1 = 0;
+          if (amax > 0.0f) {
+            c0 = f32_to_e2m1(ldexpf(y[b * 32 + e], -shared));
+            c1 = f32_to_e2m1(ldexpf(y[b * 32 + e + 1], -shared));
+          }
+          dst[(b * 32 + e) / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
+        }
+        dst[D / 2 + b] = static_cast<uint8_t>(sbyte);
+      }
+      break;
+    default:
+      break;
+  }
+  __syncthreads();
+}
+
+// Blocks of M tokens, D <= 256 * NCH: the block's values are loaded into
+// registers before the segment lookup, so both share one round trip.
+template <int M, int NCH>
+__global__ void __launch_bounds__(kThreads) compress_small(CompressArgs a, int64_t n_blocks) {
+  extern __shared__ float y[];            // [D] entry values, then [kThreads/64] partials
+  __shared__ EntrySlot slot;
+  float* red = y + a.D;
+  const int tid = threadIdx.x, D = a.D;
+  const bool per_channel = a.gate_cols != 1;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    const int64_t t0 = blk * M;
+    float xv[NCH][M], gv[NCH][M];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kThreads;
+      const int cc = c < D ? c : 0;
+      const int gc = per_channel ? cc : 0;
+#pragma unroll
+      for (int t = 0; t < M; ++t) {
+        xv[i][t] = load_x(a.x, a.x_fmt, (t0 + t) * D + cc);
+        gv[i][t] = a.gate[(t0 + t) * a.gate_cols + gc];
+      }
+    }
+    locate(a, t0, &slot);
+    if (!slot.ok) continue;
+    float sq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < D) {
+        const float v = gated_sum(M, xv[i], gv[i]);
+        y[c] = v;
+        sq = fmaf(v, v, sq);
+      }
+    }
+    finish_entry(a, y, red, sq, slot);
+  }
+}
+
+// Any m and D: values are read inside the block loop.
+__global__ void __launch_bounds__(kThreads) compress_any(CompressArgs a, int64_t n_blocks) {
+  extern __shared__ float y[];
+  __shared__ EntrySlot slot;
+  float* red = y + a.D;
+  const int tid = threadIdx.x, D = a.D, m = a.m;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    const int64_t t0 = blk * m;
+    locate(a, t0, &slot);
+    if (!slot.ok) continue;
     float sq = 0.0f;
     for (int c = tid; c < D; c += kThreads) {
-      const int gc = gate_cols == 1 ? 0 : c;
+      const int gc = a.gate_cols == 1 ? 0 : c;
       float gmax = -INFINITY;
-      for (int t = 0; t < m; ++t) gmax = fmaxf(gmax, gate[(t0 + t) * gate_cols + gc]);
+      for (int t = 0; t < m; ++t) gmax = fmaxf(gmax, a.gate[(t0 + t) * a.gate_cols + gc]);
       float den = 0.0f, acc = 0.0f;
       for (int t = 0; t < m; ++t) {
-        const float e = expf(gate[(t0 + t) * gate_cols + gc] - gmax);
+        const float e = expf(a.gate[(t0 + t) * a.gate_cols + gc] - gmax);
         den += e;
-        acc = fmaf(e, load_x(x, x_fmt, (t0 + t) * D + c), acc);
+        acc = fmaf(e, load_x(a.x, a.x_fmt, (t0 + t) * D + c), acc);
       }
       const float v = acc / den;
       y[c] = v;
       sq = fmaf(v, v, sq);
     }
-    if (normalize) {
-      sq = wave_sum(sq);
-      if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sq;
-      __syncthreads();
-      float tot = 0.0f;
-      for (int w = 0; w < kThreads / kWave; ++w) tot += red[w];
-      const float r = static_cast<float>(1.0 / sqrt(static_cast<double>(tot) / D + eps));
-      for (int c = tid; c < D; c += kThreads)
-        y[c] = y[c] * r * (norm_w ? norm_w[c] : 1.0f);
-    }
-    __syncthreads();
-    if (R > 0) {
-      for (int i = tid; i < R / 2; i += kThreads) {
-        float sn, cs;
-        rope_sincos(pos, a.rope_theta[i], &sn, &cs);
-        const int d = D - R + 2 * i;
-        const float a = y[d], b = y[d + 1];
-        y[d] = a * cs - b * sn;
-        y[d + 1] = a * sn + b * cs;
-      }
-      __syncthreads();
-    }
-    // quantised store
-    const size_t rb = row_bytes(out_fmt, D, R);
-    uint8_t* dst = out + row * rb;
-    switch (out_fmt) {
-      case CSA_F32:
-        for (int c = tid; c < D; c += kThreads) reinterpret_cast<float*>(dst)[c] = y[c];
-        break;
-      case CSA_BF16:
-        for (int c = tid; c < D; c += kThreads) reinterpret_cast<uint16_t*>(dst)[c] = f32_to_bf16(y[c]);
-        break;
-      case CSA_FP8:
-        for (int c = tid; c < D; c += kThreads) dst[c] = static_cast<uint8_t>(f32_to_e4m3(y[c]));
-        break;
-      case CSA_SPLIT:
-        for (int c = tid; c < D; c += kThreads) {
-          if (c < D - R) dst[c] = static_cast<uint8_t>(f32_to_e4m3(y[c]));
-          else reinterpret_cast<uint16_t*>(dst + (D - R))[c - (D - R)] = f32_to_bf16(y[c]);
-        }
-        break;
-      case CSA_MXFP4:
-        for (int b = tid; b < D / 32; b += kThreads) {
-          float amax = 0.0f;
-          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[b * 32 + e]));
-          uint32_t sbyte = 0;
-          int shared = 0;
-          if (amax > 0.0f) {
-            int ex;
-            frexpf(amax, &ex);
-            shared = ex - 1 - 2;
-            shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
-            sbyte = static_cast<uint32_t>(shared + 127);
-          }
-          for (int e = 0; e < 32; e += 2) {
-            uint32_t c0 = 0, c1 = 0;
-            if (amax > 0.0f) {
-              c0 = f32_to_e2m1(ldexpf(y[b * 32 + e], -shared));
-              c1 = f32_to_e2m1(ldexpf(y[b * 32 + e + 1], -shared));
-            }
-            dst[(b * 32 + e) / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
-          }
-          dst[D / 2 + b] = static_cast<uint8_t>(sbyte);
-        }
-        break;
-      default:
-        break;
-    }
-    __syncthreads();
+    finish_entry(a, y, red, sq, slot);
   }
 }
 
@@ -149,8 +237,18 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
   const int64_t grid = n_blocks < 65536 ? n_blocks : 65536;
   const size_t shm = (static_cast<size_t>(a.D) + kThreads / kWave) * sizeof(float);
-  hipLaunchKernelGGL(compress_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), shm,
-                     stream, a, n_blocks);
+  const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
+  const int nch = (a.D + kThreads - 1) / kThreads;
+  if (a.m == 4 && nch <= 2) {
+    if (nch == 1) hipLaunchKernelGGL((compress_small<4, 1>), g, b, shm, stream, a, n_blocks);
+    else hipLaunchKernelGGL((compress_small<4, 2>), g, b, shm, stream, a, n_blocks);
+  } else if (a.m == 1 && nch <= 4) {
+    if (nch == 1) hipLaunchKernelGGL((compress_small<1, 1>), g, b, shm, stream, a, n_blocks);
+    else if (nch == 2) hipLaunchKernelGGL((compress_small<1, 2>), g, b, shm, stream, a, n_blocks);
+    else hipLaunchKernelGGL((compress_small<1, 4>), g, b, shm, stream, a, n_blocks);
+  } else {
+    hipLaunchKernelGGL(compress_any, g, b, shm, stream, a, n_blocks);
+  }
   return hipGetLastError();
 }
 

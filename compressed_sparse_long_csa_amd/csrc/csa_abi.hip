@@ -164,8 +164,6 @@ static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream)
     if (a.D != 512 || a.rope_dim != 64)
       return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path needs D == 512 and rope_dim == 64", name);
     if (a.H % 16 != 0) return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path needs H %% 16 == 0", name);
-    if (a.idx != nullptr && a.k > 2048)
-      return fail(CSA_ERR_UNSUPPORTED, "%s: MFMA path supports k <= 2048", name);
   } else {
     return fail(CSA_ERR_UNSUPPORTED,
                 "%s: supported formats are all-F32, or q/win/out BF16 with a SPLIT cache", name);

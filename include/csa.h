@@ -195,8 +195,11 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
  *   qhat = RoPE_p(RMSNorm(q[b,h]))           (gamma = q_norm_w or 1, eps)
  *   l_j  = scale * qhat . e_j                (the stored entry is key and value)
  *   out[b,h] = sum_j e^{l_j} e_j / (sum_j e^{l_j} + e^{sinks[h]})
- * The reduction over E runs in tiles of 64 entries in list order, starting
- * from the sink, the same in every variant and batch.
+ * The reduction order over E is fixed per token, the same in every variant
+ * and batch.  F32 path: E in list order from the sink.  MFMA path: four
+ * interleaved slices -- slice w takes list positions [128 s + 32 w, +32) of
+ * the compressed part and window rows [64 t + 16 w, +16) -- each reduced in
+ * order (the sink enters slice 0), then merged in slice order.
  *
  *   q, out   [B, H] rows of D values (q_fmt / out_fmt: F32 or BF16)
  *   kv       rows of D values in kv_fmt (SPLIT, or F32 on the fp32 path)
@@ -205,7 +208,7 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
  *   sinks    [H] float32
  * Paths: all-F32 (q, kv, win, out F32; any D <= 512, H <= 1024); MFMA path
  * (q BF16, kv SPLIT with D = 512, rope_dim = 64, win BF16, out BF16, H a
- * multiple of 16, k <= 2048).  Other combinations: UNSUPPORTED.
+ * multiple of 16).  Other combinations: UNSUPPORTED.
  */
 csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
                               const int64_t* q_pos, const float* q_norm_w, float eps,
