@@ -9,8 +9,9 @@
 //   I[i, s] = sum_h w[i, h] * max(0, q[i, h] . k[s])
 //
 // Decode streams every visible key once, so the kernels are HBM-bound: each
-// wave owns 16-key blocks, loads them straight from global memory into the
-// MFMA operand registers and keeps the query in registers.
+// wave owns 128 keys, issues the loads of all of them (straight from global
+// memory into the MFMA operand registers) before converting its query, and
+// keeps the query in registers for all of them; two waves per SIMD.
 //  * FP8 keys: the products must be exact for the top-k to be reproducible,
 //    and FP8 MFMA accumulation is not, so FP8 values are widened to BF16
 //    (exact) and multiplied on BF16 MFMA with fp32 accumulation.
@@ -19,16 +20,17 @@
 //  * F32: plain fp32 FMAs in dim order.
 // The dims of one 128-dim vector are assigned to k-steps so that each lane
 // reads 32 contiguous bytes; the same permutation is applied to queries and
-// keys, so each dot product is the same sum.  The head sum runs per lane over
-// head blocks in order, then over the 16 lanes of a row group in a fixed
-// butterfly.
+// keys, so each dot product is the same sum.  The MFMA output is heads x
+// keys, so the head sum runs inside a lane (head blocks in order, then the
+// lane's four heads) and then over the four row groups in a fixed order.
 #include "kernels.hpp"
 
 namespace csa {
 
 namespace {
 
-constexpr int kKeysPerWave = 64;                 // 4 blocks of 16 keys
+constexpr int kBatch = 8;                        // 16-key blocks of one wave, loaded together
+constexpr int kKeysPerWave = 16 * kBatch;        // 128 keys, one query load
 constexpr int kWaves = 4;
 constexpr int kKeysPerWg = kKeysPerWave * kWaves;
 
@@ -43,6 +45,66 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// Sum of a lane value over the four 16-lane rows of the wave, in one fixed
+// order ((row0 + row1) + (row2 + row3)); every lane receives the total.
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Work item: (query i, chunk of kKeysPerWg keys); wave wv takes keys
+// [chunk * kKeysPerWg + wv * kKeysPerWave, +kKeysPerWave).  The MFMA output
+// is heads x keys: lane (key j16, heads 4g .. 4g+3 of each 16-head block), so
+// a lane sums its 16 heads (blocks in order, then rows r) and the four row
+// groups are added once.  Key rows are read through a buffer descriptor over
+// the query's N visible rows: rows past N read as zero, and a row address is
+// a 32-bit offset with the block step in the scalar offset.
+struct IdxItem {
+  int i;
+  int64_t N, s0;
+  int nb;                          // 16-key blocks of this wave with keys < N
+  buf_rsrc rs;                     // the query's visible key rows
+};
+
+__device__ __forceinline__ bool idx_item(const IndexerArgs& a, int64_t item, int64_t n_chunk,
+                                         int wv, int row_bytes, IdxItem* it) {
+  it->i = static_cast<int>(item / n_chunk);
+  const int64_t chunk = item % n_chunk;
+  int64_t N = (a.q_pos[it->i] + 1) / a.m;
+  if (N > a.ld) N = a.ld;
+  it->N = N;
+  it->s0 = chunk * kKeysPerWg + wv * kKeysPerWave;
+  if (it->s0 >= N) return false;                      // uniform over the wave (no barriers)
+  const int64_t left = (N - it->s0 + 15) / 16;
+  it->nb = left < kBatch ? static_cast<int>(left) : kBatch;
+  it->rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + a.key_off[it->i] * row_bytes,
+                     static_cast<uint32_t>(N * row_bytes));
+  return true;
+}
+
+__device__ __forceinline__ uint4 buf_load_x4(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                    static_cast<uint32_t>(v[3]));
+}
+
+// max(x, 0) on the bit pattern: a negative float is a negative integer (-0 -> +0)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Score of the 16 keys of one block from its heads x keys MFMA tiles: lane
+// sums its 16 heads (blocks in order, rows r in order), then the row groups.
+template <int NHB>
+__device__ __forceinline__ float head_sum(const f32x4 (&c)[NHB], const float (&wr)[NHB][4]) {
+  float part = 0.0f;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part = fmaf(wr[hb][r], relu(c[hb][r]), part);
+  return rows_sum(part);
+}
+
 // --------------------------------------------------------------- FP8, d = 128
 template <int NHB>   // head blocks of 16
 __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
@@ -50,74 +112,60 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
   constexpr int H = NHB * 16;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, j16 = lane & 15;
-  const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int i = static_cast<int>(item / n_chunk);
-    const int64_t chunk = item % n_chunk;
-    int64_t N = (a.q_pos[i] + 1) / a.m;
-    if (N > a.ld) N = a.ld;
-    const int64_t s0 = chunk * kKeysPerWg + wv * kKeysPerWave;
-    if (chunk * kKeysPerWg >= N) continue;            // uniform over the workgroup
-    if (s0 >= N) continue;                            // uniform over the wave (no barriers below)
-    // query operand: head hb*16 + j16, dims [32g, 32g+32) as 4 k-steps of 8
+    IdxItem it;
+    if (!idx_item(a, item, n_chunk, wv, 128, &it)) continue;
+    const int i = it.i;
+    // key rows: lane (key j16, dims [32g, 32g+32)) = 32 contiguous bytes
+    const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * 128u + g * 32u;
+    uint4 kr[kBatch][2];
+#pragma unroll
+    for (int kb = 0; kb < kBatch; ++kb) {
+      kr[kb][0] = buf_load_x4(it.rs, voff, kb * 2048u);
+      kr[kb][1] = buf_load_x4(it.rs, voff + 16u, kb * 2048u);
+    }
+    // query operand: head hb*16 + j16, dims [32g, 32g+32) as 4 k-steps of 8;
+    // weights of the heads this lane sums: hb*16 + 4g + r
     bf16x8 qb[NHB][4];
-    float wh[NHB];
+    float wr[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const int h = hb * 16 + j16;
-      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + h) * 128 + g * 32);
+      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
       const uint4 v0 = qp[0], v1 = qp[1];
       qb[hb][0] = fp8x8_to_bf16(v0.x, v0.y);
       qb[hb][1] = fp8x8_to_bf16(v0.z, v0.w);
       qb[hb][2] = fp8x8_to_bf16(v1.x, v1.y);
       qb[hb][3] = fp8x8_to_bf16(v1.z, v1.w);
-      wh[hb] = a.w[static_cast<int64_t>(i) * H + h];
+      const float4 wv4 = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+      wr[hb][0] = wv4.x; wr[hb][1] = wv4.y; wr[hb][2] = wv4.z; wr[hb][3] = wv4.w;
     }
-    const int64_t kbase = a.key_off[i];
-    uint4 kr[4][2];
+    float* out = a.scores + static_cast<int64_t>(i) * a.ld + it.s0 + j16;
+    // software pipeline: the MFMAs of block kb run while the head sum of
+    // block kb-1 is computed from its finished tiles
+    f32x4 cp[NHB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t s = s0 + kb * 16 + j16;
-      if (s < N) {
-        const uint4* kp = reinterpret_cast<const uint4*>(keys + (kbase + s) * 128 + g * 32);
-        kr[kb][0] = kp[0];
-        kr[kb][1] = kp[1];
-      } else {
-        kr[kb][0] = make_uint4(0, 0, 0, 0);
-        kr[kb][1] = make_uint4(0, 0, 0, 0);
+    for (int kb = 0; kb <= kBatch; ++kb) {
+      // blocks past N hold zero rows (the buffer range check); their scores are not stored
+      f32x4 cc[NHB];
+      if (kb < kBatch) {
+        const bf16x8 kk[4] = {fp8x8_to_bf16(kr[kb][0].x, kr[kb][0].y), fp8x8_to_bf16(kr[kb][0].z, kr[kb][0].w),
+                              fp8x8_to_bf16(kr[kb][1].x, kr[kb][1].y), fp8x8_to_bf16(kr[kb][1].z, kr[kb][1].w)};
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) cc[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // rows = heads (A), cols = keys (B); the NHB chains interleave
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+            cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t sb = s0 + kb * 16;
-      if (sb >= N) break;
-      const bf16x8 k0 = fp8x8_to_bf16(kr[kb][0].x, kr[kb][0].y);
-      const bf16x8 k1 = fp8x8_to_bf16(kr[kb][0].z, kr[kb][0].w);
-      const bf16x8 k2 = fp8x8_to_bf16(kr[kb][1].x, kr[kb][1].y);
-      const bf16x8 k3 = fp8x8_to_bf16(kr[kb][1].z, kr[kb][1].w);
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        // rows = keys (A), cols = heads (B): lane holds head j16, keys 4g..4g+3
-        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[hb][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[hb][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qb[hb][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qb[hb][3], c, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] = fmaf(wh[hb], fmaxf(c[r], 0.0f), part[r]);
+      if (kb > 0) {
+        const float tot = head_sum<NHB>(cp, wr);
+        if (g == 0 && it.s0 + (kb - 1) * 16 + j16 < it.N) out[(kb - 1) * 16] = tot;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) part[r] += __shfl_xor(part[r], o, 64);
-      }
-      if (j16 < 4) {
-        const int64_t s = sb + g * 4 + j16;
-        const float v = j16 == 0 ? part[0] : j16 == 1 ? part[1] : j16 == 2 ? part[2] : part[3];
-        if (s < N) a.scores[static_cast<int64_t>(i) * a.ld + s] = v;
-      }
+      for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
     }
   }
 }
@@ -132,69 +180,52 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
   constexpr int RB = 68;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, j16 = lane & 15;
-  const uint8_t* keys = static_cast<const uint8_t*>(a.keys);
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int i = static_cast<int>(item / n_chunk);
-    const int64_t chunk = item % n_chunk;
-    int64_t N = (a.q_pos[i] + 1) / a.m;
-    if (N > a.ld) N = a.ld;
-    const int64_t s0 = chunk * kKeysPerWg + wv * kKeysPerWave;
-    if (chunk * kKeysPerWg >= N) continue;
-    if (s0 >= N) continue;
+    IdxItem it;
+    if (!idx_item(a, item, n_chunk, wv, RB, &it)) continue;
+    const int i = it.i;
+    const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * RB;
+    uint4 kc[kBatch];
+    uint32_t ksc[kBatch];
+#pragma unroll
+    for (int kb = 0; kb < kBatch; ++kb) {
+      kc[kb] = buf_load_x4(it.rs, voff + g * 16u, kb * 16u * RB);
+      ksc[kb] = __builtin_amdgcn_raw_buffer_load_b8(it.rs, static_cast<int>(voff + 64u + g),
+                                                    static_cast<int>(kb * 16u * RB), 0);
+    }
     i32x8 qop[NHB];
     int qsc[NHB];
-    float wh[NHB];
+    float wr[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const int h = hb * 16 + j16;
-      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + h) * RB;
-      const uint32_t* cp = reinterpret_cast<const uint32_t*>(row + g * 16);
-      qop[hb] = i32x8{static_cast<int>(cp[0]), static_cast<int>(cp[1]), static_cast<int>(cp[2]),
-                      static_cast<int>(cp[3]), 0, 0, 0, 0};
+      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * RB;
+      const uint4 c4 = *reinterpret_cast<const uint4*>(row + g * 16);
+      qop[hb] = i32x8{static_cast<int>(c4.x), static_cast<int>(c4.y), static_cast<int>(c4.z),
+                      static_cast<int>(c4.w), 0, 0, 0, 0};
       qsc[hb] = row[64 + g];
-      wh[hb] = a.w[static_cast<int64_t>(i) * H + h];
+      const float4 wv4 = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+      wr[hb][0] = wv4.x; wr[hb][1] = wv4.y; wr[hb][2] = wv4.z; wr[hb][3] = wv4.w;
     }
-    const int64_t kbase = a.key_off[i];
-    i32x8 kop[4];
-    int ksc[4];
+    float* out = a.scores + static_cast<int64_t>(i) * a.ld + it.s0 + j16;
+    f32x4 cp[NHB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t s = s0 + kb * 16 + j16;
-      if (s < N) {
-        const uint8_t* row = keys + (kbase + s) * RB;
-        const uint32_t* cp = reinterpret_cast<const uint32_t*>(row + g * 16);
-        kop[kb] = i32x8{static_cast<int>(cp[0]), static_cast<int>(cp[1]), static_cast<int>(cp[2]),
-                        static_cast<int>(cp[3]), 0, 0, 0, 0};
-        ksc[kb] = row[64 + g];
-      } else {
-        kop[kb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        ksc[kb] = 127;
+    for (int kb = 0; kb <= kBatch; ++kb) {
+      f32x4 cc[NHB];
+      if (kb < kBatch) {
+        const i32x8 kop = {static_cast<int>(kc[kb].x), static_cast<int>(kc[kb].y),
+                           static_cast<int>(kc[kb].z), static_cast<int>(kc[kb].w), 0, 0, 0, 0};
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+          cc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qop[hb], kop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, qsc[hb], 0, static_cast<int>(ksc[kb]));
       }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t sb = s0 + kb * 16;
-      if (sb >= N) break;
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop[kb], qop[hb], c, 4, 4, 0, ksc[kb], 0,
-                                                             qsc[hb]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] = fmaf(wh[hb], fmaxf(c[r], 0.0f), part[r]);
+      if (kb > 0) {
+        const float tot = head_sum<NHB>(cp, wr);
+        if (g == 0 && it.s0 + (kb - 1) * 16 + j16 < it.N) out[(kb - 1) * 16] = tot;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) part[r] += __shfl_xor(part[r], o, 64);
-      }
-      if (j16 < 4) {
-        const int64_t s = sb + g * 4 + j16;
-        const float v = j16 == 0 ? part[0] : j16 == 1 ? part[1] : j16 == 2 ? part[2] : part[3];
-        if (s < N) a.scores[static_cast<int64_t>(i) * a.ld + s] = v;
-      }
+      for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
     }
   }
 }
