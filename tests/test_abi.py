@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the built library loads, exports every function
+include/csa.h declares, and rejects bad arguments on the host before any
+device work (no compute call runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_long_csa_amd as csa
+from compressed_sparse_long_csa_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("__")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"libcsa.so does not export {n}"
+
+
+def test_version_status_strings_and_row_bytes(lib):
+    assert lib.csa_abi_version() >= 1
+    lib.csa_status_string.restype = ctypes.c_char_p
+    for code, name in ((0, b"CSA_OK"), (1, b"CSA_ERR_INVALID_ARG"), (2, b"CSA_ERR_UNSUPPORTED")):
+        assert lib.csa_status_string(code) == name
+    lib.csa_row_bytes.restype = ctypes.c_size_t
+    for fmt in (csa.F32, csa.BF16, csa.FP8, csa.MXFP4, csa.SPLIT):
+        assert lib.csa_row_bytes(fmt, 512, 64) == synth.row_bytes(fmt, 512, 64)
+    assert lib.csa_row_bytes(csa.SPLIT, 512, 64) == 576          # 448 FP8 + 64 BF16 dims
+    assert lib.csa_row_bytes(csa.MXFP4, 128, 0) == 68             # 64 code bytes + 4 scales
+    assert lib.csa_row_bytes(csa.MXFP4, 100, 0) == 0              # not a multiple of 32
+    assert lib.csa_row_bytes(99, 512, 64) == 0
+
+
+def _last_error(lib):
+    lib.csa_last_error.restype = ctypes.c_char_p
+    return lib.csa_last_error().decode()
+
+
+def _fake(n=1):
+    """A non-null host address: argument checks run before any pointer is used."""
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_topk_argument_errors(lib):
+    p = _fake()
+    for ld, nq, k, want in ((100, 1, 0, INVALID), (100, 1, 4097, INVALID), (0, 1, 8, INVALID),
+                            ((1 << 28) + 1, 1, 8, INVALID), (100, -1, 8, INVALID)):
+        st = lib.topk_select(p, ctypes.c_int64(ld), nq, None, k, p, None, None)
+        assert st == want, (ld, nq, k, st)
+        assert "topk_select" in _last_error(lib)
+    assert lib.topk_select(None, ctypes.c_int64(100), 1, None, 8, None, None, None) == INVALID
+    assert lib.topk_select(None, ctypes.c_int64(100), 0, None, 8, None, None, None) == OK
+
+
+def test_compress_argument_errors(lib):
+    p = _fake()
+    base = dict(x=p, x_fmt=csa.F32, gate=p, gate_cols=1, n_tok=8, D=512, m=4, nseg=1, off=p, pos0=p,
+                row=p, normalize=1, norm_w=None, eps=1e-6, R=64, base=1e4, out=p, out_fmt=csa.SPLIT)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.csa_compress(a["x"], a["x_fmt"], a["gate"], a["gate_cols"], ctypes.c_int64(a["n_tok"]),
+                                a["D"], a["m"], a["nseg"], a["off"], a["pos0"], a["row"], a["normalize"],
+                                a["norm_w"], ctypes.c_float(a["eps"]), a["R"], ctypes.c_float(a["base"]),
+                                a["out"], a["out_fmt"], None)
+    assert call(n_tok=7) == INVALID                 # n_tok % m != 0
+    assert call(m=0) == INVALID
+    assert call(gate_cols=3) == INVALID             # neither 1 nor D
+    assert call(R=63) == INVALID                    # odd RoPE dims
+    assert call(out_fmt=csa.MXFP4, D=100, R=0) == INVALID
+    assert call(R=0) == INVALID                     # SPLIT needs RoPE dims
+    assert call(x_fmt=csa.FP8) == INVALID
+    assert call(D=8192) == UNSUPPORTED
+    assert call(x=None) == INVALID
+    assert call(eps=-1.0) == INVALID
+
+
+def test_attention_argument_errors(lib):
+    p = _fake()
+
+    def call(q_fmt=csa.BF16, kv_fmt=csa.SPLIT, win_fmt=csa.BF16, out_fmt=csa.BF16, D=512, R=64, H=64,
+             variant=0, q=p):
+        return lib.hybrid_attn_decode(q, q_fmt, 2, H, D, p, None, ctypes.c_float(1e-6), R,
+                                      ctypes.c_float(1e4), p, kv_fmt, p, 4, p, 512, p, win_fmt, 128,
+                                      p, p, ctypes.c_float(0.04), p, out_fmt, variant, None)
+    assert call(kv_fmt=csa.FP8) == UNSUPPORTED       # neither the all-F32 nor the MFMA path
+    assert call(D=256) == UNSUPPORTED                # the MFMA path is D = 512, 64 RoPE dims
+    assert call(H=40) == UNSUPPORTED                 # heads in tiles of 16
+    assert call(q_fmt=csa.F32, kv_fmt=csa.F32, win_fmt=csa.F32, out_fmt=csa.F32, D=640) == UNSUPPORTED
+    assert call(variant=7) == INVALID
+    assert call(q=None) == INVALID
+    assert "hybrid_attn_decode" in _last_error(lib)
+
+
+def test_indexer_argument_errors(lib):
+    p = _fake()
+
+    def call(fmt=csa.FP8, H=64, d=128, nq=2, m=4):
+        return lib.indexer_score(p, p, nq, H, d, p, fmt, p, p, m, p, ctypes.c_int64(1024), None)
+    assert call(fmt=csa.SPLIT) in (INVALID, UNSUPPORTED)
+    assert call(d=96) in (INVALID, UNSUPPORTED)      # FP8 / MXFP4 keys are 128-dim
+    assert call(H=40) in (INVALID, UNSUPPORTED)
+    assert call(m=0) == INVALID
+    assert call(nq=0) == OK
