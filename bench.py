@@ -16,8 +16,11 @@ of 16 sequences of 65,536 tokens (16,384 compressed entries each, top-k 512,
 FP8 indexer 64 x 128, 64 query heads, head dim 512).
 
 Prints one JSON line.  `roofline` is measured for the dominant kernel
-(indexer_score) with events around its launches on its stream;
-`cpu_baseline` times the float64 oracle on a bounded sample on the host.
+(indexer_score, which moves most of the step's bytes) with events around its
+launches on its stream; `kernels` gives every kernel's duration, algorithmic
+bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
+float64 oracle on a bounded sample on the host.  `--copy-probe MIB` only runs
+a plain copy of known size, the reference for rocprofv3 byte counters.
 """
 import argparse
 import hashlib
@@ -37,6 +40,7 @@ from compressed_sparse_long_csa_amd import synth  # noqa: E402
 
 METRIC = "CSA/HCA decode query-tokens/s and achieved HBM GB/s at 64K-1M context"
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 EPS, BASE = 1e-6, 10000.0
 
 
@@ -144,6 +148,15 @@ def algorithmic_bytes(W):
     return step_bytes, per_kernel
 
 
+def algorithmic_flops(W):
+    """Matrix FLOPs of the two contraction kernels (2 per multiply-add)."""
+    inp, c = W["inp"], W["c"]
+    N = inp.n_ent.astype(np.int64)
+    sel = np.minimum(c["k"], N) + inp.win_len.astype(np.int64)
+    return {"indexer_score": int(2 * N.sum() * c["H_I"] * W["d_I"]),
+            "hybrid_attn_decode": int(2 * 2 * sel.sum() * c["H"] * W["D"])}
+
+
 def time_graph(step, steps, warmup):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -167,19 +180,42 @@ def time_graph(step, steps, warmup):
     return e0.elapsed_time(e1) / steps, g
 
 
-def time_kernels(kernels, steps):
-    """Average duration of every kernel, with events recorded around each
-    launch on the stream the kernel runs on (torch's current stream)."""
-    ev = {n: [] for n, _ in kernels}
+def _event_pairs(f, steps):
+    """Mean time between two events recorded around f() on the current stream.
+    A spin kernel is queued first, so every launch of the loop is enqueued
+    before the GPU reaches it and host launch latency never sits between two
+    events."""
+    ev = []
+    torch.cuda._sleep(int(2e7))
     for _ in range(steps):
-        for n, f in kernels:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            f()
-            b.record()
-            ev[n].append((a, b))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        f()
+        b.record()
+        ev.append((a, b))
     torch.cuda.synchronize()
-    return {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_kernels(kernels, steps):
+    """Average device duration (us) of every kernel: events around each launch
+    on the stream the kernel runs on (torch's current stream), less the time
+    between two events with nothing in between."""
+    empty = _event_pairs(lambda: None, steps)
+    return {n: _event_pairs(f, steps) - empty for n, f in kernels}, empty
+
+
+def copy_probe(mb, reps):
+    """A plain elementwise copy (y = x * 1) of mb MiB, reps times: the
+    known-size reference (mb MiB read, mb MiB written per launch) for
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings."""
+    n = mb * 1024 * 1024 // 4
+    x = torch.ones(n, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_read_bytes_per_launch": n * 4, "launches": reps}), flush=True)
 
 
 def spot_check(W):
@@ -267,12 +303,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(decode shards by sequence; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
     csa.load_library()
     W = build_workload()
     step, kernels = make_step(W, check=True)
@@ -280,12 +321,20 @@ def main():
     torch.cuda.synchronize()
     step, kernels = make_step(W, check=False)
     ms, _graph = time_graph(step, args.steps, args.warmup)
-    per_us = time_kernels(kernels, max(20, args.steps // 4))
+    per_us, event_floor_us = time_kernels(kernels, max(20, min(100, args.steps)))
     step_bytes, kbytes = algorithmic_bytes(W)
     err = spot_check(W)
     B = W["B"]
-    dom = "indexer_score"
-    ach = kbytes[dom] / (per_us[dom] * 1e-6) / 1e9
+    dom = "indexer_score"                    # the kernel that moves most of the step's bytes
+    flops = algorithmic_flops(W)
+    kern = {}
+    for n in per_us:
+        t = per_us[n] * 1e-6
+        kern[n] = {"us": per_us[n], "bytes": kbytes[n], "gbps": kbytes[n] / t / 1e9,
+                   "hbm_frac": kbytes[n] / t / 1e9 / HBM_PEAK_GBPS}
+        if n in flops:
+            kern[n].update({"tflops": flops[n] / t / 1e12, "mfma_frac": flops[n] / t / 1e12 / BF16_PEAK_TFLOPS})
+    ach = kern[dom]["gbps"]
     line = {
         "metric": METRIC,
         "value": B / (ms * 1e-3),
@@ -306,8 +355,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_record(dom),
                      "kernel": dom, "bytes_per_launch": kbytes[dom], "us_per_launch": per_us[dom]},
-        "kernels_us": per_us,
-        "kernel_bytes": kbytes,
+        "kernels": kern,
+        "event_pair_floor_us": event_floor_us,
         "check_max_err_over_rms": err,
     }
     if not args.no_cpu_baseline:

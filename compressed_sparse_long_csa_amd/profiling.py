@@ -1,0 +1,92 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+  python -m compressed_sparse_long_csa_amd.profiling stats RESULTS_DB
+      per-kernel launch count and duration (avg / median / min, microseconds)
+      from a `rocprofv3 --kernel-trace` database (its `kernels` view).
+
+  python -m compressed_sparse_long_csa_amd.profiling traffic --kernel SUBSTR \\
+      --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-bytes N \\
+      --source FILE --out JSON
+      HBM bytes per launch of the kernels whose name contains SUBSTR, from two
+      `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per
+      dispatch).  Each counter is scaled by what it reads for a plain copy
+      kernel that moves a known number of bytes (N read, N written), so the
+      figure does not depend on the counter's unit or channel coverage.  The
+      record keeps the sha256 of the kernel's source file: a reader can tell
+      whether the counters were taken on the current kernel.
+"""
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import sqlite3
+import statistics
+import sys
+
+
+def kernel_stats(db):
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration from kernels").fetchall()
+    d = collections.defaultdict(list)
+    for name, dur in rows:
+        d[name].append(dur / 1000.0)
+    tot = sum(sum(v) for v in d.values()) or 1.0
+    out = []
+    for name, v in sorted(d.items(), key=lambda x: -sum(x[1])):
+        out.append(dict(kernel=name, launches=len(v), avg_us=statistics.mean(v),
+                        median_us=statistics.median(v), min_us=min(v), share=sum(v) / tot))
+    return out
+
+
+def counter_per_dispatch(path, substr, counter):
+    vals = collections.defaultdict(float)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {substr!r} in {path}")
+    return statistics.mean(vals.values()), len(vals)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("db")
+    t = sub.add_parser("traffic")
+    for a in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--source", "--out"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-kernel", default="elementwise")
+    t.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy launch")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(f"{'kernel':90s} {'launches':>8s} {'avg_us':>9s} {'median':>9s} {'min':>9s} {'share':>6s}")
+        for r in kernel_stats(args.db):
+            print(f"{r['kernel'][:90]:90s} {r['launches']:8d} {r['avg_us']:9.2f} {r['median_us']:9.2f} "
+                  f"{r['min_us']:9.2f} {100 * r['share']:5.1f}%")
+        return
+    f_kib, nf = counter_per_dispatch(args.fetch, args.kernel, "FETCH_SIZE")
+    w_kib, nw = counter_per_dispatch(args.write, args.kernel, "WRITE_SIZE")
+    cf_kib, _ = counter_per_dispatch(args.copy_fetch, args.copy_kernel, "FETCH_SIZE")
+    cw_kib, _ = counter_per_dispatch(args.copy_write, args.copy_kernel, "WRITE_SIZE")
+    f_scale = args.copy_bytes / (cf_kib * 1024.0)
+    w_scale = args.copy_bytes / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    with open(args.source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    rec = dict(kernel=args.kernel, dispatches=[nf, nw], fetch_kib_per_dispatch=f_kib,
+               write_kib_per_dispatch=w_kib, copy_bytes=args.copy_bytes,
+               copy_fetch_kib=cf_kib, copy_write_kib=cw_kib, fetch_scale=f_scale,
+               write_scale=w_scale, fetch_bytes=fetch_b, write_bytes=write_b,
+               bytes_per_launch=fetch_b + write_b, source=args.source, source_sha256=sha)
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+    json.dump(rec, sys.stdout, indent=1)
+    print()
+
+
+if __name__ == "__main__":
+    main()
