@@ -9,11 +9,15 @@ path, every kernel from libcsa:
   4. indexer_score -- ReLU multi-head scores over every visible entry
   5. topk_select   -- the k best entries, ascending
   6. hybrid_attn_decode -- sink MQA over the selected entries + window
-Inputs are seeded synthetic tensors already resident in HBM.  The step is
-captured once in a HIP graph and replayed; W warm-up steps, then K timed
-steps between two synchronised events.  The workload is the CSA decode batch
-of 16 sequences of 65,536 tokens (16,384 compressed entries each, top-k 512,
-FP8 indexer 64 x 128, 64 query heads, head dim 512).
+Inputs are seeded synthetic tensors already resident in HBM.  The per-layer
+state a step reads (KV cache, index keys, window rows) exists in R copies
+(default 13, about 2.4 GB) stepped in turn, so that it cannot stay in the
+256 MB last-level cache between steps, as in a model whose every layer has its
+own cache; `value_one_warm_cache` repeats one copy.  Each copy's step is
+captured in a HIP graph; W warm-up steps, then exactly K timed steps between
+two synchronised events.  The workload is the CSA decode batch of 16
+sequences of 65,536 tokens (16,384 compressed entries each, top-k 512, FP8
+indexer 64 x 128, 64 query heads, head dim 512).
 
 Prints one JSON line.  `roofline` is measured for the dominant kernel
 (indexer_score, which moves most of the step's bytes) with events around its
@@ -82,6 +86,20 @@ def build_workload(cfg_id=2, B=None, L=None, seed=2):
     W["idx"] = torch.empty((Bn, c["k"]), dtype=torch.int32, device="cuda")
     W["out"] = torch.empty((Bn, c["H"], D), dtype=torch.bfloat16, device="cuda")
     return W
+
+
+def make_replicas(W, R):
+    """R copies of the per-layer state a decode step reads (KV cache, index
+    keys, window rows); everything else is shared.  Stepping through the
+    replicas in turn keeps the working set (R x ~40 MB) above twice the
+    256 MB last-level cache, so the kernels read HBM, as a model whose every
+    layer has its own cache does."""
+    reps = [W]
+    for _ in range(R - 1):
+        Wr = dict(W)
+        Wr["kv"], Wr["keys"], Wr["win"] = W["kv"].clone(), W["keys"].clone(), W["win"].clone()
+        reps.append(Wr)
+    return reps
 
 
 def make_step(W, check=False):
@@ -157,52 +175,64 @@ def algorithmic_flops(W):
             "hybrid_attn_decode": int(2 * 2 * sel.sum() * c["H"] * W["D"])}
 
 
-def time_graph(step, steps, warmup):
+def time_graph(steps_r, steps, warmup):
+    """One captured graph per replica's step; W warm-up steps, then exactly
+    `steps` timed steps, replica r = i mod R, between two synchronised events.
+    Returns ms per step."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for _ in range(max(1, warmup)):
-            step()
+        for st in steps_r:
+            st()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
+    graphs = []
+    for st in steps_r:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st()
+        graphs.append(g)
+    R = len(graphs)
+    for i in range(warmup):
+        graphs[i % R].replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
-        g.replay()
+    for i in range(steps):
+        graphs[i % R].replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, g
+    return e0.elapsed_time(e1) / steps
 
 
-def _event_pairs(f, steps):
-    """Mean time between two events recorded around f() on the current stream.
-    A spin kernel is queued first, so every launch of the loop is enqueued
-    before the GPU reaches it and host launch latency never sits between two
-    events."""
+def _event_pairs(fs, steps):
+    """Mean time between two events recorded around f() on the current stream,
+    f taken in turn from fs.  A spin kernel is queued first, so every launch of
+    the loop is enqueued before the GPU reaches it and host launch latency never
+    sits between two events."""
     ev = []
     torch.cuda._sleep(int(2e7))
-    for _ in range(steps):
+    for i in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        f()
+        fs[i % len(fs)]()
         b.record()
         ev.append((a, b))
     torch.cuda.synchronize()
     return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def time_kernels(kernels, steps):
-    """Average device duration (us) of every kernel: events around each launch
-    on the stream the kernel runs on (torch's current stream), less the time
-    between two events with nothing in between."""
-    empty = _event_pairs(lambda: None, steps)
-    return {n: _event_pairs(f, steps) - empty for n, f in kernels}, empty
+def time_kernels(kernels_r, steps):
+    """Average device duration (us) of every kernel, launches rotating over the
+    replicas: events around each launch on the stream the kernel runs on
+    (torch's current stream), less the time between two events with nothing in
+    between."""
+    empty = _event_pairs([lambda: None], steps)
+    names = [n for n, _ in kernels_r[0]]
+    out = {}
+    for j, n in enumerate(names):
+        out[n] = _event_pairs([kr[j][1] for kr in kernels_r], steps) - empty
+    return out, empty
 
 
 def copy_probe(mb, reps):
@@ -303,6 +333,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--replicas", type=int, default=13,
+                    help="per-layer state copies stepped in turn (1 = one warm cache)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -316,12 +348,16 @@ def main():
         return
     csa.load_library()
     W = build_workload()
-    step, kernels = make_step(W, check=True)
+    step, _ = make_step(W, check=True)
     step()                                   # validated eager pass
     torch.cuda.synchronize()
-    step, kernels = make_step(W, check=False)
-    ms, _graph = time_graph(step, args.steps, args.warmup)
-    per_us, event_floor_us = time_kernels(kernels, max(20, min(100, args.steps)))
+    reps = make_replicas(W, max(1, args.replicas))
+    made = [make_step(Wr, check=False) for Wr in reps]
+    ms_warm = time_graph([made[0][0]], args.steps, args.warmup)
+    ms = time_graph([m[0] for m in made], args.steps, args.warmup)
+    per_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)))
+    made[0][0]()                             # replica 0 last, for the spot check
+    torch.cuda.synchronize()
     step_bytes, kbytes = algorithmic_bytes(W)
     err = spot_check(W)
     B = W["B"]
@@ -349,7 +385,9 @@ def main():
         "config": {"workload": "csa_decode_b16_ctx65536", "batch": B, "context": 65536,
                    "entries_per_seq": int(W["inp"].n_ent[0]), "top_k": W["c"]["k"],
                    "heads": W["c"]["H"], "head_dim": W["D"], "indexer": "fp8 64x128",
-                   "window": 128, "graph": True, "variant": "auto"},
+                   "window": 128, "graph": True, "variant": "auto",
+                   "state_replicas": len(reps)},
+        "value_one_warm_cache": B / (ms_warm * 1e-3),
         "hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
         "step_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
