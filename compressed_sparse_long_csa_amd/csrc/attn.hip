@@ -138,12 +138,12 @@ constexpr int kRowBf16 = 2 * kD;                        // 1024 bytes per window
 constexpr int kChunksSplit = kRowSplit / 16;            // 36 chunks of 16 bytes
 constexpr int kPitchSplit = kRowSplit + 16;             // LDS row pitch: rows land on distinct banks
 constexpr int kPitchWin = kRowBf16 + 16;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kStepE = 32;                              // compressed entries per wave step
-constexpr int kStepW = 16;                              // window rows per wave step
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;                   // two waves per SIMD
+constexpr int kStepE = 16;                              // compressed entries per wave step
+constexpr int kStepW = 8;                               // window rows per wave step
 constexpr int kBufBytes = kStepE * kPitchSplit;         // one step's rows (>= kStepW * kPitchWin)
-constexpr int kPPitch = 40;                             // padded rows of the P arrays
+constexpr int kPPitch = 20;                             // padded rows of the P arrays
 constexpr float kPScale = 256.0f;                       // probabilities are stored x 2^8
 static_assert(kStepW * kPitchWin <= kBufBytes, "window step must fit a buffer");
 
@@ -164,6 +164,7 @@ struct __align__(16) AttnSmem {
   float rope_cs[kR / 2][2];        // cos, sin of the query's RoPE angles
   float ml[kWaves][2][16];         // per wave: running max and sum of each head
 };
+static_assert(sizeof(AttnSmem) <= 160 * 1024, "LDS budget of one workgroup per CU");
 
 __device__ __forceinline__ const lds_u8* lds_ptr(const uint8_t* p) {
   // the buffers live in LDS; a C-style cast changes the address space
@@ -223,8 +224,8 @@ __device__ __forceinline__ float row_sum4(float v) {
 }
 
 // Per-query description of the attended list.  Wave w takes, in step s < ns,
-// list positions [128 s + 32 w, +32) of the compressed entries, then in step
-// ns + t window rows [64 t + 16 w, +16).  Rows are read through buffer
+// list positions [128 s + 16 w, +16) of the compressed entries, then in step
+// ns + t window rows [64 t + 8 w, +8).  Rows are read through buffer
 // descriptors over the query's own cache rows and window rows, so a row
 // address is a scalar byte offset.
 struct Work {
@@ -234,7 +235,7 @@ struct Work {
   buf_rsrc kv_rs, win_rs;
 };
 
-// Lane-held entry of the compressed step `step` (lanes < 32) and its validity.
+// Lane-held entry of the compressed step `step` (lanes < 16) and its validity.
 __device__ __forceinline__ int step_entry(const Work& w, int step, int wv, bool* ok) {
   const int lane = threadIdx.x & 63;
   *ok = false;
@@ -276,22 +277,19 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
                                              16, lane * 16, src * kRowBf16, 0, 0);
   }
   const int nv = w.win_count - j0;
-  return nv >= kStepW ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+  return nv >= kStepW ? (1u << kStepW) - 1u : (nv <= 0 ? 0u : (1u << nv) - 1u);
 }
 
-// Online-softmax update of head j16 from this lane's logits t (log2 domain):
-// returns alpha and writes the probabilities p = 2^(t - m_new).
-template <int NV>
-__device__ __forceinline__ float softmax_step(const float (&t)[NV], float (&pv)[NV], float& m_run,
+// Online-softmax update of head j16 from this lane's 4 logits t (log2
+// domain): returns alpha and writes the probabilities p = 2^(t - m_new).
+__device__ __forceinline__ float softmax_step(const float (&t)[4], float (&pv)[4], float& m_run,
                                               float& l_run) {
-  float mx = t[0];
-#pragma unroll
-  for (int r = 1; r < NV; ++r) mx = fmaxf(mx, t[r]);
+  const float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
   const float m_new = fmaxf(m_run, row_max4(mx));
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   float ps = 0.0f;
 #pragma unroll
-  for (int r = 0; r < NV; ++r) {
+  for (int r = 0; r < 4; ++r) {
     pv[r] = __builtin_amdgcn_exp2f(t[r] - m_new);
     ps += pv[r];
   }
@@ -301,7 +299,10 @@ __device__ __forceinline__ float softmax_step(const float (&t)[NV], float (&pv)[
 }
 
 // The entry loop of one wave.  NB output blocks of 16 dims starting at dbase,
-// the first NF of them FP8 dims (the rest the BF16 RoPE dims).
+// the first NF of them FP8 dims (the rest the BF16 RoPE dims).  A step holds
+// 16 compressed entries (or 8 window rows); the MFMA tiles are 16 rows and 32
+// (16) deep, so the second half of a tile multiplies probabilities set to zero
+// by rows of the same step (finite data) -- it adds nothing.
 template <int NB, int NF>
 __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, const bf16x8 (&qb)[kD / 32],
                                            float ch, int dbase, float& m_run, float& l_run,
@@ -318,71 +319,58 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
     }
     const uint8_t* T = ws.buf[bi];
     float alpha;
-    if (step < w.ns) {
-      // -------- logits of the step's 32 entries (two 16-row blocks) x 16 heads.
+    const bool split = step < w.ns;
+    if (split) {
+      // -------- logits of the step's 16 entries (rows) x 16 heads (cols).
       // Every operand read is issued before the math so the LDS latency
-      // overlaps, and the two blocks' MFMA chains interleave.
-      long ka[2][kDF8 / 32];
-      bf16x8 kr[2][kR / 32];
+      // overlaps; two partial chains (even / odd k-steps) interleave.
+      const uint8_t* rowp = T + j16 * kPitchSplit + g * 8;
+      long ka[kDF8 / 32];
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        const uint8_t* rowp = T + (bk * 16 + j16) * kPitchSplit + g * 8;
-#pragma unroll
-        for (int ks = 0; ks < kDF8 / 32; ++ks) ka[bk][ks] = lds_read_b64(rowp + ks * 32);
-#pragma unroll
-        for (int ks = 0; ks < kR / 32; ++ks)
-          kr[bk][ks] = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + g * 8 + ks * 64);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-      for (int ks = 0; ks < kDF8 / 32; ++ks)
-#pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
-          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(ka[bk][ks]), qb[ks], s[bk], 0, 0, 0);
+      for (int ks = 0; ks < kDF8 / 32; ++ks) ka[ks] = lds_read_b64(rowp + ks * 32);
+      bf16x8 kr[kR / 32];
 #pragma unroll
       for (int ks = 0; ks < kR / 32; ++ks)
+        kr[ks] = *reinterpret_cast<const bf16x8*>(rowp + kDF8 + g * 8 + ks * 64);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 s2[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
-          s[bk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[bk][ks], qb[kDF8 / 32 + ks], s[bk], 0, 0, 0);
-      // lane holds head j16, entries 16 bk + 4 g + r
-      float t[8], pv[8];
+      for (int ks = 0; ks < kDF8 / 32; ++ks)
+        s2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(ka[ks]), qb[ks], s2[ks & 1], 0, 0, 0);
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
+      for (int ks = 0; ks < kR / 32; ++ks)
+        s2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[ks], qb[kDF8 / 32 + ks], s2[ks & 1], 0, 0, 0);
+      const f32x4 s = s2[0] + s2[1];
+      // lane holds head j16, entries 4 g + r
+      float t[4], pv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (vmask >> (bk * 16 + g * 4 + r)) & 1u;
-          t[bk * 4 + r] = ok ? s[bk][r] * ch : -INFINITY;
-        }
-      alpha = softmax_step<8>(t, pv, m_run, l_run);
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = (vmask >> (g * 4 + r)) & 1u;
+        t[r] = ok ? s[r] * ch : -INFINITY;
+      }
+      alpha = softmax_step(t, pv, m_run, l_run);
       // probabilities to this wave's LDS in the P^T operand layout [head][entry]
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
-        const int e0 = bk * 16 + g * 4;
-        const float v0 = pv[bk * 4] * kPScale, v1 = pv[bk * 4 + 1] * kPScale;
-        const float v2 = pv[bk * 4 + 2] * kPScale, v3 = pv[bk * 4 + 3] * kPScale;
-        if (NF > 0) {
-          const uint32_t h01 = fp8x2(v0, v1), h23 = fp8x2(v2, v3);
-          const f32x2 d01 = fp8x2_to_f32(h01), d23 = fp8x2_to_f32(h23);
-          const uint32_t l01 = fp8x2(v0 - d01[0], v1 - d01[1]), l23 = fp8x2(v2 - d23[0], v3 - d23[1]);
-          *reinterpret_cast<uint32_t*>(&ws.phi[j16][e0]) = h01 | (h23 << 16);
-          *reinterpret_cast<uint32_t*>(&ws.plo[j16][e0]) = l01 | (l23 << 16);
-        }
-        if (NF < NB) {
-          uint2 bb;
-          bb.x = bf16x2_rne(v0, v1);
-          bb.y = bf16x2_rne(v2, v3);
-          *reinterpret_cast<uint2*>(&ws.pbf[j16][e0]) = bb;
-        }
+      const float v0 = pv[0] * kPScale, v1 = pv[1] * kPScale, v2 = pv[2] * kPScale, v3 = pv[3] * kPScale;
+      if (NF > 0) {
+        const uint32_t h01 = fp8x2(v0, v1), h23 = fp8x2(v2, v3);
+        const f32x2 d01 = fp8x2_to_f32(h01), d23 = fp8x2_to_f32(h23);
+        const uint32_t l01 = fp8x2(v0 - d01[0], v1 - d01[1]), l23 = fp8x2(v2 - d23[0], v3 - d23[1]);
+        *reinterpret_cast<uint32_t*>(&ws.phi[j16][g * 4]) = h01 | (h23 << 16);
+        *reinterpret_cast<uint32_t*>(&ws.plo[j16][g * 4]) = l01 | (l23 << 16);
+      }
+      if (NF < NB) {
+        uint2 bb;
+        bb.x = bf16x2_rne(v0, v1);
+        bb.y = bf16x2_rne(v2, v3);
+        *reinterpret_cast<uint2*>(&ws.pbf[j16][g * 4]) = bb;
       }
     } else {
-      // -------- window step: 16 BF16 rows x 16 heads
-      const uint8_t* rowp = T + j16 * kPitchWin + g * 16;
+      // -------- window step: 8 BF16 rows (tile rows 8..15 repeat them, masked)
+      const uint8_t* rowp = T + (j16 & (kStepW - 1)) * kPitchWin + g * 16;
       bf16x8 kw[kD / 32];
 #pragma unroll
       for (int ks = 0; ks < kD / 32; ++ks) kw[ks] = *reinterpret_cast<const bf16x8*>(rowp + ks * 64);
       __builtin_amdgcn_sched_barrier(0);
-      // two partial chains (even / odd k-steps), added once at the end
       f32x4 s2[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
       for (int ks = 0; ks < kD / 32; ++ks)
@@ -394,30 +382,35 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
         const bool ok = (vmask >> (g * 4 + r)) & 1u;
         t[r] = ok ? s[r] * ch : -INFINITY;
       }
-      alpha = softmax_step<4>(t, pv, m_run, l_run);
-      uint2 bb;
-      bb.x = bf16x2_rne(pv[0] * kPScale, pv[1] * kPScale);
-      bb.y = bf16x2_rne(pv[2] * kPScale, pv[3] * kPScale);
-      *reinterpret_cast<uint2*>(&ws.pbf[j16][g * 4]) = bb;
+      alpha = softmax_step(t, pv, m_run, l_run);
+      if (g < 2) {
+        uint2 bb;
+        bb.x = bf16x2_rne(pv[0] * kPScale, pv[1] * kPScale);
+        bb.y = bf16x2_rne(pv[2] * kPScale, pv[3] * kPScale);
+        *reinterpret_cast<uint2*>(&ws.pbf[j16][g * 4]) = bb;
+      }
     }
     if (__ballot(alpha != 1.0f) != 0ull) {              // the running max moved for some head
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[i] *= alpha;
     }
     __builtin_amdgcn_wave_barrier();
-    if (step < w.ns) {
-      // -------- P.V over the 32 entries: rows = dims, cols = heads
-      const int ebase = g * 8;
+    if (split) {
+      // -------- P.V: rows = dims, cols = heads, K = 32 entries of which 16 are
+      // this step's (lane groups 0, 1) and 16 carry p = 0 (groups 2, 3)
+      const int ebase = (g & 1) * 8;
       long phv = 0, plv = 0;
       bf16x8 pbv = {};
-      if (NF > 0) {
-        phv = lds_read_b64(&ws.phi[j16][ebase]);
-        plv = lds_read_b64(&ws.plo[j16][ebase]);
+      if (g < 2) {
+        if (NF > 0) {
+          phv = lds_read_b64(&ws.phi[j16][ebase]);
+          plv = lds_read_b64(&ws.plo[j16][ebase]);
+        }
+        if (NF < NB) pbv = *reinterpret_cast<const bf16x8*>(&ws.pbf[j16][ebase]);
       }
-      if (NF < NB) pbv = *reinterpret_cast<const bf16x8*>(&ws.pbf[j16][ebase]);
       // fp8 dims: lane j of group g supplies row (ebase + j/2), bytes d0 + 8*(j%2)
       const uint8_t* b8 = T + (ebase + (j16 >> 1)) * kPitchSplit + dbase + 8 * (j16 & 1);
-      // bf16 RoPE dims: lane j supplies row (ebase + j/4), dims d0 + 4*(j%4)
+      // bf16 RoPE dims: lane j supplies row (ebase + j/4) and row (ebase + 4 + j/4)
       const uint8_t* b16 = T + (ebase + (j16 >> 2)) * kPitchSplit + kDF8 +
                            (dbase + NF * 16 - kDF8) * 2 + 8 * (j16 & 3);
       long v8[NF > 0 ? NF : 1];
@@ -439,9 +432,11 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
       for (int i = 0; i < NB - NF; ++i)
         acc[NF + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v16[i], pbv, acc[NF + i], 0, 0, 0);
     } else {
-      const bf16x4 pbw = *reinterpret_cast<const bf16x4*>(&ws.pbf[j16][g * 4]);
-      // lane j of group g supplies row (4 g + j/4), dims d0 + 4*(j%4)
-      const uint8_t* b16 = T + (g * 4 + (j16 >> 2)) * kPitchWin + dbase * 2 + 8 * (j16 & 3);
+      // K = 16 rows: this step's 8 (lane groups 0, 1) and 8 with p = 0
+      bf16x4 pbw = {};
+      if (g < 2) pbw = *reinterpret_cast<const bf16x4*>(&ws.pbf[j16][g * 4]);
+      // lane j of group g supplies row (4 (g % 2) + j/4), dims d0 + 4*(j%4)
+      const uint8_t* b16 = T + ((g & 1) * 4 + (j16 >> 2)) * kPitchWin + dbase * 2 + 8 * (j16 & 3);
       bf16x4 vw[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) vw[i] = tr16(b16 + i * 32);
@@ -454,14 +449,15 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
 
 // DVS = number of workgroups sharing one (query, 16-head tile): each owns
 // 512 / DVS output dims; every wave of it accumulates all of them over its
-// own entries, and the four partial states are merged at the end in wave order.
+// own entries, and the eight partial states are merged at the end in wave
+// order.
 template <int DVS>
 __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_units,
                                                              int n_pad) {
   constexpr int DWG = kD / DVS;        // output dims of this workgroup
   constexpr int NB = DWG / 16;         // 16-dim MFMA blocks
   // the last slice holds the BF16 RoPE dims: its first NFR blocks are FP8 dims
-  constexpr int NFR = (kDF8 - (kD - DWG)) / 16;
+  constexpr int NFR = (kDF8 - (kD - DWG)) > 0 ? (kDF8 - (kD - DWG)) / 16 : 0;
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
 
@@ -498,11 +494,13 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                        static_cast<uint32_t>(w.win_count) * kRowBf16);
 
-  // first step's rows go out before anything else
+  // first step's rows go out before anything else -- except in wave 0, whose
+  // two buffers hold the query staging copy until the prologue is done
   bool ok0, ok1;
   const int e0 = step_entry(w, 0, wv, &ok0);
   const int e1 = step_entry(w, 1, wv, &ok1);
-  const uint32_t vmask0 = w.n_steps > 0 ? issue_step(w, 0, wv, e0, ok0, ws.buf[0]) : 0u;
+  uint32_t vmask0 = 0u;
+  if (wv != 0 && w.n_steps > 0) vmask0 = issue_step(w, 0, wv, e0, ok0, ws.buf[0]);
 
   if (tid < kR / 2) {
     float sn, cs;
@@ -512,16 +510,16 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
 
   // ---------------- prologue: qhat = RoPE(RMSNorm(q)); wave w prepares heads
-  // 4w .. 4w+3 into a bf16 staging copy (in wave 0's second buffer, free until
-  // its first DMA of step 1), then every lane takes its QK operand from it.
-  uint16_t(*qbf)[kD] = reinterpret_cast<uint16_t(*)[kD]>(sm.wave[0].buf[1]);
+  // 2w, 2w+1 (lane: head 2w + lane/32, dims [16 (lane%32), +16)) into a bf16
+  // staging copy in wave 0's buffers, then every lane takes its QK operand.
+  uint16_t(*qbf)[kD] = reinterpret_cast<uint16_t(*)[kD]>(&sm.wave[0].buf[0][0]);
   {
-    const int h = wv * 4 + (lane >> 4), c = lane & 15;  // head in tile, 32-dim chunk
+    const int h = wv * 2 + (lane >> 5), c = lane & 31;  // head in tile, 16-dim chunk
     const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(b) * a.H + ht * 16 + h) * kD + c * 32;
-    float x[32];
+                        (static_cast<int64_t>(b) * a.H + ht * 16 + h) * kD + c * 16;
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const uint4 v = reinterpret_cast<const uint4*>(q)[i];
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -532,17 +530,17 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     }
     float ss = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) ss = fmaf(x[t], x[t], ss);
+    for (int t = 0; t < 16; ++t) ss = fmaf(x[t], x[t], ss);
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     const float r = static_cast<float>(1.0 / sqrt(static_cast<double>(ss) / kD + a.eps));
 #pragma unroll
-    for (int t = 0; t < 32; ++t) x[t] = x[t] * r * (a.q_norm_w ? a.q_norm_w[c * 32 + t] : 1.0f);
+    for (int t = 0; t < 16; ++t) x[t] = x[t] * r * (a.q_norm_w ? a.q_norm_w[c * 16 + t] : 1.0f);
     __syncthreads();                                    // rope_cs ready
-    if (c * 32 >= kD - kR) {
-      const int p0 = (c * 32 - (kD - kR)) / 2;
+    if (c * 16 >= kD - kR) {
+      const int p0 = (c * 16 - (kD - kR)) / 2;
 #pragma unroll
-      for (int t = 0; t < 32; t += 2) {
+      for (int t = 0; t < 16; t += 2) {
         const float cs = sm.rope_cs[p0 + t / 2][0], sn = sm.rope_cs[p0 + t / 2][1];
         const float x0 = x[t], x1 = x[t + 1];
         x[t] = x0 * cs - x1 * sn;
@@ -550,13 +548,13 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
       }
     }
 #pragma unroll
-    for (int t = 0; t < 32; t += 8) {
+    for (int t = 0; t < 16; t += 8) {
       uint4 v;
       v.x = bf16x2_rne(x[t], x[t + 1]);
       v.y = bf16x2_rne(x[t + 2], x[t + 3]);
       v.z = bf16x2_rne(x[t + 4], x[t + 5]);
       v.w = bf16x2_rne(x[t + 6], x[t + 7]);
-      *reinterpret_cast<uint4*>(&qbf[h][c * 32 + t]) = v;
+      *reinterpret_cast<uint4*>(&qbf[h][c * 16 + t]) = v;
     }
   }
   __syncthreads();
@@ -566,6 +564,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   for (int ks = 0; ks < kD / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(&qbf[j16][ks * 32 + g * 8]);
   const float ch = a.scale * kLog2e;
   __syncthreads();                                      // the staging copy is free again
+  if (wv == 0 && w.n_steps > 0) vmask0 = issue_step(w, 0, wv, e0, ok0, ws.buf[0]);
 
   // softmax state of head j16 (the same in the four lanes of that head); the
   // sink enters once, through wave 0
@@ -579,7 +578,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   else
     entry_loop<NB, NFR>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, e1, ok1, vmask0);
 
-  // -------- merge the four waves' states in wave order, then out = acc / (2^8 * l)
+  // -------- merge the waves' states in wave order, then out = acc / (2^8 * l)
   __syncthreads();                                      // every wave is done with its buffers
   if (lane < 16) {
     sm.ml[wv][0][j16] = m_run;
@@ -601,8 +600,8 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
   const float inv = 1.0f / (L * kPScale);
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * a.H + ht * 16 + j16) * kD;
-#pragma unroll
-  for (int i = wv * (NB / kWaves); i < (wv + 1) * (NB / kWaves); ++i) {
+  // block i of the output is finished by wave i % kWaves
+  for (int i = wv; i < NB; i += kWaves) {
     f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int v = 0; v < kWaves; ++v)
@@ -617,12 +616,15 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 
 }  // namespace
 
+// HIGH_OCC: two workgroups per (query, 16 heads), 256 output dims each;
+// LOW_OCC: eight, 64 dims each; AUTO fills the chip: the fewest workgroups
+// that still give every CU one.
 int pick_dvs(int variant, int units, int cus) {
-  if (variant == CSA_VARIANT_HIGH_OCC) return 1;
-  if (variant == CSA_VARIANT_LOW_OCC) return 4;
-  if (units >= 2 * cus) return 1;
-  if (units >= cus) return 2;
-  return 4;
+  if (variant == CSA_VARIANT_HIGH_OCC) return 2;
+  if (variant == CSA_VARIANT_LOW_OCC) return 8;
+  if (units * 2 >= cus) return 2;
+  if (units * 4 >= cus) return 4;
+  return 8;
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
@@ -650,21 +652,21 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (attr_set_dev != dev) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<1>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<2>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<2>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<4>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<8>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
     if (e != hipSuccess) return e;
     attr_set_dev = dev;
   }
   switch (dvs) {
-    case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
     case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
+    case 4: hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
+    default: hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
   }
   return hipGetLastError();
 }
