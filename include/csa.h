@@ -196,9 +196,9 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
  *   l_j  = scale * qhat . e_j                (the stored entry is key and value)
  *   out[b,h] = sum_j e^{l_j} e_j / (sum_j e^{l_j} + e^{sinks[h]})
  * The reduction order over E is fixed per token, the same in every variant
- * and batch.  F32 path: E in list order from the sink.  MFMA path: four
- * interleaved slices -- slice w takes list positions [128 s + 32 w, +32) of
- * the compressed part and window rows [64 t + 16 w, +16) -- each reduced in
+ * and batch.  F32 path: E in list order from the sink.  MFMA path: eight
+ * interleaved slices -- slice w takes list positions [128 s + 16 w, +16) of
+ * the compressed part and window rows [64 t + 8 w, +8) -- each reduced in
  * order (the sink enters slice 0), then merged in slice order.
  *
  *   q, out   [B, H] rows of D values (q_fmt / out_fmt: F32 or BF16)
