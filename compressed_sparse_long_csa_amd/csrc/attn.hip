@@ -145,7 +145,9 @@ constexpr int kStepW = 8;                               // window rows per wave 
 constexpr int kBufBytes = kStepE * kPitchSplit;         // one step's rows (>= kStepW * kPitchWin)
 constexpr int kPPitch = 20;                             // padded rows of the P arrays
 constexpr float kPScale = 256.0f;                       // probabilities are stored x 2^8
+constexpr int kQPitch = kD + 8;                         // staging rows of the normalised queries
 static_assert(kStepW * kPitchWin <= kBufBytes, "window step must fit a buffer");
+static_assert(16 * kQPitch * 2 <= 2 * kBufBytes, "query staging must fit wave 0's buffers");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -230,7 +232,7 @@ __device__ __forceinline__ float row_sum4(float v) {
 // address is a scalar byte offset.
 struct Work {
   int64_t p, N;
-  int n_list, win_count, ns, n_steps;
+  int n_list, win_count, ns, n_steps, k;
   const int32_t* idx;              // this query's selected list (CSA) or nullptr
   buf_rsrc kv_rs, win_rs;
 };
@@ -244,7 +246,8 @@ __device__ __forceinline__ int step_entry(const Work& w, int step, int wv, bool*
   int e = pos;
   bool v = pos < w.n_list;
   if (w.idx != nullptr) {
-    e = v ? w.idx[pos] : 0;
+    // the load does not wait for the visibility test: its address is clamped
+    e = w.idx[pos < w.k ? pos : w.k - 1];
     v = v && e >= 0 && e < w.N;
   }
   *ok = v;
@@ -478,6 +481,17 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const int g = lane >> 4, j16 = lane & 15;
   WaveSmem& ws = sm.wave[wv];
 
+  // this lane's part of the query (head 2 wv + lane / 32, dims [16 (lane % 32), +16)),
+  // loaded first: it depends on nothing else
+  const int qh = wv * 2 + (lane >> 5), qc = lane & 31;
+  uint4 qraw[2];
+  {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                    (static_cast<int64_t>(b) * a.H + ht * 16 + qh) * kD + qc * 16);
+    qraw[0] = q[0];
+    qraw[1] = q[1];
+  }
+
   Work w;
   w.p = a.q_pos[b];
   w.N = (w.p + 1) / a.m;
@@ -485,6 +499,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   int64_t win_row0;
   window_of(a, b, w.p, &win_row0, &w.win_count);
   w.idx = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
+  w.k = a.k;
   w.n_list = a.idx != nullptr ? (w.N > 0 ? a.k : 0) : static_cast<int>(w.N);
   w.ns = (w.n_list + kWaves * kStepE - 1) / (kWaves * kStepE);
   w.n_steps = w.ns + (w.win_count + kWaves * kStepW - 1) / (kWaves * kStepW);
@@ -512,15 +527,14 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   // ---------------- prologue: qhat = RoPE(RMSNorm(q)); wave w prepares heads
   // 2w, 2w+1 (lane: head 2w + lane/32, dims [16 (lane%32), +16)) into a bf16
   // staging copy in wave 0's buffers, then every lane takes its QK operand.
-  uint16_t(*qbf)[kD] = reinterpret_cast<uint16_t(*)[kD]>(&sm.wave[0].buf[0][0]);
+  // (rows padded to 520 values so the 16 heads' rows start on different banks)
+  uint16_t(*qbf)[kQPitch] = reinterpret_cast<uint16_t(*)[kQPitch]>(&sm.wave[0].buf[0][0]);
   {
-    const int h = wv * 2 + (lane >> 5), c = lane & 31;  // head in tile, 16-dim chunk
-    const uint16_t* q = static_cast<const uint16_t*>(a.q) +
-                        (static_cast<int64_t>(b) * a.H + ht * 16 + h) * kD + c * 16;
+    const int h = qh, c = qc;                           // head in tile, 16-dim chunk
     float x[16];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(q)[i];
+      const uint4 v = qraw[i];
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
