@@ -208,3 +208,64 @@ def random_selection(rng, n_ent, k):
         if c:
             out[b, :c] = np.sort(rng.choice(int(N), size=c, replace=False)).astype(np.int32)
     return out
+
+
+# --------------------------------------------------------------- device-side generation
+# Full-size inputs (hundreds of MB) are drawn on the GPU with a seeded torch
+# generator; tests copy back only the rows the oracle needs.  Same value
+# distributions as the host generators above.
+def device_generator(seed, device="cuda"):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def device_rows(gen, n, D, fmt, R=0, device="cuda", chunk=1 << 16):
+    """n rows of N(0,1) values stored in `fmt` on `device`; uint8 [n, row_bytes]."""
+    rb = row_bytes(fmt, D, R)
+    out = torch.empty((n, rb), dtype=torch.uint8, device=device)
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        if fmt == MXFP4:
+            codes = torch.randint(0, 16, (b - a, D), generator=gen, device=device, dtype=torch.uint8)
+            out[a:b, : D // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+            out[a:b, D // 2:] = torch.randint(124, 128, (b - a, D // 32), generator=gen, device=device,
+                                              dtype=torch.uint8)
+            continue
+        x = torch.randn((b - a, D), generator=gen, device=device, dtype=torch.float32)
+        if fmt == F32:
+            out[a:b] = x.view(torch.uint8).reshape(b - a, rb)
+        elif fmt == BF16:
+            out[a:b] = x.to(torch.bfloat16).view(torch.uint8).reshape(b - a, rb)
+        elif fmt == FP8:
+            out[a:b] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        elif fmt == SPLIT:
+            out[a:b, : D - R] = x[:, : D - R].to(torch.float8_e4m3fn).view(torch.uint8)
+            out[a:b, D - R:] = x[:, D - R:].contiguous().to(torch.bfloat16).view(torch.uint8).reshape(b - a, 2 * R)
+        else:
+            raise ValueError(fmt)
+    return out
+
+
+def device_decode_inputs(seed, lengths, *, m, H, D, R, n_win=128, csa=True, k=512, idx_fmt=FP8,
+                         H_I=64, d_I=128, device="cuda"):
+    """A decode batch like decode_inputs, drawn on the device (same draw
+    order; returns device tensors plus host metadata in a dict)."""
+    gen = device_generator(seed, device)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = lengths.shape[0]
+    n_ent = lengths // m
+    kv_off = np.zeros(B, dtype=np.int64)
+    kv_off[1:] = np.cumsum(n_ent)[:-1]
+    d = dict(B=B, H=H, D=D, R=R, m=m, n_win=n_win, k=k, idx_fmt=idx_fmt, H_I=H_I, d_I=d_I,
+             lengths=lengths, n_ent=n_ent, kv_off=kv_off, q_pos=lengths - 1,
+             win_len=np.minimum(n_win, lengths).astype(np.int32), scale=float(1.0 / np.sqrt(D)))
+    d["kv"] = device_rows(gen, int(n_ent.sum()), D, SPLIT, R, device)
+    d["win"] = device_rows(gen, B * n_win, D, BF16, R, device).reshape(B, n_win, -1)
+    d["q"] = device_rows(gen, B * H, D, BF16, R, device).reshape(B, H, -1)
+    if csa:
+        d["keys"] = device_rows(gen, int(n_ent.sum()), d_I, idx_fmt, 0, device)
+        d["q_idx"] = device_rows(gen, B * H_I, d_I, idx_fmt, 0, device).reshape(B, H_I, -1)
+        d["w"] = torch.rand((B, H_I), generator=gen, device=device, dtype=torch.float32)
+    d["sinks"] = torch.randn(H, generator=gen, device=device, dtype=torch.float32)
+    return d
