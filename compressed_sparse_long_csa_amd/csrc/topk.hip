@@ -23,8 +23,9 @@
 //     ranking for few candidates, else by key-space histograms over the LDS
 //     list (bins of power-of-two width) -- a b* too large to keep refines
 //     over the row itself;
-//  5. every wave writes its selected indices in order: a running count plus
-//     the ballot prefix count of each 64-score step.
+//  5. every wave places its selected indices in order (a running count plus
+//     the ballot prefix count of each 64-score step) into an LDS copy of the
+//     output row, which is then stored with coalesced writes.
 // Wave reductions and scans use DPP row operations and lane reads, so a block
 // reduction costs one barrier.  The result is the exact set, ascending,
 // whatever the batch or launch.  Loads and stores go through buffer
@@ -41,6 +42,7 @@ constexpr int kBins = 2048;
 constexpr int kStreamJ = 8;                // independent loads per streamed step
 constexpr int kLdsJ = 4;                   // LDS reads per staged step
 constexpr int kMaxCand = 2048;             // candidates kept in LDS
+static_assert(2 * kMaxCand >= 4096, "the candidate arrays double as the output staging row");
 constexpr int kRankDirect = 96;            // candidates ranked by direct counting
 constexpr uint32_t kStageMax = 33 * 1024;  // rows staged in LDS (wave ranges included)
 constexpr uint32_t kStageSlack = 64 * (kLdsJ - 1);
@@ -388,6 +390,9 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n,
     total_eq += gb;
   }
   uint32_t sel_before = gt_before + umin(eq_before, need_eq);
+  // selected indices are placed in an LDS copy of the output row (the
+  // candidate arrays, free by now), then written out with coalesced stores
+  uint32_t* stage = sm.cand_key;                        // kMaxCand * 2 >= k words
   r.visit([&](uint32_t j, float v) __attribute__((always_inline)) {
     const bool gt = take_all ? v == v : v > Tv;
     uint64_t ms = __ballot(gt);
@@ -403,8 +408,8 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n,
     }
     if (ms != 0ull) {
       const uint32_t pos = sel_before + lanes_below(ms);
-      if (sel) {
-        __builtin_amdgcn_raw_buffer_store_b32(r.elem(j), out_rs, static_cast<int>(4u * pos), 0, 0);
+      if (sel && pos < k) {
+        stage[pos] = r.elem(j);
         if (want_s)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), outs_rs,
                                                 static_cast<int>(4u * pos), 0, 0);
@@ -413,9 +418,12 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n,
     }
   });
   const uint32_t total = umin(total_gt + umin(total_eq, need_eq), k);
-  for (uint32_t j = total + tid; j < k; j += kThreads) {
-    __builtin_amdgcn_raw_buffer_store_b32(0xffffffffu, out_rs, static_cast<int>(4u * j), 0, 0);
-    if (want_s)
+  __syncthreads();
+  for (uint32_t j = tid; j < k; j += kThreads)
+    __builtin_amdgcn_raw_buffer_store_b32(j < total ? stage[j] : 0xffffffffu, out_rs,
+                                          static_cast<int>(4u * j), 0, 0);
+  if (want_s) {
+    for (uint32_t j = total + tid; j < k; j += kThreads)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), outs_rs,
                                             static_cast<int>(4u * j), 0, 0);
   }
