@@ -2,20 +2,20 @@
 
 One step = one decode token for each of the B sequences through the whole
 path, every kernel from libcsa:
-  1. csa_compress  -- fold the newest block of m tokens of every sequence into
-                      its cache entry (split FP8/BF16 row, RMSNorm, RoPE)
-  2. csa_compress  -- the matching indexer key (FP8)
-  3. csa_compress  -- the new token's sliding-window row (m = 1, BF16)
-  4. indexer_score -- ReLU multi-head scores over every visible entry
-  5. topk_select   -- the k best entries, ascending
-  6. hybrid_attn_decode -- sink MQA over the selected entries + window
+  1. csa_compress_batch -- one launch of three compress jobs: fold the newest
+                      block of m tokens of every sequence into its cache entry
+                      (split FP8/BF16 row, RMSNorm, RoPE), the matching indexer
+                      key (FP8), and the new token's sliding-window row (m = 1)
+  2. indexer_score -- ReLU multi-head scores over every visible entry
+  3. topk_select   -- the k best entries, ascending
+  4. hybrid_attn_decode -- sink MQA over the selected entries + window
 Inputs are seeded synthetic tensors already resident in HBM.  The per-layer
 state a step reads (KV cache, index keys, window rows) exists in R copies
 (default 13, about 2.4 GB) stepped in turn, so that it cannot stay in the
 256 MB last-level cache between steps, as in a model whose every layer has its
-own cache; `value_one_warm_cache` repeats one copy.  Each copy's step is
-captured in a HIP graph; W warm-up steps, then exactly K timed steps between
-two synchronised events.  The workload is the CSA decode batch of 16
+own cache; `value_one_warm_cache` repeats one copy.  The R copies' steps are
+captured in order in one HIP graph (a pass through R layers); W warm-up
+steps, then exactly K timed steps between two synchronised events.  The workload is the CSA decode batch of 16
 sequences of 65,536 tokens (16,384 compressed entries each, top-k 512, FP8
 indexer 64 x 128, 64 query heads, head dim 512).
 
@@ -106,20 +106,20 @@ def make_step(W, check=False):
     c, inp = W["c"], W["inp"]
     B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
 
-    def k_compress_kv():
-        csa.csa_compress(W["kv_tok"], csa.BF16, W["kv_gate"], 1, B * m, D, m, B, W["seg_off"],
-                         W["seg_pos0"], W["seg_row"], 1, None, EPS, R, BASE, W["kv"], csa.SPLIT,
-                         check=check)
+    def job(x, gate, n_tok, D, mm, off, pos0, rows, normalize, R_, out, fmt):
+        return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=n_tok, D=D, m=mm, nseg=B,
+                    seg_tok_off=off, seg_pos0=pos0, seg_out_row=rows, normalize=normalize,
+                    norm_w=None, eps=EPS, rope_dim=R_, rope_base=BASE, out=out, out_fmt=fmt)
+    # the newest block's KV entry, its indexer key, and the newest token's window row
+    jobs = [job(W["kv_tok"], W["kv_gate"], B * m, D, m, W["seg_off"], W["seg_pos0"], W["seg_row"],
+                1, R, W["kv"], csa.SPLIT),
+            job(W["key_tok"], W["key_gate"], B * m, d_I, m, W["seg_off"], W["seg_pos0"],
+                W["seg_row"], 0, 0, W["keys"], csa.FP8),
+            job(W["win_tok"], W["win_gate"], B, D, 1, W["win_seg_off"], W["win_pos0"], W["win_row"],
+                1, R, W["win"], csa.BF16)]
 
-    def k_compress_key():
-        csa.csa_compress(W["key_tok"], csa.BF16, W["key_gate"], 1, B * m, d_I, m, B,
-                         W["seg_off"], W["seg_pos0"], W["seg_row"], 0, None, EPS, 0, BASE,
-                         W["keys"], csa.FP8, check=check)
-
-    def k_compress_win():
-        csa.csa_compress(W["win_tok"], csa.BF16, W["win_gate"], 1, B, D, 1, B, W["win_seg_off"],
-                         W["win_pos0"], W["win_row"], 1, None, EPS, R, BASE, W["win"], csa.BF16,
-                         check=check)
+    def k_compress():
+        csa.csa_compress_batch(jobs, check=check)
 
     def k_indexer():
         csa.indexer_score(W["q_idx"], W["w"], B, c["H_I"], d_I, W["keys"], csa.FP8, W["kv_off"],
@@ -134,8 +134,7 @@ def make_step(W, check=False):
                                inp.n_win, W["win_len"], W["sinks"], inp.scale, W["out"], csa.BF16,
                                csa.VARIANT_AUTO, check=check)
 
-    kernels = [("csa_compress_kv", k_compress_kv), ("csa_compress_key", k_compress_key),
-               ("csa_compress_win", k_compress_win), ("indexer_score", k_indexer),
+    kernels = [("csa_compress_batch", k_compress), ("indexer_score", k_indexer),
                ("topk_select", k_topk), ("hybrid_attn_decode", k_attn)]
 
     def step():
@@ -153,9 +152,9 @@ def algorithmic_bytes(W):
     split = (D - R) + 2 * R
     sel = np.minimum(k, N)
     per_kernel = {
-        "csa_compress_kv": B * m * (2 * D + 4) + B * split,
-        "csa_compress_key": B * m * (2 * d_I + 4) + B * d_I,
-        "csa_compress_win": B * (2 * D + 4) + B * 2 * D,
+        "csa_compress_batch": (B * m * (2 * D + 4) + B * split            # KV entries
+                               + B * m * (2 * d_I + 4) + B * d_I         # indexer keys
+                               + B * (2 * D + 4) + B * 2 * D),           # window rows
         "indexer_score": int((N * (d_I + 4)).sum()) + B * c["H_I"] * (d_I + 4),
         "topk_select": int((N * 4).sum()) + B * k * 4,
         "hybrid_attn_decode": int((sel * split).sum()) + int(inp.win_len.sum()) * 2 * D
@@ -176,9 +175,11 @@ def algorithmic_flops(W):
 
 
 def time_graph(steps_r, steps, warmup):
-    """One captured graph per replica's step; W warm-up steps, then exactly
-    `steps` timed steps, replica r = i mod R, between two synchronised events.
-    Returns ms per step."""
+    """Replica r's step is captured once on its own and once more, in replica
+    order, inside one graph of all R steps (a decode pass through R layers,
+    as a model would capture it).  W warm-up steps, then exactly `steps` timed
+    steps between two synchronised events: whole R-step graphs, then the
+    single-step graphs of the remainder.  Returns ms per step."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -186,20 +187,30 @@ def time_graph(steps_r, steps, warmup):
             st()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    graphs = []
+    singles = []
     for st in steps_r:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             st()
-        graphs.append(g)
-    R = len(graphs)
-    for i in range(warmup):
-        graphs[i % R].replay()
+        singles.append(g)
+    R = len(singles)
+    chain = singles[0]
+    if R > 1:
+        chain = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(chain):
+            for st in steps_r:
+                st()
+
+    def run(n):
+        for _ in range(n // R):
+            chain.replay()
+        for j in range(n % R):
+            singles[j].replay()
+    run(warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        graphs[i % R].replay()
+    run(steps)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -385,7 +396,7 @@ def main():
         "config": {"workload": "csa_decode_b16_ctx65536", "batch": B, "context": 65536,
                    "entries_per_seq": int(W["inp"].n_ent[0]), "top_k": W["c"]["k"],
                    "heads": W["c"]["H"], "head_dim": W["D"], "indexer": "fp8 64x128",
-                   "window": 128, "graph": True, "variant": "auto",
+                   "window": 128, "graph": True, "steps_per_graph": len(reps), "variant": "auto",
                    "state_replicas": len(reps)},
         "value_one_warm_cache": B / (ms_warm * 1e-3),
         "hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
-           "csa_compress", "indexer_score", "topk_select", "hybrid_attn_decode",
+           "csa_compress", "csa_compress_batch", "indexer_score", "topk_select", "hybrid_attn_decode",
            "hybrid_attn_prefill")
 
 _lib = None
@@ -51,6 +51,8 @@ def load_library():
     lib.csa_row_bytes.argtypes = [I, I, I]
     lib.csa_compress.restype = I
     lib.csa_compress.argtypes = [P, I, P, I, I64, I, I, I, P, P, P, I, P, F, I, F, P, I, P]
+    lib.csa_compress_batch.restype = I
+    lib.csa_compress_batch.argtypes = [ctypes.POINTER(CompressJob), I, P]
     lib.indexer_score.restype = I
     lib.indexer_score.argtypes = [P, P, I, I, I, P, I, P, P, I, P, I64, P]
     lib.topk_select.restype = I
@@ -106,10 +108,8 @@ def _host(t):
 
 
 # ------------------------------------------------------------------ entry points
-def csa_compress(x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0,
-                 seg_out_row, normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt,
-                 stream=None, check=True):
-    lib = load_library()
+def _compress_checks(x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0,
+                     seg_out_row, norm_w, rope_dim, out, out_fmt, check):
     _need(x, "x", min_bytes=n_tok * row_bytes(x_fmt, D))
     _need(gate, "gate", torch.float32, min_numel=n_tok * gate_cols)
     for t, nm, n in ((seg_tok_off, "seg_tok_off", nseg + 1), (seg_pos0, "seg_pos0", nseg),
@@ -126,10 +126,54 @@ def csa_compress(x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_
         need_rows = int((rows + nent).max()) if nseg else 0
         if int(rows.min()) < 0 or out.numel() * out.element_size() < need_rows * row_bytes(out_fmt, D, rope_dim):
             raise ValueError("out is too small for the rows the segments write")
+
+
+def csa_compress(x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0,
+                 seg_out_row, normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt,
+                 stream=None, check=True):
+    lib = load_library()
+    _compress_checks(x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0,
+                     seg_out_row, norm_w, rope_dim, out, out_fmt, check)
     _check(lib.csa_compress(_ptr(x), x_fmt, _ptr(gate), gate_cols, n_tok, D, m, nseg,
                             _ptr(seg_tok_off), _ptr(seg_pos0), _ptr(seg_out_row), int(normalize),
                             _ptr(norm_w), eps, rope_dim, rope_base, _ptr(out), out_fmt,
                             _stream(stream)))
+
+
+class CompressJob(ctypes.Structure):
+    """struct csa_compress_job (include/csa.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_fmt", ctypes.c_int), ("gate", ctypes.c_void_p),
+                ("gate_cols", ctypes.c_int), ("n_tok", ctypes.c_int64), ("D", ctypes.c_int),
+                ("m", ctypes.c_int), ("nseg", ctypes.c_int), ("seg_tok_off", ctypes.c_void_p),
+                ("seg_pos0", ctypes.c_void_p), ("seg_out_row", ctypes.c_void_p),
+                ("normalize", ctypes.c_int), ("norm_w", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("rope_dim", ctypes.c_int), ("rope_base", ctypes.c_float), ("out", ctypes.c_void_p),
+                ("out_fmt", ctypes.c_int)]
+
+
+COMPRESS_JOB_FIELDS = ("x", "x_fmt", "gate", "gate_cols", "n_tok", "D", "m", "nseg", "seg_tok_off",
+                       "seg_pos0", "seg_out_row", "normalize", "norm_w", "eps", "rope_dim",
+                       "rope_base", "out", "out_fmt")
+MAX_COMPRESS_JOBS = 4
+
+
+def csa_compress_batch(jobs, stream=None, check=True):
+    """jobs: sequence of dicts with csa_compress's arguments (COMPRESS_JOB_FIELDS)."""
+    lib = load_library()
+    arr = (CompressJob * max(1, len(jobs)))()
+    for i, j in enumerate(jobs):
+        _compress_checks(j["x"], j["x_fmt"], j["gate"], j["gate_cols"], j["n_tok"], j["D"], j["m"],
+                         j["nseg"], j["seg_tok_off"], j["seg_pos0"], j["seg_out_row"], j["norm_w"],
+                         j["rope_dim"], j["out"], j["out_fmt"], check)
+        c = arr[i]
+        for f in COMPRESS_JOB_FIELDS:
+            v = j[f]
+            if isinstance(v, torch.Tensor):
+                v = v.data_ptr()
+            elif v is None:
+                v = None
+            setattr(c, f, int(v) if f == "normalize" else v)
+    _check(lib.csa_compress_batch(arr, len(jobs), _stream(stream)))
 
 
 def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld,

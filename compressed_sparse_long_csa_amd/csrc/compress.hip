@@ -9,7 +9,8 @@
 //
 // One workgroup per output entry.  The block sum runs over the m tokens in
 // order, the mean square over D in a fixed tree, so an entry's bits depend
-// only on its own tokens.
+// only on its own tokens -- also when several calls share one launch
+// (csa_compress_batch: the jobs' blocks are numbered one after another).
 //
 // Latency: a decode step writes a handful of entries, so the kernel is a
 // chain of memory round trips, and it keeps that chain short.  The block's
@@ -162,73 +163,114 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float* y, fl
   __syncthreads();
 }
 
-// Blocks of M tokens, D <= 256 * NCH: the block's values are loaded into
+// One block of M tokens, D <= 256 * NCH: the block's values are loaded into
 // registers before the segment lookup, so both share one round trip.
 template <int M, int NCH>
-__global__ void __launch_bounds__(kThreads) compress_small(CompressArgs a, int64_t n_blocks) {
-  extern __shared__ float y[];            // [D] entry values, then [kThreads/64] partials
-  __shared__ EntrySlot slot;
-  float* red = y + a.D;
+__device__ __forceinline__ void block_small(const CompressArgs& a, int64_t blk, float* y, float* red,
+                                            EntrySlot* slot) {
   const int tid = threadIdx.x, D = a.D;
   const bool per_channel = a.gate_cols != 1;
-  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-    const int64_t t0 = blk * M;
-    float xv[NCH][M], gv[NCH][M];
+  const int64_t t0 = blk * M;
+  float xv[NCH][M], gv[NCH][M];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int cc = c < D ? c : 0;
-      const int gc = per_channel ? cc : 0;
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * kThreads;
+    const int cc = c < D ? c : 0;
+    const int gc = per_channel ? cc : 0;
 #pragma unroll
-      for (int t = 0; t < M; ++t) {
-        xv[i][t] = load_x(a.x, a.x_fmt, (t0 + t) * D + cc);
-        gv[i][t] = a.gate[(t0 + t) * a.gate_cols + gc];
-      }
+    for (int t = 0; t < M; ++t) {
+      xv[i][t] = load_x(a.x, a.x_fmt, (t0 + t) * D + cc);
+      gv[i][t] = a.gate[(t0 + t) * a.gate_cols + gc];
     }
-    locate(a, t0, &slot);
-    if (!slot.ok) continue;
-    float sq = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < D) {
-        const float v = gated_sum(M, xv[i], gv[i]);
-        y[c] = v;
-        sq = fmaf(v, v, sq);
-      }
-    }
-    finish_entry(a, y, red, sq, slot);
   }
-}
-
-// Any m and D: values are read inside the block loop.
-__global__ void __launch_bounds__(kThreads) compress_any(CompressArgs a, int64_t n_blocks) {
-  extern __shared__ float y[];
-  __shared__ EntrySlot slot;
-  float* red = y + a.D;
-  const int tid = threadIdx.x, D = a.D, m = a.m;
-  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
-    const int64_t t0 = blk * m;
-    locate(a, t0, &slot);
-    if (!slot.ok) continue;
-    float sq = 0.0f;
-    for (int c = tid; c < D; c += kThreads) {
-      const int gc = a.gate_cols == 1 ? 0 : c;
-      float gmax = -INFINITY;
-      for (int t = 0; t < m; ++t) gmax = fmaxf(gmax, a.gate[(t0 + t) * a.gate_cols + gc]);
-      float den = 0.0f, acc = 0.0f;
-      for (int t = 0; t < m; ++t) {
-        const float e = expf(a.gate[(t0 + t) * a.gate_cols + gc] - gmax);
-        den += e;
-        acc = fmaf(e, load_x(a.x, a.x_fmt, (t0 + t) * D + c), acc);
-      }
-      const float v = acc / den;
+  locate(a, t0, slot);
+  if (!slot->ok) return;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + i * kThreads;
+    if (c < D) {
+      const float v = gated_sum(M, xv[i], gv[i]);
       y[c] = v;
       sq = fmaf(v, v, sq);
     }
-    finish_entry(a, y, red, sq, slot);
+  }
+  finish_entry(a, y, red, sq, *slot);
+}
+
+// One block, any m and D: values are read inside the block loop.
+__device__ __forceinline__ void block_any(const CompressArgs& a, int64_t blk, float* y, float* red,
+                                          EntrySlot* slot) {
+  const int tid = threadIdx.x, D = a.D, m = a.m;
+  const int64_t t0 = blk * m;
+  locate(a, t0, slot);
+  if (!slot->ok) return;
+  float sq = 0.0f;
+  for (int c = tid; c < D; c += kThreads) {
+    const int gc = a.gate_cols == 1 ? 0 : c;
+    float gmax = -INFINITY;
+    for (int t = 0; t < m; ++t) gmax = fmaxf(gmax, a.gate[(t0 + t) * a.gate_cols + gc]);
+    float den = 0.0f, acc = 0.0f;
+    for (int t = 0; t < m; ++t) {
+      const float e = expf(a.gate[(t0 + t) * a.gate_cols + gc] - gmax);
+      den += e;
+      acc = fmaf(e, load_x(a.x, a.x_fmt, (t0 + t) * D + c), acc);
+    }
+    const float v = acc / den;
+    y[c] = v;
+    sq = fmaf(v, v, sq);
+  }
+  finish_entry(a, y, red, sq, *slot);
+}
+
+// Block shapes with a register-resident body; kAny covers the rest.
+enum BlockKind { kM4C1, kM4C2, kM1C1, kM1C2, kM1C4, kAny };
+
+__device__ __forceinline__ void run_block(const CompressArgs& a, int kind, int64_t blk, float* y,
+                                          float* red, EntrySlot* slot) {
+  switch (kind) {
+    case kM4C1: block_small<4, 1>(a, blk, y, red, slot); break;
+    case kM4C2: block_small<4, 2>(a, blk, y, red, slot); break;
+    case kM1C1: block_small<1, 1>(a, blk, y, red, slot); break;
+    case kM1C2: block_small<1, 2>(a, blk, y, red, slot); break;
+    case kM1C4: block_small<1, 4>(a, blk, y, red, slot); break;
+    default: block_any(a, blk, y, red, slot); break;
   }
 }
+
+template <int Kind>
+__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int64_t n_blocks) {
+  extern __shared__ float y[];            // [D] entry values, then [kThreads/64] partials
+  __shared__ EntrySlot slot;
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x)
+    run_block(a, Kind, blk, y, y + a.D, &slot);
+}
+
+// Several independent compress calls in one launch: global block b belongs
+// to the job j with blk0[j] <= b < blk0[j + 1] (uniform over the workgroup).
+__global__ void __launch_bounds__(kThreads) compress_jobs_kernel(CompressJobs J) {
+  extern __shared__ float y[];
+  __shared__ EntrySlot slot;
+  const int64_t total = J.blk0[J.n];
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    int j = 0;
+    while (j + 1 < J.n && b >= J.blk0[j + 1]) ++j;
+    const CompressArgs& a = J.a[j];
+    run_block(a, J.kind[j], b - J.blk0[j], y, y + a.D, &slot);
+  }
+}
+
+int block_kind(const CompressArgs& a) {
+  const int nch = (a.D + kThreads - 1) / kThreads;
+  if (a.m == 4 && nch == 1) return kM4C1;
+  if (a.m == 4 && nch == 2) return kM4C2;
+  if (a.m == 1 && nch == 1) return kM1C1;
+  if (a.m == 1 && nch == 2) return kM1C2;
+  if (a.m == 1 && nch <= 4) return kM1C4;
+  return kAny;
+}
+
+size_t shm_bytes(int D) { return (static_cast<size_t>(D) + kThreads / kWave) * sizeof(float); }
 
 }  // namespace
 
@@ -236,19 +278,38 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   const int64_t n_blocks = a.n_tok / a.m;
   if (n_blocks == 0) return hipSuccess;
   const int64_t grid = n_blocks < 65536 ? n_blocks : 65536;
-  const size_t shm = (static_cast<size_t>(a.D) + kThreads / kWave) * sizeof(float);
+  const size_t shm = shm_bytes(a.D);
   const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
-  const int nch = (a.D + kThreads - 1) / kThreads;
-  if (a.m == 4 && nch <= 2) {
-    if (nch == 1) hipLaunchKernelGGL((compress_small<4, 1>), g, b, shm, stream, a, n_blocks);
-    else hipLaunchKernelGGL((compress_small<4, 2>), g, b, shm, stream, a, n_blocks);
-  } else if (a.m == 1 && nch <= 4) {
-    if (nch == 1) hipLaunchKernelGGL((compress_small<1, 1>), g, b, shm, stream, a, n_blocks);
-    else if (nch == 2) hipLaunchKernelGGL((compress_small<1, 2>), g, b, shm, stream, a, n_blocks);
-    else hipLaunchKernelGGL((compress_small<1, 4>), g, b, shm, stream, a, n_blocks);
-  } else {
-    hipLaunchKernelGGL(compress_any, g, b, shm, stream, a, n_blocks);
+  switch (block_kind(a)) {
+    case kM4C1: hipLaunchKernelGGL(compress_kernel<kM4C1>, g, b, shm, stream, a, n_blocks); break;
+    case kM4C2: hipLaunchKernelGGL(compress_kernel<kM4C2>, g, b, shm, stream, a, n_blocks); break;
+    case kM1C1: hipLaunchKernelGGL(compress_kernel<kM1C1>, g, b, shm, stream, a, n_blocks); break;
+    case kM1C2: hipLaunchKernelGGL(compress_kernel<kM1C2>, g, b, shm, stream, a, n_blocks); break;
+    case kM1C4: hipLaunchKernelGGL(compress_kernel<kM1C4>, g, b, shm, stream, a, n_blocks); break;
+    default: hipLaunchKernelGGL(compress_kernel<kAny>, g, b, shm, stream, a, n_blocks); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t stream) {
+  CompressJobs J{};
+  J.n = 0;
+  J.blk0[0] = 0;
+  int maxD = 1;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nb = jobs[i].n_tok / jobs[i].m;
+    if (nb == 0) continue;
+    J.a[J.n] = jobs[i];
+    J.kind[J.n] = block_kind(jobs[i]);
+    J.blk0[J.n + 1] = J.blk0[J.n] + nb;
+    maxD = jobs[i].D > maxD ? jobs[i].D : maxD;
+    ++J.n;
+  }
+  if (J.n == 0) return hipSuccess;
+  const int64_t total = J.blk0[J.n];
+  const int64_t grid = total < 65536 ? total : 65536;
+  hipLaunchKernelGGL(compress_jobs_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     shm_bytes(maxD), stream, J);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // C ABI of libcsa: argument validation, format / path dispatch, error state.
 // The contract of every entry point is documented in include/csa.h.
+#include <stddef.h>
 #include <stdio.h>
 #include <stdarg.h>
 
@@ -25,6 +26,11 @@ csa_status launched(hipError_t e, const char* what) {
 }
 
 bool fmt_ok(csa_fmt f) { return f >= CSA_F32 && f <= CSA_SPLIT; }
+
+// the layout the Python binding mirrors (LP64)
+static_assert(sizeof(csa_compress_job) == 128 && offsetof(csa_compress_job, out_fmt) == 120,
+              "csa_compress_job layout");
+static_assert(CSA_COMPRESS_MAX_JOBS == kMaxCompressJobs, "job limit");
 }  // namespace
 
 int device_cu_count() {
@@ -66,38 +72,86 @@ size_t csa_row_bytes(csa_fmt fmt, int D, int rope_dim) {
   return row_bytes(fmt, D, rope_dim);
 }
 
+}  // extern "C"
+
+namespace {
+// Argument checks and kernel arguments of one compress call ("what" names the
+// entry point in the error text); `empty` is set when there is nothing to do.
+csa_status compress_args(const char* what, const void* x, csa_fmt x_fmt, const float* gate,
+                         int gate_cols, int64_t n_tok, int D, int m, int nseg,
+                         const int64_t* seg_tok_off, const int64_t* seg_pos0,
+                         const int64_t* seg_out_row, int normalize, const float* norm_w, float eps,
+                         int rope_dim, float rope_base, void* out, csa_fmt out_fmt,
+                         CompressArgs* a, bool* empty) {
+  *empty = false;
+  if (n_tok < 0) return fail(CSA_ERR_INVALID_ARG, "%s: n_tok < 0", what);
+  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "%s: m must be >= 1", what);
+  if (D < 2) return fail(CSA_ERR_INVALID_ARG, "%s: D must be >= 2", what);
+  if (D > 4096) return fail(CSA_ERR_UNSUPPORTED, "%s: D > 4096", what);
+  if (n_tok % m != 0) return fail(CSA_ERR_INVALID_ARG, "%s: n_tok %% m != 0", what);
+  if (x_fmt != CSA_F32 && x_fmt != CSA_BF16)
+    return fail(CSA_ERR_INVALID_ARG, "%s: x_fmt must be CSA_F32 or CSA_BF16", what);
+  if (!fmt_ok(out_fmt)) return fail(CSA_ERR_INVALID_ARG, "%s: bad out_fmt", what);
+  if (gate_cols != 1 && gate_cols != D)
+    return fail(CSA_ERR_INVALID_ARG, "%s: gate_cols must be 1 or D", what);
+  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D || rope_dim > 2 * kMaxRopePairs)
+    return fail(CSA_ERR_INVALID_ARG, "%s: rope_dim must be even, <= D and <= 128", what);
+  if (rope_dim > 0 && !(rope_base > 0.0f))
+    return fail(CSA_ERR_INVALID_ARG, "%s: rope_base must be > 0", what);
+  if (out_fmt == CSA_MXFP4 && D % 32 != 0)
+    return fail(CSA_ERR_INVALID_ARG, "%s: MXFP4 needs D %% 32 == 0", what);
+  if (out_fmt == CSA_SPLIT && (rope_dim == 0 || D - rope_dim < 1))
+    return fail(CSA_ERR_INVALID_ARG, "%s: SPLIT needs 0 < rope_dim < D", what);
+  if (nseg < 1) return fail(CSA_ERR_INVALID_ARG, "%s: nseg must be >= 1", what);
+  if (!(eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "%s: eps must be >= 0", what);
+  if (n_tok == 0) { *empty = true; return CSA_OK; }
+  if (!x || !gate || !seg_tok_off || !seg_pos0 || !seg_out_row || !out)
+    return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", what);
+  *a = CompressArgs{x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0, seg_out_row,
+                    normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt, {}};
+  fill_rope_theta(a->rope_theta, rope_dim, rope_base);
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
 csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gate_cols,
                         int64_t n_tok, int D, int m, int nseg, const int64_t* seg_tok_off,
                         const int64_t* seg_pos0, const int64_t* seg_out_row, int normalize,
                         const float* norm_w, float eps, int rope_dim, float rope_base, void* out,
                         csa_fmt out_fmt, hipStream_t stream) {
-  if (n_tok < 0) return fail(CSA_ERR_INVALID_ARG, "csa_compress: n_tok < 0");
-  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "csa_compress: m must be >= 1");
-  if (D < 2) return fail(CSA_ERR_INVALID_ARG, "csa_compress: D must be >= 2");
-  if (D > 4096) return fail(CSA_ERR_UNSUPPORTED, "csa_compress: D > 4096");
-  if (n_tok % m != 0) return fail(CSA_ERR_INVALID_ARG, "csa_compress: n_tok %% m != 0");
-  if (x_fmt != CSA_F32 && x_fmt != CSA_BF16)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: x_fmt must be CSA_F32 or CSA_BF16");
-  if (!fmt_ok(out_fmt)) return fail(CSA_ERR_INVALID_ARG, "csa_compress: bad out_fmt");
-  if (gate_cols != 1 && gate_cols != D)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: gate_cols must be 1 or D");
-  if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D || rope_dim > 2 * kMaxRopePairs)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_dim must be even, <= D and <= 128");
-  if (rope_dim > 0 && !(rope_base > 0.0f))
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: rope_base must be > 0");
-  if (out_fmt == CSA_MXFP4 && D % 32 != 0)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: MXFP4 needs D %% 32 == 0");
-  if (out_fmt == CSA_SPLIT && (rope_dim == 0 || D - rope_dim < 1))
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: SPLIT needs 0 < rope_dim < D");
-  if (nseg < 1) return fail(CSA_ERR_INVALID_ARG, "csa_compress: nseg must be >= 1");
-  if (!(eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "csa_compress: eps must be >= 0");
-  if (n_tok == 0) { g_err[0] = '\0'; return CSA_OK; }
-  if (!x || !gate || !seg_tok_off || !seg_pos0 || !seg_out_row || !out)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress: null pointer");
-  CompressArgs a{x, x_fmt, gate, gate_cols, n_tok, D, m, nseg, seg_tok_off, seg_pos0, seg_out_row,
-                 normalize, norm_w, eps, rope_dim, rope_base, out, out_fmt, {}};
-  fill_rope_theta(a.rope_theta, rope_dim, rope_base);
+  CompressArgs a{};
+  bool empty = false;
+  const csa_status st = compress_args("csa_compress", x, x_fmt, gate, gate_cols, n_tok, D, m, nseg,
+                                      seg_tok_off, seg_pos0, seg_out_row, normalize, norm_w, eps,
+                                      rope_dim, rope_base, out, out_fmt, &a, &empty);
+  if (st != CSA_OK) return st;
+  if (empty) { g_err[0] = '\0'; return CSA_OK; }
   return launched(launch_compress(a, stream), "csa_compress");
+}
+
+csa_status csa_compress_batch(const csa_compress_job* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 0 || n_jobs > CSA_COMPRESS_MAX_JOBS)
+    return fail(CSA_ERR_INVALID_ARG, "csa_compress_batch: n_jobs must be in [0, %d]",
+                CSA_COMPRESS_MAX_JOBS);
+  if (n_jobs > 0 && !jobs) return fail(CSA_ERR_INVALID_ARG, "csa_compress_batch: null jobs");
+  CompressArgs a[CSA_COMPRESS_MAX_JOBS];
+  int n = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const csa_compress_job& j = jobs[i];
+    char what[48];
+    snprintf(what, sizeof(what), "csa_compress_batch: job %d", i);
+    bool empty = false;
+    const csa_status st = compress_args(what, j.x, j.x_fmt, j.gate, j.gate_cols, j.n_tok, j.D, j.m,
+                                        j.nseg, j.seg_tok_off, j.seg_pos0, j.seg_out_row,
+                                        j.normalize, j.norm_w, j.eps, j.rope_dim, j.rope_base,
+                                        j.out, j.out_fmt, &a[n], &empty);
+    if (st != CSA_OK) return st;
+    if (!empty) ++n;
+  }
+  if (n == 0) { g_err[0] = '\0'; return CSA_OK; }
+  return launched(launch_compress_jobs(a, n, stream), "csa_compress_batch");
 }
 
 csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,

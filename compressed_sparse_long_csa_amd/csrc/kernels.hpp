@@ -26,6 +26,17 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
 
+constexpr int kMaxCompressJobs = 4;
+struct CompressJobs {
+  CompressArgs a[kMaxCompressJobs];
+  int64_t blk0[kMaxCompressJobs + 1];   // first global block of each job
+  int kind[kMaxCompressJobs];
+  int n;
+};
+static_assert(sizeof(CompressJobs) <= 4096, "kernel arguments are limited to 4 KiB");
+// Jobs with no complete block are skipped; n <= kMaxCompressJobs.
+hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t stream);
+
 struct IndexerArgs {
   const void* q; const float* w; int nq; int H; int d; const void* keys; csa_fmt fmt;
   const int64_t* key_off; const int64_t* q_pos; int m; float* scores; int64_t ld;

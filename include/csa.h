@@ -124,6 +124,50 @@ csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gat
                         hipStream_t stream);
 
 /*
+ * csa_compress_batch -- several csa_compress calls in one launch.
+ *
+ * Source: the same passages as csa_compress.  A decode step writes, for the
+ * same new tokens, the compressed KV entry, the matching indexer key and the
+ * sliding-window row; this call writes all of them with one kernel launch.
+ *
+ * Job i carries exactly the arguments of one csa_compress call and produces
+ * the same bytes as that call would (each output entry is computed by one
+ * workgroup in the same order).  The jobs run in no particular order, so
+ * their output rows must not overlap and no job may read what another
+ * writes.  `jobs` is a host array of n_jobs entries, read during the call
+ * only.
+ *
+ * Errors: INVALID_ARG if n_jobs < 0, n_jobs > CSA_COMPRESS_MAX_JOBS or jobs
+ * is NULL with n_jobs > 0; otherwise the first failing job's csa_compress
+ * error, with its job number in csa_last_error().  Nothing is launched when
+ * any job fails its checks.  Jobs with n_tok = 0 are skipped.
+ */
+#define CSA_COMPRESS_MAX_JOBS 4
+typedef struct csa_compress_job {
+  const void* x;
+  csa_fmt x_fmt;
+  const float* gate;
+  int gate_cols;
+  int64_t n_tok;
+  int D;
+  int m;
+  int nseg;
+  const int64_t* seg_tok_off;
+  const int64_t* seg_pos0;
+  const int64_t* seg_out_row;
+  int normalize;
+  const float* norm_w;
+  float eps;
+  int rope_dim;
+  float rope_base;
+  void* out;
+  csa_fmt out_fmt;
+} csa_compress_job;
+
+csa_status csa_compress_batch(const csa_compress_job* jobs /*[host]*/, int n_jobs,
+                              hipStream_t stream);
+
+/*
  * indexer_score -- lightning-indexer scores.
  *
  * Source: 硅星人 article, CSA paragraph and the indexer detail (multi-head

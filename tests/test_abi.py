@@ -93,6 +93,28 @@ def test_compress_argument_errors(lib):
     assert call(eps=-1.0) == INVALID
 
 
+def test_compress_batch_argument_errors(lib):
+    p = _fake()
+    job = binding.CompressJob(x=p.value, x_fmt=csa.F32, gate=p.value, gate_cols=1, n_tok=8, D=512,
+                              m=4, nseg=1, seg_tok_off=p.value, seg_pos0=p.value, seg_out_row=p.value,
+                              normalize=1, norm_w=None, eps=1e-6, rope_dim=64, rope_base=1e4,
+                              out=p.value, out_fmt=csa.SPLIT)
+    bad = binding.CompressJob.from_buffer_copy(job)
+    bad.m = 0
+    arr = (binding.CompressJob * 5)(job, bad, job, job, job)
+    for n in (-1, 5):
+        assert lib.csa_compress_batch(arr, n, None) == INVALID
+        assert "n_jobs" in _last_error(lib)
+    assert lib.csa_compress_batch(None, 2, None) == INVALID
+    # a failing job stops the call before any launch and is named
+    assert lib.csa_compress_batch(arr, 2, None) == INVALID
+    assert "job 1" in _last_error(lib)
+    assert lib.csa_compress_batch(arr, 0, None) == OK
+    empty = binding.CompressJob.from_buffer_copy(job)
+    empty.n_tok = 0
+    assert lib.csa_compress_batch((binding.CompressJob * 1)(empty), 1, None) == OK
+
+
 def test_attention_argument_errors(lib):
     p = _fake()
 

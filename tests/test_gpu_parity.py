@@ -123,6 +123,39 @@ def test_compress_matches_oracle(m, gate_cols, out_fmt, D, R):
     assert flips <= max(2, raw.size // 1000)
 
 
+@pytest.mark.parametrize("n_jobs", [3, 4])
+def test_compress_batch_matches_single_calls(n_jobs):
+    """One csa_compress_batch launch writes the same bytes as the jobs' own
+    csa_compress calls (KV entries, indexer keys, window rows, and an HCA
+    MXFP4 job that takes the generic block path)."""
+    specs = [(4, 512, 64, csa.SPLIT, True, [4 * 5, 0, 4 * 9]),
+             (4, 128, 0, csa.FP8, False, [4 * 5, 0, 4 * 9]),
+             (1, 512, 64, csa.BF16, True, [3, 1, 7]),
+             (128, 128, 0, csa.MXFP4, False, [256, 128])][:n_jobs]
+    jobs, singles = [], []
+    for j, (m, D, R, fmt, norm, seg_len) in enumerate(specs):
+        T = sum(seg_len)
+        tok = synth.token_inputs(70 + j, T, D)
+        nseg = len(seg_len)
+        off = np.concatenate([[0], np.cumsum(seg_len)]).astype(np.int64)
+        pos0 = (np.arange(nseg, dtype=np.int64) * 1000 + 17) * m
+        rows = np.concatenate([[2], 2 + np.cumsum([s // m for s in seg_len])[:-1]]).astype(np.int64)
+        n_rows = int(rows[-1] + seg_len[-1] // m)
+        rb = csa.row_bytes(fmt, D, R)
+        args = dict(x=dev(tok.x).to(torch.bfloat16), x_fmt=csa.BF16, gate=dev(tok.gate), gate_cols=1,
+                    n_tok=T, D=D, m=m, nseg=nseg, seg_tok_off=dev(off), seg_pos0=dev(pos0),
+                    seg_out_row=dev(rows), normalize=norm, norm_w=None, eps=EPS, rope_dim=R,
+                    rope_base=ROPE_BASE, out_fmt=fmt)
+        out_b = torch.full((n_rows * rb,), 0xA5, dtype=torch.uint8, device=DEV)
+        out_s = out_b.clone()
+        jobs.append(dict(args, out=out_b))
+        singles.append(out_s)
+        csa.csa_compress(*(args[f] for f in csa.binding.COMPRESS_JOB_FIELDS[:16]), out_s, fmt)
+    csa.csa_compress_batch(jobs)
+    for j, (job, ref) in enumerate(zip(jobs, singles)):
+        assert torch.equal(job["out"], ref), f"job {j}: batch bytes differ from csa_compress"
+
+
 # ------------------------------------------------------------------ indexer
 @pytest.mark.parametrize("fmt,H_I,d_I,lengths", [
     (csa.F32, 4, 64, [2048, 777, 5]),
