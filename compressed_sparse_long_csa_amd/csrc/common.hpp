@@ -98,6 +98,14 @@ __device__ __forceinline__ uint32_t buf_load_u32(buf_rsrc r, uint32_t byte_off) 
   return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0);
 }
 
+// A value the caller knows to be equal on every lane of the wave, moved to
+// scalar registers (so what is derived from it stays scalar).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // ------------------------------------------------------------------ wave reductions
 // Butterfly over the 64 lanes; the order of operations is fixed by the lane
 // pattern, so every lane ends with the same bits on every run.

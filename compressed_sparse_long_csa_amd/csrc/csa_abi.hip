@@ -161,7 +161,8 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
   if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "indexer_score: nq < 0");
   if (n_heads < 1 || d_idx < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: n_heads, d_idx must be >= 1");
   if (m < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: m must be >= 1");
-  if (ld < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: ld must be >= 1");
+  if (ld < 1 || ld > (int64_t{1} << 24))
+    return fail(CSA_ERR_INVALID_ARG, "indexer_score: ld must be in [1, 2^24]");
   if (fmt != CSA_F32 && fmt != CSA_FP8 && fmt != CSA_MXFP4)
     return fail(CSA_ERR_INVALID_ARG, "indexer_score: fmt must be CSA_F32, CSA_FP8 or CSA_MXFP4");
   if (fmt == CSA_F32) {

@@ -9,9 +9,10 @@
 //   I[i, s] = sum_h w[i, h] * max(0, q[i, h] . k[s])
 //
 // Decode streams every visible key once, so the kernels are HBM-bound: each
-// wave owns 128 keys, issues the loads of all of them (straight from global
-// memory into the MFMA operand registers) before converting its query, and
-// keeps the query in registers for all of them; two waves per SIMD.
+// wave owns 128 keys, issues the loads of its query and then of all its keys
+// (straight from global memory into the MFMA operand registers), and works
+// on each 16-key block as soon as that block has arrived, so the arithmetic
+// runs under the transfer; two waves per SIMD.
 //  * FP8 keys: the products must be exact for the top-k to be reproducible,
 //    and FP8 MFMA accumulation is not, so FP8 values are widened to BF16
 //    (exact) and multiplied on BF16 MFMA with fp32 accumulation.
@@ -21,8 +22,8 @@
 // The dims of one 128-dim vector are assigned to k-steps so that each lane
 // reads 32 contiguous bytes; the same permutation is applied to queries and
 // keys, so each dot product is the same sum.  The MFMA output is heads x
-// keys, so the head sum runs inside a lane (head blocks in order, then the
-// lane's four heads) and then over the four row groups in a fixed order.
+// keys, so the head sum runs inside a lane (a fixed tree over the lane's 16
+// heads) and then over the four row groups in a fixed order.
 #include "kernels.hpp"
 
 namespace csa {
@@ -72,15 +73,19 @@ __device__ __forceinline__ bool idx_item(const IndexerArgs& a, int64_t item, int
                                          int wv, int row_bytes, IdxItem* it) {
   it->i = static_cast<int>(item / n_chunk);
   const int64_t chunk = item % n_chunk;
-  int64_t N = (a.q_pos[it->i] + 1) / a.m;
+  // per-query values are wave-uniform: keep them (and the descriptor) in
+  // scalar registers, so buffer loads need no per-lane descriptor check.
+  // Both are read in one round trip.
+  const int64_t qpos = a.q_pos[it->i], koff = a.key_off[it->i];
+  int64_t N = (uniform64(qpos) + 1) / a.m;
   if (N > a.ld) N = a.ld;
   it->N = N;
   it->s0 = chunk * kKeysPerWg + wv * kKeysPerWave;
+  it->rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * row_bytes,
+                     static_cast<uint32_t>(N * row_bytes));
   if (it->s0 >= N) return false;                      // uniform over the wave (no barriers)
   const int64_t left = (N - it->s0 + 15) / 16;
   it->nb = left < kBatch ? static_cast<int>(left) : kBatch;
-  it->rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + a.key_off[it->i] * row_bytes,
-                     static_cast<uint32_t>(N * row_bytes));
   return true;
 }
 
@@ -94,15 +99,31 @@ __device__ __forceinline__ uint4 buf_load_x4(buf_rsrc r, uint32_t voff, uint32_t
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Score of the 16 keys of one block from its heads x keys MFMA tiles: lane
-// sums its 16 heads (blocks in order, rows r in order), then the row groups.
+// sums its 16 heads in a fixed tree (pairs of rows within a head block, then
+// head blocks pairwise), then the row groups.  The tree keeps the dependent
+// chain short; the order never changes, so the bits do not either.
 template <int NHB>
 __device__ __forceinline__ float head_sum(const f32x4 (&c)[NHB], const float (&wr)[NHB][4]) {
-  float part = 0.0f;
+  float s[NHB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb)
+    s[hb] = fmaf(wr[hb][1], relu(c[hb][1]), wr[hb][0] * relu(c[hb][0])) +
+            fmaf(wr[hb][3], relu(c[hb][3]), wr[hb][2] * relu(c[hb][2]));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part = fmaf(wr[hb][r], relu(c[hb][r]), part);
-  return rows_sum(part);
+  for (int w = 1; w < NHB; w *= 2)
+#pragma unroll
+    for (int hb = 0; hb + w < NHB; hb += 2 * w) s[hb] += s[hb + w];
+  return rows_sum(s[0]);
+}
+
+// Score stores: a descriptor over the query's N valid scores drops stores
+// past N; lanes other than row group 0 (which hold the same totals) aim past
+// every valid range.
+__device__ __forceinline__ buf_rsrc score_rsrc(const IndexerArgs& a, const IdxItem& it) {
+  return make_rsrc(a.scores + static_cast<int64_t>(it.i) * a.ld, static_cast<uint32_t>(it.N * 4));
+}
+__device__ __forceinline__ uint32_t score_voff(const IdxItem& it, int g, int j16) {
+  return g == 0 ? static_cast<uint32_t>(it.s0 + j16) * 4u : 0x80000000u;
 }
 
 // --------------------------------------------------------------- FP8, d = 128
@@ -110,13 +131,26 @@ template <int NHB>   // head blocks of 16
 __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
                                                           int64_t n_chunk) {
   constexpr int H = NHB * 16;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     IdxItem it;
     if (!idx_item(a, item, n_chunk, wv, 128, &it)) continue;
     const int i = it.i;
+    // query operand rows (head hb*16 + j16, dims [32g, 32g+32)) and the
+    // weights of the heads this lane sums (hb*16 + 4g + r), loaded before the
+    // keys so that waiting for them never waits for a key block
+    uint4 qraw[NHB][2];
+    float4 wraw[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
+      qraw[hb][0] = qp[0];
+      qraw[hb][1] = qp[1];
+      wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+    }
     // key rows: lane (key j16, dims [32g, 32g+32)) = 32 contiguous bytes
     const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * 128u + g * 32u;
     uint4 kr[kBatch][2];
@@ -125,22 +159,19 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
       kr[kb][0] = buf_load_x4(it.rs, voff, kb * 2048u);
       kr[kb][1] = buf_load_x4(it.rs, voff + 16u, kb * 2048u);
     }
-    // query operand: head hb*16 + j16, dims [32g, 32g+32) as 4 k-steps of 8;
-    // weights of the heads this lane sums: hb*16 + 4g + r
+    __builtin_amdgcn_sched_barrier(0);     // keep this issue order: block kb waits for itself only
     bf16x8 qb[NHB][4];
     float wr[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
-      const uint4 v0 = qp[0], v1 = qp[1];
-      qb[hb][0] = fp8x8_to_bf16(v0.x, v0.y);
-      qb[hb][1] = fp8x8_to_bf16(v0.z, v0.w);
-      qb[hb][2] = fp8x8_to_bf16(v1.x, v1.y);
-      qb[hb][3] = fp8x8_to_bf16(v1.z, v1.w);
-      const float4 wv4 = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
-      wr[hb][0] = wv4.x; wr[hb][1] = wv4.y; wr[hb][2] = wv4.z; wr[hb][3] = wv4.w;
+      qb[hb][0] = fp8x8_to_bf16(qraw[hb][0].x, qraw[hb][0].y);
+      qb[hb][1] = fp8x8_to_bf16(qraw[hb][0].z, qraw[hb][0].w);
+      qb[hb][2] = fp8x8_to_bf16(qraw[hb][1].x, qraw[hb][1].y);
+      qb[hb][3] = fp8x8_to_bf16(qraw[hb][1].z, qraw[hb][1].w);
+      wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
     }
-    float* out = a.scores + static_cast<int64_t>(i) * a.ld + it.s0 + j16;
+    const buf_rsrc out_rs = score_rsrc(a, it);
+    const uint32_t out_off = score_voff(it, g, j16);
     // software pipeline: the MFMAs of block kb run while the head sum of
     // block kb-1 is computed from its finished tiles
     f32x4 cp[NHB];
@@ -162,7 +193,8 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
       }
       if (kb > 0) {
         const float tot = head_sum<NHB>(cp, wr);
-        if (g == 0 && it.s0 + (kb - 1) * 16 + j16 < it.N) out[(kb - 1) * 16] = tot;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
+                                              (kb - 1) * 64, 0);
       }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
@@ -178,13 +210,27 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
                                                             int64_t n_chunk) {
   constexpr int H = NHB * 16;
   constexpr int RB = 68;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     IdxItem it;
     if (!idx_item(a, item, n_chunk, wv, RB, &it)) continue;
     const int i = it.i;
+    // query codes, scales and weights first (see the FP8 kernel)
+    i32x8 qop[NHB];
+    int qsc[NHB];
+    float4 wraw[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * RB;
+      const uint4 c4 = *reinterpret_cast<const uint4*>(row + g * 16);
+      qop[hb] = i32x8{static_cast<int>(c4.x), static_cast<int>(c4.y), static_cast<int>(c4.z),
+                      static_cast<int>(c4.w), 0, 0, 0, 0};
+      qsc[hb] = row[64 + g];
+      wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+    }
     const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * RB;
     uint4 kc[kBatch];
     uint32_t ksc[kBatch];
@@ -194,20 +240,14 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
       ksc[kb] = __builtin_amdgcn_raw_buffer_load_b8(it.rs, static_cast<int>(voff + 64u + g),
                                                     static_cast<int>(kb * 16u * RB), 0);
     }
-    i32x8 qop[NHB];
-    int qsc[NHB];
+    __builtin_amdgcn_sched_barrier(0);     // keep this issue order
     float wr[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * RB;
-      const uint4 c4 = *reinterpret_cast<const uint4*>(row + g * 16);
-      qop[hb] = i32x8{static_cast<int>(c4.x), static_cast<int>(c4.y), static_cast<int>(c4.z),
-                      static_cast<int>(c4.w), 0, 0, 0, 0};
-      qsc[hb] = row[64 + g];
-      const float4 wv4 = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
-      wr[hb][0] = wv4.x; wr[hb][1] = wv4.y; wr[hb][2] = wv4.z; wr[hb][3] = wv4.w;
+      wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
     }
-    float* out = a.scores + static_cast<int64_t>(i) * a.ld + it.s0 + j16;
+    const buf_rsrc out_rs = score_rsrc(a, it);
+    const uint32_t out_off = score_voff(it, g, j16);
     f32x4 cp[NHB];
 #pragma unroll
     for (int kb = 0; kb <= kBatch; ++kb) {
@@ -222,7 +262,8 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
       }
       if (kb > 0) {
         const float tot = head_sum<NHB>(cp, wr);
-        if (g == 0 && it.s0 + (kb - 1) * 16 + j16 < it.N) out[(kb - 1) * 16] = tot;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
+                                              (kb - 1) * 64, 0);
       }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];

@@ -190,6 +190,8 @@ csa_status csa_compress_batch(const csa_compress_job* jobs /*[host]*/, int n_job
  *   scores  [nq, ld] float32
  * Supported: F32 any n_heads <= 64, d_idx <= 256; FP8 / MXFP4 with n_heads a
  * multiple of 16 (<= 128) and d_idx == 128.  Else UNSUPPORTED.
+ * Errors: INVALID_ARG for ld < 1 or ld > 2^24 (16.7M entries, 64M tokens at
+ * m = 4), m < 1, nq < 0, null pointers, a format other than the three above.
  */
 csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
                          const void* keys, csa_fmt fmt, const int64_t* key_off,

@@ -135,10 +135,12 @@ def test_attention_argument_errors(lib):
 def test_indexer_argument_errors(lib):
     p = _fake()
 
-    def call(fmt=csa.FP8, H=64, d=128, nq=2, m=4):
-        return lib.indexer_score(p, p, nq, H, d, p, fmt, p, p, m, p, ctypes.c_int64(1024), None)
+    def call(fmt=csa.FP8, H=64, d=128, nq=2, m=4, ld=1024):
+        return lib.indexer_score(p, p, nq, H, d, p, fmt, p, p, m, p, ctypes.c_int64(ld), None)
     assert call(fmt=csa.SPLIT) in (INVALID, UNSUPPORTED)
     assert call(d=96) in (INVALID, UNSUPPORTED)      # FP8 / MXFP4 keys are 128-dim
     assert call(H=40) in (INVALID, UNSUPPORTED)
     assert call(m=0) == INVALID
+    assert call(ld=0) == INVALID
+    assert call(ld=(1 << 24) + 1) == INVALID          # key rows must stay under 2^31 bytes
     assert call(nq=0) == OK
