@@ -39,24 +39,29 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ window bounds
-__device__ __forceinline__ void window_of(const AttnArgs& a, int b, int64_t p, int64_t* row0,
+__device__ __forceinline__ void window_of(const AttnArgs& a, int b, int64_t p, int win_len,
+                                          int64_t tok_pos0, int64_t tok_off, int64_t* row0,
                                           int* count) {
   if (a.win_mode == 0 || a.n_win == 0) {   // no window
     *row0 = 0;
     *count = 0;
   } else if (a.win_mode == 1) {             // decode: rows [0, win_len) of win[b]
-    int c = a.win_len[b];
-    c = c < 0 ? 0 : (c > a.n_win ? a.n_win : c);
+    const int c = win_len < 0 ? 0 : (win_len > a.n_win ? a.n_win : win_len);
     *row0 = static_cast<int64_t>(b) * a.n_win;
     *count = c;
   } else {                                  // prefill: positions max(0, p-n_win+1) .. p of the run
     int64_t first = p - a.n_win + 1;
     if (first < 0) first = 0;
-    if (first < a.tok_pos0[b]) first = a.tok_pos0[b];
+    if (first < tok_pos0) first = tok_pos0;
     const int64_t c = p - first + 1;
-    *row0 = a.tok_off[b] + (first - a.tok_pos0[b]);
+    *row0 = tok_off + (first - tok_pos0);
     *count = c > 0 ? static_cast<int>(c) : 0;
   }
+}
+__device__ __forceinline__ void window_of(const AttnArgs& a, int b, int64_t p, int64_t* row0,
+                                          int* count) {
+  window_of(a, b, p, a.win_mode == 1 ? a.win_len[b] : 0, a.win_mode == 2 ? a.tok_pos0[b] : 0,
+            a.win_mode == 2 ? a.tok_off[b] : 0, row0, count);
 }
 
 // ================================================================== fp32 path
@@ -147,7 +152,7 @@ constexpr int kPPitch = 20;                             // padded rows of the P 
 constexpr float kPScale = 256.0f;                       // probabilities are stored x 2^8
 constexpr int kQPitch = kD + 8;                         // staging rows of the normalised queries
 static_assert(kStepW * kPitchWin <= kBufBytes, "window step must fit a buffer");
-static_assert(16 * kQPitch * 2 <= 2 * kBufBytes, "query staging must fit wave 0's buffers");
+static_assert(8 * kQPitch * 2 <= kBufBytes, "eight staged query rows must fit one buffer");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -237,51 +242,82 @@ struct Work {
   buf_rsrc kv_rs, win_rs;
 };
 
-// Lane-held entry of the compressed step `step` (lanes < 16) and its validity.
-__device__ __forceinline__ int step_entry(const Work& w, int step, int wv, bool* ok) {
-  const int lane = threadIdx.x & 63;
-  *ok = false;
-  if (step >= w.ns || lane >= kStepE) return 0;
-  const int pos = step * (kWaves * kStepE) + wv * kStepE + lane;
-  int e = pos;
-  bool v = pos < w.n_list;
-  if (w.idx != nullptr) {
-    // the load does not wait for the visibility test: its address is clamped
-    e = w.idx[pos < w.k ? pos : w.k - 1];
-    v = v && e >= 0 && e < w.N;
-  }
-  *ok = v;
-  return v ? e : 0;
+// The selected entries of a wave's first kTabSteps compressed steps, read
+// in the prologue: register t, lane l holds step 4 t + l / 16, row l % 16
+// (entry 0 where the slot is empty or invalid), and `valid` the matching
+// ballot.  Later steps (lists longer than 1024) read theirs in the loop.
+constexpr int kTabSteps = 8;
+struct EntryTab {
+  int e[kTabSteps / 4];
+  uint64_t valid[kTabSteps / 4];
+};
+
+// Selected entry of list position pos, and whether it is a visible entry.
+__device__ __forceinline__ int list_entry(const Work& w, int pos, bool* ok) {
+  // the load does not wait for the range test: its address is clamped
+  const int e = w.idx[pos < w.k ? pos : w.k - 1];
+  *ok = pos < w.n_list && e >= 0 && e < w.N;
+  return *ok ? e : 0;
 }
 
 // Direct buffer->LDS loads of one wave step into `dst`; returns the step's
 // row-validity mask (bit r = row r holds a real entry).  Rows without an
-// entry load entry 0 / window row 0 and stay masked.
-__device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, int my_e,
-                                               bool my_ok, uint8_t* dst) {
+// entry load entry 0, or read as zeros past the end of the query's rows, and
+// stay masked.  A compressed step is 16 load instructions, a window step 8
+// (the loop's wait counts rely on it).
+__device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, const EntryTab& tab,
+                                               uint8_t* dst) {
   const int lane = threadIdx.x & 63;
   typedef __attribute__((address_space(3))) void lds_void;
   if (step < w.ns) {
-    if (lane < kChunksSplit) {
+    const int pos0 = step * (kWaves * kStepE) + wv * kStepE;
+    uint32_t vmask;
+    int ereg = 0, base = 0;
+    if (w.idx == nullptr) {
+      const int nv = w.n_list - pos0;
+      vmask = nv >= kStepE ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+    } else if (step < kTabSteps) {
+      ereg = tab.e[0];
+      uint64_t vb = tab.valid[0];
 #pragma unroll
-      for (int r = 0; r < kStepE; ++r) {
-        const int e = __builtin_amdgcn_readlane(my_e, r);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w.kv_rs, (lds_void*)(lds_ptr(dst + r * kPitchSplit)),
-                                                 16, lane * 16, e * kRowSplit, 0, 0);
+      for (int t = 1; t < kTabSteps / 4; ++t)
+        if ((step >> 2) == t) { ereg = tab.e[t]; vb = tab.valid[t]; }
+      base = (step & 3) * 16;
+      vmask = static_cast<uint32_t>(vb >> base) & 0xffffu;
+    } else {
+      bool ok = false;
+      if (lane < kStepE) ereg = list_entry(w, pos0 + lane, &ok);
+      vmask = static_cast<uint32_t>(__ballot(lane < kStepE && ok));
+    }
+    if (lane < kChunksSplit) {
+      if (w.idx == nullptr) {
+        // (an HCA row past the query's N entries reads as zeros: buffer range check)
+#pragma unroll
+        for (int r = 0; r < kStepE; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w.kv_rs, (lds_void*)(lds_ptr(dst + r * kPitchSplit)),
+                                                   16, lane * 16, (pos0 + r) * kRowSplit, 0, 0);
+      } else {
+#pragma unroll
+        for (int r = 0; r < kStepE; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w.kv_rs, (lds_void*)(lds_ptr(dst + r * kPitchSplit)),
+                                                   16, lane * 16,
+                                                   __builtin_amdgcn_readlane(ereg, base + r) * kRowSplit, 0, 0);
       }
     }
-    return static_cast<uint32_t>(__ballot(lane < kStepE && my_ok));
+    return vmask;
   }
   const int j0 = (step - w.ns) * (kWaves * kStepW) + wv * kStepW;
 #pragma unroll
-  for (int r = 0; r < kStepW; ++r) {
-    const int src = j0 + r < w.win_count ? j0 + r : 0;
+  for (int r = 0; r < kStepW; ++r)       // rows past the window read as zeros
     __builtin_amdgcn_raw_ptr_buffer_load_lds(w.win_rs, (lds_void*)(lds_ptr(dst + r * kPitchWin)),
-                                             16, lane * 16, src * kRowBf16, 0, 0);
-  }
+                                             16, lane * 16, (j0 + r) * kRowBf16, 0, 0);
   const int nv = w.win_count - j0;
   return nv >= kStepW ? (1u << kStepW) - 1u : (nv <= 0 ? 0u : (1u << nv) - 1u);
 }
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (the
+// other counters not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Online-softmax update of head j16 from this lane's 4 logits t (log2
 // domain): returns alpha and writes the probabilities p = 2^(t - m_new).
@@ -309,17 +345,23 @@ __device__ __forceinline__ float softmax_step(const float (&t)[4], float (&pv)[4
 template <int NB, int NF>
 __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, const bf16x8 (&qb)[kD / 32],
                                            float ch, int dbase, float& m_run, float& l_run,
-                                           f32x4 (&acc)[NB], int e_next, bool ok_next,
-                                           uint32_t vmask_cur) {
+                                           f32x4 (&acc)[NB], const EntryTab& tab, uint32_t vmask_cur) {
   const int lane = threadIdx.x & 63, g = lane >> 4, j16 = lane & 15;
   for (int step = 0; step < w.n_steps; ++step) {
     const int bi = step & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this step's rows landed
-    const uint32_t vmask = vmask_cur;
+    // the next step's rows go out first (its buffer was read to the end by
+    // the previous step), then the wait leaves exactly those loads in flight:
+    // two steps of rows are in flight while a step computes
+    uint32_t vmask_next = 0u;
     if (step + 1 < w.n_steps) {
-      vmask_cur = issue_step(w, step + 1, wv, e_next, ok_next, ws.buf[bi ^ 1]);
-      e_next = step_entry(w, step + 2, wv, &ok_next);
+      vmask_next = issue_step(w, step + 1, wv, tab, ws.buf[bi ^ 1]);
+      if (step + 1 < w.ns) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepE));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    const uint32_t vmask = vmask_cur;
+    vmask_cur = vmask_next;
     const uint8_t* T = ws.buf[bi];
     float alpha;
     const bool split = step < w.ns;
@@ -481,8 +523,10 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const int g = lane >> 4, j16 = lane & 15;
   WaveSmem& ws = sm.wave[wv];
 
-  // this lane's part of the query (head 2 wv + lane / 32, dims [16 (lane % 32), +16)),
-  // loaded first: it depends on nothing else
+  // ---------------- everything the prologue reads goes out at once: this
+  // lane's part of the query (head 2 wv + lane / 32, dims [16 (lane % 32),
+  // +16)), its RoPE frequency, the head's sink, the query's position, cache
+  // offset and window, and the wave's selected entries (validated below)
   const int qh = wv * 2 + (lane >> 5), qc = lane & 31;
   uint4 qraw[2];
   {
@@ -491,14 +535,26 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     qraw[0] = q[0];
     qraw[1] = q[1];
   }
+  const double theta = a.rope_theta[tid < kR / 2 ? tid : 0];
+  const float sink = a.sinks[ht * 16 + j16];
+  const int64_t p_ld = a.q_pos[b], kv0_ld = a.kv_off[b];
+  const int wl_ld = a.win_mode == 1 ? a.win_len[b] : 0;
+  const int64_t tp0_ld = a.win_mode == 2 ? a.tok_pos0[b] : 0, toff_ld = a.win_mode == 2 ? a.tok_off[b] : 0;
+  const int32_t* idx_q = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
+  int e_ld[kTabSteps / 4];
+#pragma unroll
+  for (int t = 0; t < kTabSteps / 4; ++t) {
+    const int pos = (4 * t + (lane >> 4)) * (kWaves * kStepE) + wv * kStepE + (lane & 15);
+    e_ld[t] = idx_q != nullptr ? idx_q[pos < a.k ? pos : a.k - 1] : 0;   // clamped address
+  }
 
   Work w;
-  w.p = a.q_pos[b];
+  w.p = uniform64(p_ld);
   w.N = (w.p + 1) / a.m;
-  const int64_t kv0 = a.kv_off[b];
+  const int64_t kv0 = uniform64(kv0_ld);
   int64_t win_row0;
-  window_of(a, b, w.p, &win_row0, &w.win_count);
-  w.idx = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
+  window_of(a, b, w.p, wl_ld, uniform64(tp0_ld), uniform64(toff_ld), &win_row0, &w.win_count);
+  w.idx = idx_q;
   w.k = a.k;
   w.n_list = a.idx != nullptr ? (w.N > 0 ? a.k : 0) : static_cast<int>(w.N);
   w.ns = (w.n_list + kWaves * kStepE - 1) / (kWaves * kStepE);
@@ -508,27 +564,35 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
                       kv_bytes < 0xffffffffull ? static_cast<uint32_t>(kv_bytes) : 0xffffffffu);
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                        static_cast<uint32_t>(w.win_count) * kRowBf16);
-
-  // first step's rows go out before anything else -- except in wave 0, whose
-  // two buffers hold the query staging copy until the prologue is done
-  bool ok0, ok1;
-  const int e0 = step_entry(w, 0, wv, &ok0);
-  const int e1 = step_entry(w, 1, wv, &ok1);
+  EntryTab tab;
+#pragma unroll
+  for (int t = 0; t < kTabSteps / 4; ++t) {
+    const int step = 4 * t + (lane >> 4);
+    const int pos = step * (kWaves * kStepE) + wv * kStepE + (lane & 15);
+    const bool ok = w.idx != nullptr && step < w.ns && pos < w.n_list && e_ld[t] >= 0 && e_ld[t] < w.N;
+    tab.e[t] = ok ? e_ld[t] : 0;
+    tab.valid[t] = __ballot(ok);
+  }
+  // the first step's rows go out before the query is prepared
   uint32_t vmask0 = 0u;
-  if (wv != 0 && w.n_steps > 0) vmask0 = issue_step(w, 0, wv, e0, ok0, ws.buf[0]);
+  if (w.n_steps > 0) vmask0 = issue_step(w, 0, wv, tab, ws.buf[0]);
 
   if (tid < kR / 2) {
     float sn, cs;
-    rope_sincos(w.p, a.rope_theta[tid], &sn, &cs);
+    rope_sincos(w.p, theta, &sn, &cs);
     sm.rope_cs[tid][0] = cs;
     sm.rope_cs[tid][1] = sn;
   }
 
   // ---------------- prologue: qhat = RoPE(RMSNorm(q)); wave w prepares heads
   // 2w, 2w+1 (lane: head 2w + lane/32, dims [16 (lane%32), +16)) into a bf16
-  // staging copy in wave 0's buffers, then every lane takes its QK operand.
-  // (rows padded to 520 values so the 16 heads' rows start on different banks)
-  uint16_t(*qbf)[kQPitch] = reinterpret_cast<uint16_t(*)[kQPitch]>(&sm.wave[0].buf[0][0]);
+  // staging copy (heads 0-7 in wave 0's second buffer, 8-15 in wave 1's: the
+  // second buffers receive rows only once the loop starts), then every lane
+  // takes its QK operand.  Rows are padded to 520 values so that the heads'
+  // rows start on different banks.
+  auto qrow = [&](int h) __attribute__((always_inline)) {
+    return reinterpret_cast<uint16_t*>(&sm.wave[h >> 3].buf[1][0]) + (h & 7) * kQPitch;
+  };
   {
     const int h = qh, c = qc;                           // head in tile, 16-dim chunk
     float x[16];
@@ -548,8 +612,17 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     const float r = static_cast<float>(1.0 / sqrt(static_cast<double>(ss) / kD + a.eps));
+    if (a.q_norm_w != nullptr) {
+      const float4* gw = reinterpret_cast<const float4*>(a.q_norm_w + c * 16);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) x[t] = x[t] * r * (a.q_norm_w ? a.q_norm_w[c * 16 + t] : 1.0f);
+      for (int t = 0; t < 4; ++t) {
+        const float4 gv = gw[t];
+        x[4 * t] *= r * gv.x; x[4 * t + 1] *= r * gv.y; x[4 * t + 2] *= r * gv.z; x[4 * t + 3] *= r * gv.w;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) x[t] *= r;
+    }
     __syncthreads();                                    // rope_cs ready
     if (c * 16 >= kD - kR) {
       const int p0 = (c * 16 - (kD - kR)) / 2;
@@ -568,29 +641,28 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
       v.y = bf16x2_rne(x[t + 2], x[t + 3]);
       v.z = bf16x2_rne(x[t + 4], x[t + 5]);
       v.w = bf16x2_rne(x[t + 6], x[t + 7]);
-      *reinterpret_cast<uint4*>(&qbf[h][c * 16 + t]) = v;
+      *reinterpret_cast<uint4*>(qrow(h) + c * 16 + t) = v;
     }
   }
   __syncthreads();
   // QK operand of this lane: head j16, dims [32*ks + 8*g, +8)
   bf16x8 qb[kD / 32];
 #pragma unroll
-  for (int ks = 0; ks < kD / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(&qbf[j16][ks * 32 + g * 8]);
+  for (int ks = 0; ks < kD / 32; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow(j16) + ks * 32 + g * 8);
   const float ch = a.scale * kLog2e;
   __syncthreads();                                      // the staging copy is free again
-  if (wv == 0 && w.n_steps > 0) vmask0 = issue_step(w, 0, wv, e0, ok0, ws.buf[0]);
 
   // softmax state of head j16 (the same in the four lanes of that head); the
   // sink enters once, through wave 0
-  float m_run = a.sinks[ht * 16 + j16] * kLog2e;
+  float m_run = sink * kLog2e;
   float l_run = wv == 0 ? 1.0f : 0.0f;
   f32x4 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (dbase + DWG <= kDF8)
-    entry_loop<NB, NB>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, e1, ok1, vmask0);
+    entry_loop<NB, NB>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
   else
-    entry_loop<NB, NFR>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, e1, ok1, vmask0);
+    entry_loop<NB, NFR>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
 
   // -------- merge the waves' states in wave order, then out = acc / (2^8 * l)
   __syncthreads();                                      // every wave is done with its buffers
