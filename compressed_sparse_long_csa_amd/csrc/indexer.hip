@@ -127,21 +127,84 @@ __device__ __forceinline__ uint32_t score_voff(const IdxItem& it, int g, int j16
 }
 
 // --------------------------------------------------------------- FP8, d = 128
+// Each wave streams a run of R groups of 64 keys (4 blocks of 16) of one
+// query: the loads of group t+2 go out as soon as group t has been
+// multiplied, so two groups are in flight while one computes, and the query
+// stays in registers for the whole run.
+constexpr int kGroupKeys = 64;
+
+// lane (key j16 of block kb, dims [32g, 32g+32)) = 32 contiguous bytes; a
+// group past the run aims past the end of the buffer (zeros, no traffic)
+__device__ __forceinline__ void load_group_fp8(buf_rsrc rs, uint32_t voff0, int t, int ng, uint4 (&kr)[4][2]) {
+  const uint32_t base = t < ng ? voff0 + static_cast<uint32_t>(t) * (kGroupKeys * 128u) : 0x80000000u;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    kr[kb][0] = buf_load_x4(rs, base, kb * 2048u);
+    kr[kb][1] = buf_load_x4(rs, base + 16u, kb * 2048u);
+  }
+}
+
+// MFMAs of one group's blocks; block kb's head sum is computed (and stored)
+// while block kb+1 multiplies.  `done` counts the run's blocks multiplied so
+// far, `live` the blocks whose scores are kept (4 per group of the run).
+// Every block issues exactly one store (a store with nothing to keep aims
+// past the buffer), so each pass of the group loop issues the same memory
+// operations and the compiler's wait counts stay exact.
+template <int NHB>
+__device__ __forceinline__ void group_fp8(const uint4 (&kr)[4][2], const bf16x8 (&qb)[NHB][4],
+                                          const float (&wr)[NHB][4], f32x4 (&cp)[NHB], int& done,
+                                          int live, buf_rsrc out_rs, uint32_t out_off) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bf16x8 kk[4] = {fp8x8_to_bf16(kr[kb][0].x, kr[kb][0].y), fp8x8_to_bf16(kr[kb][0].z, kr[kb][0].w),
+                          fp8x8_to_bf16(kr[kb][1].x, kr[kb][1].y), fp8x8_to_bf16(kr[kb][1].z, kr[kb][1].w)};
+    f32x4 cc[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) cc[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // rows = heads (A), cols = keys (B); the NHB chains interleave
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
+    {
+      const float tot = head_sum<NHB>(cp, wr);   // (block done-1; nothing to keep when done = 0)
+      const bool keep = done > 0 && done <= live;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs,
+                                            static_cast<int>(keep ? out_off : 0x80000000u),
+                                            keep ? (done - 1) * 64 : 0, 0);
+    }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
+    ++done;
+  }
+}
+
 template <int NHB>   // head blocks of 16
 __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
-                                                          int64_t n_chunk) {
+                                                          int64_t n_chunk, int R) {
   constexpr int H = NHB * 16;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
+  const int64_t run_keys = static_cast<int64_t>(R) * kGroupKeys;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    IdxItem it;
-    if (!idx_item(a, item, n_chunk, wv, 128, &it)) continue;
-    const int i = it.i;
+    // query i; wave wv's run: keys [s0, s0 + R*64) of chunk `item % n_chunk`
+    const int i = static_cast<int>(item / n_chunk);
+    const int64_t chunk = item % n_chunk;
+    const int64_t qpos = a.q_pos[i], koff = a.key_off[i];
+    int64_t N = (uniform64(qpos) + 1) / a.m;
+    if (N > a.ld) N = a.ld;
+    const int64_t s0 = (chunk * 4 + wv) * run_keys;
+    const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * 128,
+                                  static_cast<uint32_t>(N * 128));
+    if (s0 >= N) continue;                               // uniform over the wave (no barriers)
+    const int64_t left = (N - s0 + kGroupKeys - 1) / kGroupKeys;
+    const int ng = left < R ? static_cast<int>(left) : R;
     // query operand rows (head hb*16 + j16, dims [32g, 32g+32)) and the
-    // weights of the heads this lane sums (hb*16 + 4g + r), loaded before the
-    // keys so that waiting for them never waits for a key block
+    // weights of the heads this lane sums (hb*16 + 4g + r),
+    // loaded before the keys so that waiting for them never waits for a key group
     uint4 qraw[NHB][2];
     float4 wraw[NHB];
 #pragma unroll
@@ -151,15 +214,11 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
       qraw[hb][1] = qp[1];
       wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
     }
-    // key rows: lane (key j16, dims [32g, 32g+32)) = 32 contiguous bytes
-    const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * 128u + g * 32u;
-    uint4 kr[kBatch][2];
-#pragma unroll
-    for (int kb = 0; kb < kBatch; ++kb) {
-      kr[kb][0] = buf_load_x4(it.rs, voff, kb * 2048u);
-      kr[kb][1] = buf_load_x4(it.rs, voff + 16u, kb * 2048u);
-    }
-    __builtin_amdgcn_sched_barrier(0);     // keep this issue order: block kb waits for itself only
+    const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * 128u + g * 32u;
+    uint4 ka[4][2], kb[4][2];
+    load_group_fp8(rs, voff0, 0, ng, ka);
+    load_group_fp8(rs, voff0, 1, ng, kb);
+    __builtin_amdgcn_sched_barrier(0);     // keep this issue order
     bf16x8 qb[NHB][4];
     float wr[NHB][4];
 #pragma unroll
@@ -170,35 +229,26 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
       qb[hb][3] = fp8x8_to_bf16(qraw[hb][1].z, qraw[hb][1].w);
       wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
     }
-    const buf_rsrc out_rs = score_rsrc(a, it);
-    const uint32_t out_off = score_voff(it, g, j16);
-    // software pipeline: the MFMAs of block kb run while the head sum of
-    // block kb-1 is computed from its finished tiles
+    // scores: a descriptor over the query's N valid scores drops stores past
+    // N; lanes other than row group 0 (which hold the same totals) aim past it
+    const buf_rsrc out_rs = make_rsrc(a.scores + static_cast<int64_t>(i) * a.ld, static_cast<uint32_t>(N * 4));
+    const uint32_t out_off = g == 0 ? static_cast<uint32_t>(s0 + j16) * 4u : 0x80000000u;
     f32x4 cp[NHB];
-#pragma unroll
-    for (int kb = 0; kb <= kBatch; ++kb) {
-      // blocks past N hold zero rows (the buffer range check); their scores are not stored
-      f32x4 cc[NHB];
-      if (kb < kBatch) {
-        const bf16x8 kk[4] = {fp8x8_to_bf16(kr[kb][0].x, kr[kb][0].y), fp8x8_to_bf16(kr[kb][0].z, kr[kb][0].w),
-                              fp8x8_to_bf16(kr[kb][1].x, kr[kb][1].y), fp8x8_to_bf16(kr[kb][1].z, kr[kb][1].w)};
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) cc[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        // rows = heads (A), cols = keys (B); the NHB chains interleave
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-            cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
-      }
-      if (kb > 0) {
-        const float tot = head_sum<NHB>(cp, wr);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
-                                              (kb - 1) * 64, 0);
-      }
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
+    for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int done = 0;
+    const int live = 4 * ng;
+    // groups in pairs, both always processed (a group past the run holds
+    // zeros and keeps no score)
+    for (int t = 0; t < ng; t += 2) {
+      group_fp8<NHB>(ka, qb, wr, cp, done, live, out_rs, out_off);
+      load_group_fp8(rs, voff0, t + 2, ng, ka);
+      group_fp8<NHB>(kb, qb, wr, cp, done, live, out_rs, out_off);
+      load_group_fp8(rs, voff0, t + 3, ng, kb);
     }
+    const float tot = head_sum<NHB>(cp, wr);
+    if (done <= live)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
+                                            (done - 1) * 64, 0);
   }
 }
 
@@ -308,22 +358,35 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
                        shm, stream, a, n_chunk);
     return hipGetLastError();
   }
-  const int64_t n_chunk = (a.ld + kKeysPerWg - 1) / kKeysPerWg;
-  const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-  const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
   const int nhb = a.H / 16;
-#define CSA_IDX_CASE(K, NB) \
-  case NB: hipLaunchKernelGGL(K<NB>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk); break;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
   if (a.fmt == CSA_FP8) {
+    // run length: enough 64-key groups per wave that one round of two waves
+    // per SIMD covers the batch, at least 2 (two groups in flight), at most 32
+    const int64_t groups = static_cast<int64_t>(a.nq) * ((a.ld + kGroupKeys - 1) / kGroupKeys);
+    const int64_t waves = static_cast<int64_t>(device_cu_count()) * 8;
+    int64_t R = (groups + waves - 1) / waves;
+    R = R < 2 ? 2 : (R > 32 ? 32 : R);
+    const int64_t item_keys = 4 * R * kGroupKeys;
+    const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
+    const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
+    const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
+    const int r = static_cast<int>(R);
     switch (nhb) {
-      CSA_IDX_CASE(indexer_fp8_kernel, 1)
-      CSA_IDX_CASE(indexer_fp8_kernel, 2)
-      CSA_IDX_CASE(indexer_fp8_kernel, 4)
-      CSA_IDX_CASE(indexer_fp8_kernel, 8)
+      case 1: hipLaunchKernelGGL(indexer_fp8_kernel<1>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
+      case 2: hipLaunchKernelGGL(indexer_fp8_kernel<2>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
+      case 4: hipLaunchKernelGGL(indexer_fp8_kernel<4>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
+      case 8: hipLaunchKernelGGL(indexer_fp8_kernel<8>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
       default: return hipErrorInvalidValue;
     }
-  } else {
+    return hipGetLastError();
+  }
+  const int64_t n_chunk = (a.ld + kKeysPerWg - 1) / kKeysPerWg;
+  const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
+  const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
+#define CSA_IDX_CASE(K, NB) \
+  case NB: hipLaunchKernelGGL(K<NB>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk); break;
+  {
     switch (nhb) {
       CSA_IDX_CASE(indexer_mxfp4_kernel, 1)
       CSA_IDX_CASE(indexer_mxfp4_kernel, 2)
