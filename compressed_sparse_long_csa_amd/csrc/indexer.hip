@@ -127,16 +127,20 @@ __device__ __forceinline__ uint32_t score_voff(const IdxItem& it, int g, int j16
 }
 
 // --------------------------------------------------------------- FP8, d = 128
-// Each wave streams a run of R groups of 64 keys (4 blocks of 16) of one
-// query: the loads of group t+2 go out as soon as group t has been
-// multiplied, so two groups are in flight while one computes, and the query
-// stays in registers for the whole run.
+// Each wave streams up to R groups of 64 keys (4 blocks of 16) of one query:
+// the loads of group t+2 go out as soon as group t has been multiplied, so
+// two groups are in flight while one computes, and the query stays in
+// registers throughout.  With long shares (R > 2) the W waves of a query
+// take its groups in turn (wave w: groups w, w+W, w+2W, ...), so the groups
+// being read at any moment lie next to each other in memory; with R <= 2
+// every load is issued at once anyway, and wave w takes groups [wR, wR+R).
 constexpr int kGroupKeys = 64;
 
 // lane (key j16 of block kb, dims [32g, 32g+32)) = 32 contiguous bytes; a
 // group past the run aims past the end of the buffer (zeros, no traffic)
-__device__ __forceinline__ void load_group_fp8(buf_rsrc rs, uint32_t voff0, int t, int ng, uint4 (&kr)[4][2]) {
-  const uint32_t base = t < ng ? voff0 + static_cast<uint32_t>(t) * (kGroupKeys * 128u) : 0x80000000u;
+__device__ __forceinline__ void load_group_fp8(buf_rsrc rs, uint32_t voff0, uint32_t stride, int t, int ng,
+                                               uint4 (&kr)[4][2]) {
+  const uint32_t base = t < ng ? voff0 + static_cast<uint32_t>(t) * stride : 0x80000000u;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     kr[kb][0] = buf_load_x4(rs, base, kb * 2048u);
@@ -144,16 +148,17 @@ __device__ __forceinline__ void load_group_fp8(buf_rsrc rs, uint32_t voff0, int 
   }
 }
 
-// MFMAs of one group's blocks; block kb's head sum is computed (and stored)
-// while block kb+1 multiplies.  `done` counts the run's blocks multiplied so
-// far, `live` the blocks whose scores are kept (4 per group of the run).
-// Every block issues exactly one store (a store with nothing to keep aims
-// past the buffer), so each pass of the group loop issues the same memory
-// operations and the compiler's wait counts stay exact.
+// MFMAs of one group's blocks; the head sum of the block before (held in
+// cp) is computed and stored while a block multiplies.  `pend` is the score
+// offset (bytes, relative to the lane's first score) of the block in cp, or
+// -1 when there is none to keep; `grp` that of this group, or -1 for a group
+// past the wave's share.  Every block issues exactly one store (one with
+// nothing to keep aims past the buffer), so each pass of the group loop
+// issues the same memory operations and the compiler's wait counts stay exact.
 template <int NHB>
 __device__ __forceinline__ void group_fp8(const uint4 (&kr)[4][2], const bf16x8 (&qb)[NHB][4],
-                                          const float (&wr)[NHB][4], f32x4 (&cp)[NHB], int& done,
-                                          int live, buf_rsrc out_rs, uint32_t out_off) {
+                                          const float (&wr)[NHB][4], f32x4 (&cp)[NHB], int& pend, int grp,
+                                          buf_rsrc out_rs, uint32_t out_off) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const bf16x8 kk[4] = {fp8x8_to_bf16(kr[kb][0].x, kr[kb][0].y), fp8x8_to_bf16(kr[kb][0].z, kr[kb][0].w),
@@ -167,20 +172,17 @@ __device__ __forceinline__ void group_fp8(const uint4 (&kr)[4][2], const bf16x8 
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
         cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
-    {
-      const float tot = head_sum<NHB>(cp, wr);   // (block done-1; nothing to keep when done = 0)
-      const bool keep = done > 0 && done <= live;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs,
-                                            static_cast<int>(keep ? out_off : 0x80000000u),
-                                            keep ? (done - 1) * 64 : 0, 0);
-    }
+    const float tot = head_sum<NHB>(cp, wr);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs,
+                                          static_cast<int>(pend >= 0 ? out_off : 0x80000000u),
+                                          pend >= 0 ? pend : 0, 0);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
-    ++done;
+    pend = grp >= 0 ? grp + kb * 64 : -1;
   }
 }
 
-template <int NHB>   // head blocks of 16
+template <int NHB, bool IL>   // head blocks of 16; interleaved shares
 __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
                                                           int64_t n_chunk, int R) {
   constexpr int H = NHB * 16;
@@ -188,20 +190,27 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
-  const int64_t run_keys = static_cast<int64_t>(R) * kGroupKeys;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    // query i; wave wv's run: keys [s0, s0 + R*64) of chunk `item % n_chunk`
+    // query i; item `chunk` holds four of the query's waves
     const int i = static_cast<int>(item / n_chunk);
     const int64_t chunk = item % n_chunk;
     const int64_t qpos = a.q_pos[i], koff = a.key_off[i];
     int64_t N = (uniform64(qpos) + 1) / a.m;
     if (N > a.ld) N = a.ld;
-    const int64_t s0 = (chunk * 4 + wv) * run_keys;
+    // (N <= 2^24, so group counts fit 32 bits)
+    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;                     // waves of this query
+    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);   // this wave's turn
+    const uint32_t G = static_cast<uint32_t>((N + kGroupKeys - 1) / kGroupKeys);
     const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * 128,
                                   static_cast<uint32_t>(N * 128));
-    if (s0 >= N) continue;                               // uniform over the wave (no barriers)
-    const int64_t left = (N - s0 + kGroupKeys - 1) / kGroupKeys;
-    const int ng = left < R ? static_cast<int>(left) : R;
+    // the wave's groups: first, first + step, ...
+    const uint32_t first = IL ? wq : wq * static_cast<uint32_t>(R);
+    const uint32_t step = IL ? W : 1u;
+    if (first >= G) continue;                            // uniform over the wave (no barriers)
+    const uint32_t mine = (G - first + step - 1u) / step;
+    const int ng = mine < static_cast<uint32_t>(R) ? static_cast<int>(mine) : R;
+    const uint32_t s0 = first * kGroupKeys;              // first key of the wave's first group
+    const uint32_t stride = step * (kGroupKeys * 128u);
     // query operand rows (head hb*16 + j16, dims [32g, 32g+32)) and the
     // weights of the heads this lane sums (hb*16 + 4g + r),
     // loaded before the keys so that waiting for them never waits for a key group
@@ -216,8 +225,8 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     }
     const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * 128u + g * 32u;
     uint4 ka[4][2], kb[4][2];
-    load_group_fp8(rs, voff0, 0, ng, ka);
-    load_group_fp8(rs, voff0, 1, ng, kb);
+    load_group_fp8(rs, voff0, stride, 0, ng, ka);
+    load_group_fp8(rs, voff0, stride, 1, ng, kb);
     __builtin_amdgcn_sched_barrier(0);     // keep this issue order
     bf16x8 qb[NHB][4];
     float wr[NHB][4];
@@ -235,20 +244,19 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     const uint32_t out_off = g == 0 ? static_cast<uint32_t>(s0 + j16) * 4u : 0x80000000u;
     f32x4 cp[NHB];
     for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    int done = 0;
-    const int live = 4 * ng;
-    // groups in pairs, both always processed (a group past the run holds
-    // zeros and keeps no score)
+    int pend = -1;
+    const int out_stride = static_cast<int>(step * kGroupKeys * 4u);
+    // groups in pairs, both always processed (a group past the wave's share
+    // holds zeros and keeps no score)
     for (int t = 0; t < ng; t += 2) {
-      group_fp8<NHB>(ka, qb, wr, cp, done, live, out_rs, out_off);
-      load_group_fp8(rs, voff0, t + 2, ng, ka);
-      group_fp8<NHB>(kb, qb, wr, cp, done, live, out_rs, out_off);
-      load_group_fp8(rs, voff0, t + 3, ng, kb);
+      group_fp8<NHB>(ka, qb, wr, cp, pend, t * out_stride, out_rs, out_off);
+      load_group_fp8(rs, voff0, stride, t + 2, ng, ka);
+      group_fp8<NHB>(kb, qb, wr, cp, pend, t + 1 < ng ? (t + 1) * out_stride : -1, out_rs, out_off);
+      load_group_fp8(rs, voff0, stride, t + 3, ng, kb);
     }
     const float tot = head_sum<NHB>(cp, wr);
-    if (done <= live)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
-                                            (done - 1) * 64, 0);
+    if (pend >= 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off), pend, 0);
   }
 }
 
@@ -371,12 +379,24 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
     const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
     const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
-    const int r = static_cast<int>(R);
+    const int r = static_cast<int>(R), il = R > 2 ? 1 : 0;
     switch (nhb) {
-      case 1: hipLaunchKernelGGL(indexer_fp8_kernel<1>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
-      case 2: hipLaunchKernelGGL(indexer_fp8_kernel<2>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
-      case 4: hipLaunchKernelGGL(indexer_fp8_kernel<4>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
-      case 8: hipLaunchKernelGGL(indexer_fp8_kernel<8>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); break;
+      case 1:
+        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<1, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        else hipLaunchKernelGGL((indexer_fp8_kernel<1, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        break;
+      case 2:
+        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<2, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        else hipLaunchKernelGGL((indexer_fp8_kernel<2, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        break;
+      case 4:
+        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        else hipLaunchKernelGGL((indexer_fp8_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        break;
+      case 8:
+        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<8, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        else hipLaunchKernelGGL((indexer_fp8_kernel<8, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
+        break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
