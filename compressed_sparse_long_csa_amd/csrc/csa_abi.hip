@@ -190,7 +190,14 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
   if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
   if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "topk_select: null pointer");
   TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};
-  return launched(launch_topk(a, stream), "topk_select");
+  bool capturing = false;
+  const hipError_t e = launch_topk(a, stream, &capturing);
+  if (capturing)
+    return fail(CSA_ERR_UNSUPPORTED,
+                "topk_select: rows longer than 33792 need a %zu-byte device workspace, which "
+                "cannot be allocated during stream capture: make one call of this size first",
+                plan_topk(ld, nq, k).ws_bytes);
+  return launched(e, "topk_select");
 }
 
 static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream) {

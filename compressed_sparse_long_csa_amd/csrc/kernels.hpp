@@ -47,7 +47,12 @@ struct TopkArgs {
   const float* scores; int64_t ld; int nq; const int64_t* n_valid; int k;
   int32_t* idx; float* top_scores;
 };
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+// Long rows (ld > 33792) take two passes through a device workspace: P slices
+// of Cs scores, ws_bytes of candidates (P = 0: one pass, no workspace).
+struct TopkPlan { int P; uint32_t Cs; size_t ws_bytes; };
+TopkPlan plan_topk(int64_t ld, int nq, int k);
+// *capturing is set when the workspace would have to grow during stream capture.
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream, bool* capturing);
 
 // Attention over [selected or all compressed entries] ++ [window rows].
 // The window of query b is `win_count` consecutive rows starting at row

@@ -30,6 +30,8 @@
 // reduction costs one barrier.  The result is the exact set, ascending,
 // whatever the batch or launch.  Loads and stores go through buffer
 // descriptors, so slots past a row's end need neither branches nor clamps.
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace csa {
@@ -204,18 +206,31 @@ struct Row {
   }
 };
 
+// One selection: the k best of n scores.  `out_len` entries are written to
+// idx (the selected, ascending, then -1) and, when `top` is set, to top (their
+// scores, then -inf).  An element's output index is map[position] when map is
+// set, else base + position.
+struct RowIO {
+  const float* scores;
+  uint32_t n;
+  int32_t* idx;
+  float* top;
+  uint32_t out_len;
+  int32_t base;
+  const int32_t* map;
+};
+
 template <bool kStaged>
-__device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n, uint32_t C,
-                                         TopkSmem& sm, float* vals) {
+__device__ __forceinline__ void topk_row(const RowIO& io, uint32_t k, uint32_t C, TopkSmem& sm,
+                                         float* vals) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t k = static_cast<uint32_t>(a.k);
-  const buf_rsrc out_rs = make_rsrc(a.idx + static_cast<int64_t>(row) * a.k, 4u * k);
-  const bool want_s = a.top_scores != nullptr;
-  const buf_rsrc outs_rs =
-      make_rsrc(want_s ? a.top_scores + static_cast<int64_t>(row) * a.k : nullptr, want_s ? 4u * k : 0u);
+  const uint32_t n = io.n;
+  const buf_rsrc out_rs = make_rsrc(io.idx, 4u * io.out_len);
+  const bool want_s = io.top != nullptr;
+  const buf_rsrc outs_rs = make_rsrc(want_s ? io.top : nullptr, want_s ? 4u * io.out_len : 0u);
 
   Row<kStaged> r;
-  r.rs = make_rsrc(a.scores + static_cast<int64_t>(row) * a.ld, 4u * n);
+  r.rs = make_rsrc(io.scores, 4u * n);
   r.n = n;
   r.w0 = static_cast<uint32_t>(wv) * C;
   r.nj = C / 64u;
@@ -419,48 +434,181 @@ __device__ __forceinline__ void topk_row(const TopkArgs& a, int row, uint32_t n,
   });
   const uint32_t total = umin(total_gt + umin(total_eq, need_eq), k);
   __syncthreads();
-  for (uint32_t j = tid; j < k; j += kThreads)
-    __builtin_amdgcn_raw_buffer_store_b32(j < total ? stage[j] : 0xffffffffu, out_rs,
-                                          static_cast<int>(4u * j), 0, 0);
+  for (uint32_t j = tid; j < io.out_len; j += kThreads) {
+    int32_t v = -1;
+    if (j < total) v = io.map != nullptr ? io.map[stage[j]] : io.base + static_cast<int32_t>(stage[j]);
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(v), out_rs, static_cast<int>(4u * j), 0, 0);
+  }
   if (want_s) {
-    for (uint32_t j = total + tid; j < k; j += kThreads)
+    for (uint32_t j = total + tid; j < io.out_len; j += kThreads)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), outs_rs,
                                             static_cast<int>(4u * j), 0, 0);
   }
 }
 
+__device__ __forceinline__ uint32_t row_len(const TopkArgs& a, int row) {
+  int64_t n = a.n_valid ? a.n_valid[row] : a.ld;
+  n = n < 0 ? 0 : (n > a.ld ? a.ld : n);
+  return static_cast<uint32_t>(n);
+}
+
+__device__ __forceinline__ void select_row(const RowIO& io, uint32_t k, uint32_t cap, TopkSmem& sm,
+                                           float* vals) {
+  const uint32_t C = ((io.n + kWaves - 1) / kWaves + 63u) / 64u * 64u;
+  if (kWaves * C <= cap) topk_row<true>(io, k, C, sm, vals);
+  else topk_row<false>(io, k, C, sm, vals);
+}
+
+// One workgroup per row.
 __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, uint32_t cap) {
   __shared__ TopkSmem sm;
   extern __shared__ float vals[];            // cap + kStageSlack scores
   const int row = blockIdx.x;
-  int64_t n = a.n_valid ? a.n_valid[row] : a.ld;
-  n = n < 0 ? 0 : (n > a.ld ? a.ld : n);
-  const uint32_t nn = static_cast<uint32_t>(n);
-  const uint32_t C = ((nn + kWaves - 1) / kWaves + 63u) / 64u * 64u;
-  if (kWaves * C <= cap) topk_row<true>(a, row, nn, C, sm, vals);
-  else topk_row<false>(a, row, nn, C, sm, vals);
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const RowIO io{a.scores + static_cast<int64_t>(row) * a.ld, row_len(a, row),
+                 a.idx + static_cast<int64_t>(row) * a.k,
+                 a.top_scores ? a.top_scores + static_cast<int64_t>(row) * a.k : nullptr, k, 0, nullptr};
+  select_row(io, k, cap, sm, vals);
+}
+
+// Long rows: the row is cut into P slices of Cs scores.  The global top-k of
+// a row lies in the union of its slices' top-k (an entry beaten by fewer than
+// k entries of the row is beaten by fewer than k of its slice, ties to the
+// lower index in both), so the slices' sets are selected first, one
+// workgroup per slice, and written one after another (slice order, then
+// ascending index: the order of the row) into a candidate row of
+// sum_p min(k, |slice p|) entries; a second pass selects from the candidates.
+__device__ __forceinline__ uint32_t cand_before(uint32_t n, uint32_t p, uint32_t Cs, uint32_t k) {
+  const uint32_t full = n / Cs;                       // complete slices (each gives k, Cs >= k)
+  const uint32_t f = p < full ? p : full;
+  uint32_t c = f * k;
+  if (p > full) c += umin(k, n - full * Cs);          // the partial slice
+  return c;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_slice_kernel(TopkArgs a, int P, uint32_t Cs, uint32_t cap,
+                                                              int32_t* cidx, float* cscore) {
+  __shared__ TopkSmem sm;
+  extern __shared__ float vals[];
+  const int row = blockIdx.x / P;
+  const uint32_t p = blockIdx.x % P;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t n = row_len(a, row);
+  const uint32_t s0 = p * Cs;
+  if (s0 >= n) return;                               // uniform over the workgroup
+  const uint32_t ns = umin(Cs, n - s0);
+  const uint32_t off = cand_before(n, p, Cs, k);
+  const int64_t cbase = static_cast<int64_t>(row) * P * k + off;
+  const RowIO io{a.scores + static_cast<int64_t>(row) * a.ld + s0, ns, cidx + cbase, cscore + cbase,
+                 umin(k, ns), static_cast<int32_t>(s0), nullptr};
+  select_row(io, k, cap, sm, vals);
+}
+
+__global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a, int P, uint32_t Cs, uint32_t cap,
+                                                              const int32_t* cidx, const float* cscore) {
+  __shared__ TopkSmem sm;
+  extern __shared__ float vals[];
+  const int row = blockIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t n = row_len(a, row);
+  const int64_t cbase = static_cast<int64_t>(row) * P * k;
+  const RowIO io{cscore + cbase, cand_before(n, static_cast<uint32_t>(P), Cs, k),
+                 a.idx + static_cast<int64_t>(row) * a.k,
+                 a.top_scores ? a.top_scores + static_cast<int64_t>(row) * a.k : nullptr, k, 0, cidx + cbase};
+  select_row(io, k, cap, sm, vals);
 }
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
-  if (a.nq == 0) return hipSuccess;
-  const uint64_t cmax = (static_cast<uint64_t>(a.ld) + kWaves - 1) / kWaves;
+namespace {
+
+// Staged-LDS capacity for rows of up to n scores (0: the row is streamed).
+uint32_t stage_cap(uint64_t n) {
+  const uint64_t cmax = (n + kWaves - 1) / kWaves;
   const uint64_t need = kWaves * ((cmax + 63) / 64 * 64);
-  const uint32_t cap = need <= kStageMax ? static_cast<uint32_t>(need) : 0u;
-  const size_t shm = cap ? (static_cast<size_t>(cap) + kStageSlack) * sizeof(float) : 0;
+  return need <= kStageMax ? static_cast<uint32_t>(need) : 0u;
+}
+size_t stage_bytes(uint32_t cap) { return cap ? (static_cast<size_t>(cap) + kStageSlack) * sizeof(float) : 0; }
+
+// Candidate workspace of the long-row path, one per device, grown on demand
+// and never freed (a captured graph may still use an old one).
+std::mutex g_ws_mu;
+struct Workspace { void* ptr = nullptr; size_t bytes = 0; };
+Workspace g_ws[64];
+
+hipError_t workspace(size_t bytes, hipStream_t stream, void** out, bool* capturing) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &st);
+    if (e != hipSuccess) return e;
+    if (st != hipStreamCaptureStatusNone) { *capturing = true; return hipErrorStreamCaptureUnsupported; }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e;
+    w.ptr = p;
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+TopkPlan plan_topk(int64_t ld, int nq, int k) {
+  TopkPlan pl{};
+  if (static_cast<uint64_t>(ld) <= kStageMax) return pl;         // one workgroup per row, staged
+  // slices of about 16K scores (staged), at most 16K candidates per row
+  const int64_t by_len = (ld + 16383) / 16384;
+  int64_t by_cand = 16384 / k;
+  by_cand = by_cand < 2 ? 2 : by_cand;
+  pl.P = static_cast<int>(by_len < by_cand ? by_len : by_cand);
+  pl.Cs = static_cast<uint32_t>(((ld + pl.P - 1) / pl.P + 63) / 64 * 64);
+  pl.ws_bytes = static_cast<size_t>(nq) * pl.P * k * (sizeof(int32_t) + sizeof(float));
+  return pl;
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream, bool* capturing) {
+  *capturing = false;
+  if (a.nq == 0) return hipSuccess;
   static thread_local int configured_dev = -1;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (configured_dev != dev) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>((kStageMax + kStageSlack) * sizeof(float)));
-    if (e != hipSuccess) return e;
+    const int max_shm = static_cast<int>((kStageMax + kStageSlack) * sizeof(float));
+    for (const void* f : {reinterpret_cast<const void*>(&topk_kernel), reinterpret_cast<const void*>(&topk_slice_kernel),
+                          reinterpret_cast<const void*>(&topk_merge_kernel)}) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_shm);
+      if (e != hipSuccess) return e;
+    }
     configured_dev = dev;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), shm, stream, a, cap);
+  const TopkPlan pl = plan_topk(a.ld, a.nq, a.k);
+  if (pl.P == 0) {
+    const uint32_t cap = stage_cap(static_cast<uint64_t>(a.ld));
+    hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), stage_bytes(cap), stream, a, cap);
+    return hipGetLastError();
+  }
+  void* ws = nullptr;
+  e = workspace(pl.ws_bytes, stream, &ws, capturing);
+  if (e != hipSuccess) return e;
+  const size_t per = static_cast<size_t>(a.nq) * pl.P * a.k;
+  int32_t* cidx = static_cast<int32_t*>(ws);
+  float* cscore = reinterpret_cast<float*>(cidx + per);
+  const uint32_t cap_s = stage_cap(pl.Cs);
+  hipLaunchKernelGGL(topk_slice_kernel, dim3(static_cast<unsigned>(a.nq) * pl.P), dim3(kThreads),
+                     stage_bytes(cap_s), stream, a, pl.P, pl.Cs, cap_s, cidx, cscore);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t cap_m = stage_cap(static_cast<uint64_t>(pl.P) * a.k);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.nq), dim3(kThreads), stage_bytes(cap_m), stream, a, pl.P,
+                     pl.Cs, cap_m, cidx, cscore);
   return hipGetLastError();
 }
 

@@ -214,8 +214,15 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
  * not be NaN.  n_valid is clamped to [0, ld] on the device.
  *
  *   scores  [nq, ld] float32;  idx [nq, k] int32;  top_scores [nq, k] or NULL
+ * Rows longer than 33792 scores (ld > 33792) are selected in two passes
+ * (slices of the row, then a merge of the slices' sets) through a device
+ * workspace of nq * P * k * 8 bytes (P <= 64 slices) that the library keeps
+ * per device, grows on demand and never frees.  Calls with such rows that
+ * overlap on one device (different streams) share it and race.
  * Errors: INVALID_ARG for k < 1, k > 4096, ld < 1, ld > 2^28, nq < 0,
- * null pointers.
+ * null pointers; UNSUPPORTED when the workspace would have to grow while
+ * `stream` is being captured into a graph (make one call of that size
+ * before capturing); HIP when it cannot be allocated.
  */
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
                        int32_t* idx, float* top_scores, hipStream_t stream);

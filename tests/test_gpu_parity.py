@@ -189,6 +189,9 @@ def test_indexer_matches_oracle(fmt, H_I, d_I, lengths):
     (16384, 512, 0, None), (16384, 512, 5, None), (5000, 1024, 0, [5000, 4999, 1024, 1000, 1, 0]),
     (262144, 1024, 0, [262144, 100000]), (3000, 64, 3, [3000, 64, 65, 2]), (70000, 2048, 0, None),
     (33792, 1024, 0, [33792, 33000, 20000]), (34000, 1024, 2, [34000, 33792, 4097]),
+    # rows past 33792 scores: slices + candidate merge
+    (262144, 512, 7, [262144, 262100, 16385, 40000]), (1048576, 512, 0, [1048576, 500000]),
+    (100000, 4096, 0, [100000, 4096, 4095]),
 ])
 def test_topk_exact(ld, k, tie_levels, n_valid):
     nq = len(n_valid) if n_valid else 4
@@ -208,6 +211,34 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
         assert np.all(got[i, c:] == -1)
         assert np.array_equal(gs[i, :c], s[i, want])
         assert np.all(np.isneginf(gs[i, c:]))
+
+
+def test_topk_long_rows_in_a_graph():
+    """The long-row path (slices, then a candidate merge through the library's
+    workspace) captured in a HIP graph: every replay, with eager work in
+    between, gives the eager result."""
+    nq, ld, k = 3, 200000, 1024
+    s, nv = synth.random_scores(77, nq, ld, [200000, 150000, 34000], 0)
+    S, NV = dev(s), dev(nv)
+    eager = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(S, ld, nq, NV, k, eager)           # sizes the workspace outside capture
+    torch.cuda.synchronize()
+    out = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        csa.topk_select(S, ld, nq, NV, k, out, check=False)
+    for _ in range(3):
+        out.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        other = torch.empty_like(eager)
+        csa.topk_select(S, ld, nq, NV, k, other)       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    for i in range(nq):
+        want = OM.top_k(s[i, : nv[i]].astype(np.float64), k)
+        assert np.array_equal(eager.cpu().numpy()[i, : len(want)], want)
 
 
 @pytest.mark.parametrize("ld", [20000, 40000])
