@@ -32,6 +32,7 @@ import json
 import os
 import sys
 import time
+import types
 
 import numpy as np
 import torch
@@ -71,21 +72,49 @@ def build_workload(cfg_id=2, B=None, L=None, seed=2):
         key_tok=dev(key_tok).to(torch.bfloat16), key_gate=dev(key_gate),
         win_tok=dev(win_tok).to(torch.bfloat16), win_gate=dev(win_gate),
     )
-    n_ent = torch.from_numpy(inp.n_ent)
-    last = torch.from_numpy(inp.kv_off) + n_ent - 1
-    seg_off = torch.arange(0, Bn + 1, dtype=torch.int64) * m
-    W["seg_off"] = seg_off.cuda()
+    _step_state(W, inp, Bn, m)
+    return W
+
+
+def build_device_workload(L, B=16, seed=7):
+    """The same CSA decode step at context L (B sequences), drawn on the
+    device (seeded), for the context scan."""
+    c = synth.CONFIGS[2]
+    m, D, R, d_I = c["m"], c["D"], c["R"], c["d_I"]
+    d = synth.device_decode_inputs(seed, [L] * B, m=m, H=c["H"], D=D, R=R, n_win=128, csa=True,
+                                   k=c["k"], H_I=c["H_I"], d_I=d_I)
+    inp = types.SimpleNamespace(n_win=d["n_win"], scale=d["scale"], n_ent=d["n_ent"],
+                                win_len=d["win_len"], kv_off=d["kv_off"], q_pos=d["q_pos"])
+    gen = synth.device_generator(seed + 1000)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)  # noqa: E731
+    W = dict(c=c, inp=inp, B=B, m=m, D=D, R=R, d_I=d_I, q=d["q"],
+             q_pos=torch.as_tensor(d["q_pos"], device="cuda"), kv=d["kv"],
+             kv_off=torch.as_tensor(d["kv_off"], device="cuda"), win=d["win"],
+             win_len=torch.as_tensor(d["win_len"], device="cuda"), sinks=d["sinks"], keys=d["keys"],
+             q_idx=d["q_idx"], w=d["w"],
+             kv_tok=rnd(B * m, D).to(torch.bfloat16), kv_gate=rnd(B * m, 1),
+             key_tok=rnd(B * m, d_I).to(torch.bfloat16), key_gate=rnd(B * m, 1),
+             win_tok=rnd(B, D).to(torch.bfloat16), win_gate=torch.zeros((B, 1), device="cuda"))
+    _step_state(W, inp, B, m)
+    return W
+
+
+def _step_state(W, inp, Bn, m):
+    """Segments of the step's compress jobs, and the scratch / output tensors."""
+    n_ent = torch.from_numpy(np.asarray(inp.n_ent))
+    last = torch.from_numpy(np.asarray(inp.kv_off)) + n_ent - 1
+    W["seg_off"] = (torch.arange(0, Bn + 1, dtype=torch.int64) * m).cuda()
     W["seg_pos0"] = ((n_ent - 1) * m).cuda()                # first token of the newest block
     W["seg_row"] = last.cuda()
     W["win_seg_off"] = torch.arange(0, Bn + 1, dtype=torch.int64).cuda()
-    W["win_pos0"] = torch.from_numpy(inp.q_pos).cuda()
-    W["win_row"] = (torch.arange(Bn, dtype=torch.int64) * inp.n_win + (torch.from_numpy(inp.win_len).long() - 1)).cuda()
+    W["win_pos0"] = torch.from_numpy(np.asarray(inp.q_pos)).cuda()
+    W["win_row"] = (torch.arange(Bn, dtype=torch.int64) * inp.n_win
+                    + (torch.from_numpy(np.asarray(inp.win_len)).long() - 1)).cuda()
     W["n_valid"] = n_ent.cuda()
-    W["ld"] = int(inp.n_ent.max())
+    W["ld"] = int(np.asarray(inp.n_ent).max())
     W["scores"] = torch.empty((Bn, W["ld"]), dtype=torch.float32, device="cuda")
-    W["idx"] = torch.empty((Bn, c["k"]), dtype=torch.int32, device="cuda")
-    W["out"] = torch.empty((Bn, c["H"], D), dtype=torch.bfloat16, device="cuda")
-    return W
+    W["idx"] = torch.empty((Bn, W["c"]["k"]), dtype=torch.int32, device="cuda")
+    W["out"] = torch.empty((Bn, W["c"]["H"], W["D"]), dtype=torch.bfloat16, device="cuda")
 
 
 def make_replicas(W, R):
@@ -337,6 +366,36 @@ def traffic_record(kernel):
         return None
 
 
+def context_scan(contexts, steps, warmup):
+    """The same decode step (B = 16) at longer contexts, the state replicated
+    as for the headline line so that every step reads HBM.  Per context: ms
+    per step, query-tokens/s, each kernel's device time and the indexer's HBM
+    fraction."""
+    rows = []
+    for L in contexts:
+        W = build_device_workload(L)
+        step_bytes, kbytes = algorithmic_bytes(W)
+        # copies of the state so that the bytes one pass over them reads exceed
+        # twice the 256 MB last-level cache
+        n_rep = max(1, -(-600_000_000 // step_bytes))
+        reps = make_replicas(W, n_rep)
+        made = [make_step(Wr, check=False) for Wr in reps]
+        for st, _ in made:
+            st()
+        torch.cuda.synchronize()
+        ms = time_graph([m[0] for m in made], steps, warmup)
+        per_us, _ = time_kernels([m[1] for m in made], max(20, min(60, steps)))
+        idx_gbps = kbytes["indexer_score"] / (per_us["indexer_score"] * 1e-6) / 1e9
+        rows.append({"context": L, "ms_per_step": ms, "query_tokens_per_s": W["B"] / (ms * 1e-3),
+                     "step_hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
+                     "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
+                     "indexer_gbps": idx_gbps, "indexer_hbm_frac": idx_gbps / HBM_PEAK_GBPS,
+                     "state_replicas": n_rep})
+        del W, reps, made
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +405,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--replicas", type=int, default=13,
                     help="per-layer state copies stepped in turn (1 = one warm cache)")
+    ap.add_argument("--no-context-scan", action="store_true",
+                    help="skip the same step at 256K and 1M contexts")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -408,6 +469,8 @@ def main():
         "event_pair_floor_us": event_floor_us,
         "check_max_err_over_rms": err,
     }
+    if not args.no_context_scan:
+        line["context_scan"] = context_scan([262144, 1048576], args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
     print(json.dumps(line), flush=True)
