@@ -288,6 +288,20 @@ def copy_probe(mb, reps):
     print(json.dumps({"copy_probe_read_bytes_per_launch": n * 4, "launches": reps}), flush=True)
 
 
+def copy_gbps(mb=512, reps=20):
+    """Read + write bandwidth of torch's elementwise copy of mb MiB (two
+    buffers used in turn, each larger than the last-level cache): the rate a
+    plain streaming kernel reaches on this part, for comparison."""
+    n = mb * 1024 * 1024 // 4
+    xs = [torch.ones(n, device="cuda") for _ in range(2)]
+    y = torch.empty_like(xs[0])
+    fs = [lambda x=x: torch.mul(x, 1.0, out=y) for x in xs]
+    fs[0]()
+    torch.cuda.synchronize()
+    us = _event_pairs(fs, reps) - _event_pairs([lambda: None], reps)
+    return 2 * n * 4 / (us * 1e-6) / 1e9
+
+
 def spot_check(W):
     """Compare the step's attention output for one sequence with the oracle."""
     from oracle import formats as OF
@@ -467,6 +481,7 @@ def main():
                      "kernel": dom, "bytes_per_launch": kbytes[dom], "us_per_launch": per_us[dom]},
         "kernels": kern,
         "event_pair_floor_us": event_floor_us,
+        "copy_probe_gbps": copy_gbps(),
         "check_max_err_over_rms": err,
     }
     if not args.no_context_scan:
