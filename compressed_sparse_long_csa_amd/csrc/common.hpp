@@ -106,6 +106,13 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Load of a value the whole wave reads at one address, through the scalar
+// data cache (constant address space: the kernel never writes it).
+__device__ __forceinline__ int64_t scalar_load(const int64_t* p, int64_t i) {
+  typedef const __attribute__((address_space(4))) int64_t c64;
+  return ((c64*)(p))[i];
+}
+
 // ------------------------------------------------------------------ wave reductions
 // Butterfly over the 64 lanes; the order of operations is fixed by the lane
 // pattern, so every lane ends with the same bits on every run.

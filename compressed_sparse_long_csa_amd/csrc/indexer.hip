@@ -194,7 +194,22 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     // query i; item `chunk` holds four of the query's waves
     const int i = static_cast<int>(item / n_chunk);
     const int64_t chunk = item % n_chunk;
-    const int64_t qpos = a.q_pos[i], koff = a.key_off[i];
+    // query operand rows (head hb*16 + j16, dims [32g, 32g+32)) and the
+    // weights of the heads this lane sums (hb*16 + 4g + r): their addresses
+    // depend on i only, so they go out first, in the same round trip as the
+    // query's position and key offset (and before the keys, so that waiting
+    // for them never waits for a key group)
+    uint4 qraw[NHB][2];
+    float4 wraw[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
+      qraw[hb][0] = qp[0];
+      qraw[hb][1] = qp[1];
+      wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+    }
+    const int64_t qpos = scalar_load(a.q_pos, i), koff = scalar_load(a.key_off, i);
+    asm volatile("" : : "s"(qpos), "s"(koff) : "memory");   // one round trip; the loads above stay above
     int64_t N = (uniform64(qpos) + 1) / a.m;
     if (N > a.ld) N = a.ld;
     // (N <= 2^24, so group counts fit 32 bits)
@@ -211,23 +226,17 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     const int ng = mine < static_cast<uint32_t>(R) ? static_cast<int>(mine) : R;
     const uint32_t s0 = first * kGroupKeys;              // first key of the wave's first group
     const uint32_t stride = step * (kGroupKeys * 128u);
-    // query operand rows (head hb*16 + j16, dims [32g, 32g+32)) and the
-    // weights of the heads this lane sums (hb*16 + 4g + r),
-    // loaded before the keys so that waiting for them never waits for a key group
-    uint4 qraw[NHB][2];
-    float4 wraw[NHB];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
-      qraw[hb][0] = qp[0];
-      qraw[hb][1] = qp[1];
-      wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
-    }
     const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * 128u + g * 32u;
     uint4 ka[4][2], kb[4][2];
     load_group_fp8(rs, voff0, stride, 0, ng, ka);
     load_group_fp8(rs, voff0, stride, 1, ng, kb);
-    __builtin_amdgcn_sched_barrier(0);     // keep this issue order
+    // the query is used only from here on: its conversion must not be
+    // scheduled above the key loads (it would wait for the query first)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      asm volatile("" : "+v"(qraw[hb][0].x), "+v"(qraw[hb][0].y), "+v"(qraw[hb][0].z), "+v"(qraw[hb][0].w),
+                   "+v"(qraw[hb][1].x), "+v"(qraw[hb][1].y), "+v"(qraw[hb][1].z), "+v"(qraw[hb][1].w),
+                   "+v"(wraw[hb].x), "+v"(wraw[hb].y), "+v"(wraw[hb].z), "+v"(wraw[hb].w) : : "memory");
     bf16x8 qb[NHB][4];
     float wr[NHB][4];
 #pragma unroll
