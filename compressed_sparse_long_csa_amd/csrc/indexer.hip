@@ -30,11 +30,6 @@ namespace csa {
 
 namespace {
 
-constexpr int kBatch = 8;                        // 16-key blocks of one wave, loaded together
-constexpr int kKeysPerWave = 16 * kBatch;        // 128 keys, one query load
-constexpr int kWaves = 4;
-constexpr int kKeysPerWg = kKeysPerWave * kWaves;
-
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   bf16x8 r;
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -55,40 +50,11 @@ __device__ __forceinline__ float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Work item: (query i, chunk of kKeysPerWg keys); wave wv takes keys
-// [chunk * kKeysPerWg + wv * kKeysPerWave, +kKeysPerWave).  The MFMA output
-// is heads x keys: lane (key j16, heads 4g .. 4g+3 of each 16-head block), so
-// a lane sums its 16 heads (blocks in order, then rows r) and the four row
-// groups are added once.  Key rows are read through a buffer descriptor over
-// the query's N visible rows: rows past N read as zero, and a row address is
-// a 32-bit offset with the block step in the scalar offset.
-struct IdxItem {
-  int i;
-  int64_t N, s0;
-  int nb;                          // 16-key blocks of this wave with keys < N
-  buf_rsrc rs;                     // the query's visible key rows
-};
-
-__device__ __forceinline__ bool idx_item(const IndexerArgs& a, int64_t item, int64_t n_chunk,
-                                         int wv, int row_bytes, IdxItem* it) {
-  it->i = static_cast<int>(item / n_chunk);
-  const int64_t chunk = item % n_chunk;
-  // per-query values are wave-uniform: keep them (and the descriptor) in
-  // scalar registers, so buffer loads need no per-lane descriptor check.
-  // Both are read in one round trip.
-  const int64_t qpos = a.q_pos[it->i], koff = a.key_off[it->i];
-  int64_t N = (uniform64(qpos) + 1) / a.m;
-  if (N > a.ld) N = a.ld;
-  it->N = N;
-  it->s0 = chunk * kKeysPerWg + wv * kKeysPerWave;
-  it->rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * row_bytes,
-                     static_cast<uint32_t>(N * row_bytes));
-  if (it->s0 >= N) return false;                      // uniform over the wave (no barriers)
-  const int64_t left = (N - it->s0 + 15) / 16;
-  it->nb = left < kBatch ? static_cast<int>(left) : kBatch;
-  return true;
-}
-
+// The MFMA output is heads x keys: lane (key j16, heads 4g .. 4g+3 of each
+// 16-head block), so a lane sums its 16 heads and the four row groups are
+// added once.  Key rows are read through a buffer descriptor over the
+// query's N visible rows: rows past N read as zero, and a row address is a
+// 32-bit offset with the block step in the scalar offset.
 __device__ __forceinline__ uint4 buf_load_x4(buf_rsrc r, uint32_t voff, uint32_t soff) {
   const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
   return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
@@ -114,16 +80,6 @@ __device__ __forceinline__ float head_sum(const f32x4 (&c)[NHB], const float (&w
 #pragma unroll
     for (int hb = 0; hb + w < NHB; hb += 2 * w) s[hb] += s[hb + w];
   return rows_sum(s[0]);
-}
-
-// Score stores: a descriptor over the query's N valid scores drops stores
-// past N; lanes other than row group 0 (which hold the same totals) aim past
-// every valid range.
-__device__ __forceinline__ buf_rsrc score_rsrc(const IndexerArgs& a, const IdxItem& it) {
-  return make_rsrc(a.scores + static_cast<int64_t>(it.i) * a.ld, static_cast<uint32_t>(it.N * 4));
-}
-__device__ __forceinline__ uint32_t score_voff(const IdxItem& it, int g, int j16) {
-  return g == 0 ? static_cast<uint32_t>(it.s0 + j16) * 4u : 0x80000000u;
 }
 
 // --------------------------------------------------------------- FP8, d = 128
@@ -272,69 +228,114 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
 // --------------------------------------------------------------- MXFP4, d = 128
 // Row: 64 bytes of E2M1 codes then 4 E8M0 scales.  Scaled MFMA 16x16x128:
 // lane (row j16, k-block g) supplies 16 code bytes and the scale of block g.
+// Shares of 64-key groups as in the FP8 kernel.
+constexpr uint32_t kRowFp4 = 68;
+
+// voff0: start of the lane's key row; lane takes code bytes [16g, 16g+16) and
+// the scale byte 64 + g of each row
+__device__ __forceinline__ void load_group_fp4(buf_rsrc rs, uint32_t voff0, uint32_t g, uint32_t stride, int t,
+                                               int ng, uint4 (&kc)[4], uint32_t (&ks)[4]) {
+  const uint32_t base = t < ng ? voff0 + static_cast<uint32_t>(t) * stride : 0x80000000u;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    kc[kb] = buf_load_x4(rs, base + 16u * g, kb * 16u * kRowFp4);
+    ks[kb] = __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>(base + 64u + g),
+                                                 static_cast<int>(kb * 16u * kRowFp4), 0);
+  }
+}
+
 template <int NHB>
+__device__ __forceinline__ void group_fp4(const uint4 (&kc)[4], const uint32_t (&ks)[4], const i32x8 (&qop)[NHB],
+                                          const int (&qsc)[NHB], const float (&wr)[NHB][4], f32x4 (&cp)[NHB],
+                                          int& pend, int grp, buf_rsrc out_rs, uint32_t out_off) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const i32x8 kop = {static_cast<int>(kc[kb].x), static_cast<int>(kc[kb].y), static_cast<int>(kc[kb].z),
+                       static_cast<int>(kc[kb].w), 0, 0, 0, 0};
+    f32x4 cc[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      cc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          qop[hb], kop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, qsc[hb], 0, static_cast<int>(ks[kb]));
+    const float tot = head_sum<NHB>(cp, wr);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs,
+                                          static_cast<int>(pend >= 0 ? out_off : 0x80000000u),
+                                          pend >= 0 ? pend : 0, 0);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
+    pend = grp >= 0 ? grp + kb * 64 : -1;
+  }
+}
+
+template <int NHB, bool IL>
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64_t n_items,
-                                                            int64_t n_chunk) {
+                                                            int64_t n_chunk, int R) {
   constexpr int H = NHB * 16;
-  constexpr int RB = 68;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    IdxItem it;
-    if (!idx_item(a, item, n_chunk, wv, RB, &it)) continue;
-    const int i = it.i;
-    // query codes, scales and weights first (see the FP8 kernel)
+    const int i = static_cast<int>(item / n_chunk);
+    const int64_t chunk = item % n_chunk;
+    // query codes, scales and weights first, with the position and key offset
+    // (see the FP8 kernel)
     i32x8 qop[NHB];
     int qsc[NHB];
     float4 wraw[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
-      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * RB;
+      const uint8_t* row = qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * kRowFp4;
       const uint4 c4 = *reinterpret_cast<const uint4*>(row + g * 16);
       qop[hb] = i32x8{static_cast<int>(c4.x), static_cast<int>(c4.y), static_cast<int>(c4.z),
                       static_cast<int>(c4.w), 0, 0, 0, 0};
       qsc[hb] = row[64 + g];
       wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
     }
-    const uint32_t voff = static_cast<uint32_t>(it.s0 + j16) * RB;
-    uint4 kc[kBatch];
-    uint32_t ksc[kBatch];
+    const int64_t qpos = scalar_load(a.q_pos, i), koff = scalar_load(a.key_off, i);
+    asm volatile("" : : "s"(qpos), "s"(koff) : "memory");   // one round trip; the loads above stay above
+    int64_t N = (uniform64(qpos) + 1) / a.m;
+    if (N > a.ld) N = a.ld;
+    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;
+    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);
+    const uint32_t G = static_cast<uint32_t>((N + kGroupKeys - 1) / kGroupKeys);
+    const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * kRowFp4,
+                                  static_cast<uint32_t>(N * kRowFp4));
+    const uint32_t first = IL ? wq : wq * static_cast<uint32_t>(R);
+    const uint32_t step = IL ? W : 1u;
+    if (first >= G) continue;                            // uniform over the wave (no barriers)
+    const uint32_t mine = (G - first + step - 1u) / step;
+    const int ng = mine < static_cast<uint32_t>(R) ? static_cast<int>(mine) : R;
+    const uint32_t s0 = first * kGroupKeys;
+    const uint32_t stride = step * (kGroupKeys * kRowFp4);
+    const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * kRowFp4;
+    uint4 kca[4], kcb[4];
+    uint32_t ksa[4], ksb[4];
+    load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, 0, ng, kca, ksa);
+    load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, 1, ng, kcb, ksb);
 #pragma unroll
-    for (int kb = 0; kb < kBatch; ++kb) {
-      kc[kb] = buf_load_x4(it.rs, voff + g * 16u, kb * 16u * RB);
-      ksc[kb] = __builtin_amdgcn_raw_buffer_load_b8(it.rs, static_cast<int>(voff + 64u + g),
-                                                    static_cast<int>(kb * 16u * RB), 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);     // keep this issue order
+    for (int hb = 0; hb < NHB; ++hb)
+      asm volatile("" : "+v"(wraw[hb].x), "+v"(wraw[hb].y), "+v"(wraw[hb].z), "+v"(wraw[hb].w) : : "memory");
     float wr[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
     }
-    const buf_rsrc out_rs = score_rsrc(a, it);
-    const uint32_t out_off = score_voff(it, g, j16);
+    const buf_rsrc out_rs = make_rsrc(a.scores + static_cast<int64_t>(i) * a.ld, static_cast<uint32_t>(N * 4));
+    const uint32_t out_off = g == 0 ? static_cast<uint32_t>(s0 + j16) * 4u : 0x80000000u;
     f32x4 cp[NHB];
-#pragma unroll
-    for (int kb = 0; kb <= kBatch; ++kb) {
-      f32x4 cc[NHB];
-      if (kb < kBatch) {
-        const i32x8 kop = {static_cast<int>(kc[kb].x), static_cast<int>(kc[kb].y),
-                           static_cast<int>(kc[kb].z), static_cast<int>(kc[kb].w), 0, 0, 0, 0};
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-          cc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qop[hb], kop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, qsc[hb], 0, static_cast<int>(ksc[kb]));
-      }
-      if (kb > 0) {
-        const float tot = head_sum<NHB>(cp, wr);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off),
-                                              (kb - 1) * 64, 0);
-      }
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
+    for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int pend = -1;
+    const int out_stride = static_cast<int>(step * kGroupKeys * 4u);
+    for (int t = 0; t < ng; t += 2) {
+      group_fp4<NHB>(kca, ksa, qop, qsc, wr, cp, pend, t * out_stride, out_rs, out_off);
+      load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, t + 2, ng, kca, ksa);
+      group_fp4<NHB>(kcb, ksb, qop, qsc, wr, cp, pend, t + 1 < ng ? (t + 1) * out_stride : -1, out_rs, out_off);
+      load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, t + 3, ng, kcb, ksb);
     }
+    const float tot = head_sum<NHB>(cp, wr);
+    if (pend >= 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off), pend, 0);
   }
 }
 
@@ -377,45 +378,32 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
   }
   const int nhb = a.H / 16;
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-  if (a.fmt == CSA_FP8) {
-    // run length: enough 64-key groups per wave that one round of two waves
-    // per SIMD covers the batch, at least 2 (two groups in flight), at most 32
-    const int64_t groups = static_cast<int64_t>(a.nq) * ((a.ld + kGroupKeys - 1) / kGroupKeys);
-    const int64_t waves = static_cast<int64_t>(device_cu_count()) * 8;
-    int64_t R = (groups + waves - 1) / waves;
-    R = R < 2 ? 2 : (R > 32 ? 32 : R);
-    const int64_t item_keys = 4 * R * kGroupKeys;
-    const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
-    const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
-    const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
-    const int r = static_cast<int>(R), il = R > 2 ? 1 : 0;
-    switch (nhb) {
-      case 1:
-        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<1, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        else hipLaunchKernelGGL((indexer_fp8_kernel<1, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        break;
-      case 2:
-        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<2, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        else hipLaunchKernelGGL((indexer_fp8_kernel<2, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        break;
-      case 4:
-        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        else hipLaunchKernelGGL((indexer_fp8_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        break;
-      case 8:
-        if (il) hipLaunchKernelGGL((indexer_fp8_kernel<8, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        else hipLaunchKernelGGL((indexer_fp8_kernel<8, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);
-        break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  const int64_t n_chunk = (a.ld + kKeysPerWg - 1) / kKeysPerWg;
+  // share length: enough 64-key groups per wave that one round of two waves
+  // per SIMD covers the batch, at least 2 (two groups in flight), at most 32
+  const int64_t groups = static_cast<int64_t>(a.nq) * ((a.ld + kGroupKeys - 1) / kGroupKeys);
+  const int64_t waves = static_cast<int64_t>(device_cu_count()) * 8;
+  int64_t R = (groups + waves - 1) / waves;
+  R = R < 2 ? 2 : (R > 32 ? 32 : R);
+  const int64_t item_keys = 4 * R * kGroupKeys;
+  const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
   const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
   const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
-#define CSA_IDX_CASE(K, NB) \
-  case NB: hipLaunchKernelGGL(K<NB>, dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk); break;
-  {
+  const int r = static_cast<int>(R);
+  const bool il = R > 2;
+#define CSA_IDX_CASE(K, NB)                                                                              \
+  case NB:                                                                                               \
+    if (il) hipLaunchKernelGGL((K<NB, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);   \
+    else hipLaunchKernelGGL((K<NB, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);     \
+    break;
+  if (a.fmt == CSA_FP8) {
+    switch (nhb) {
+      CSA_IDX_CASE(indexer_fp8_kernel, 1)
+      CSA_IDX_CASE(indexer_fp8_kernel, 2)
+      CSA_IDX_CASE(indexer_fp8_kernel, 4)
+      CSA_IDX_CASE(indexer_fp8_kernel, 8)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
     switch (nhb) {
       CSA_IDX_CASE(indexer_mxfp4_kernel, 1)
       CSA_IDX_CASE(indexer_mxfp4_kernel, 2)

@@ -184,6 +184,35 @@ def test_indexer_matches_oracle(fmt, H_I, d_I, lengths):
         assert np.all(got[b, N:] == -7.0), "scores past N must stay untouched"
 
 
+@pytest.mark.parametrize("fmt", [csa.FP8, csa.MXFP4])
+def test_indexer_long_contexts(fmt):
+    """Long rows, where each wave streams a share of several 64-key groups and
+    (FP8) the waves of a query take its groups in turn: every score of three
+    ragged rows against the oracle."""
+    lengths = [1048576, 600001, 4097]
+    m, H_I, d_I = 4, 64, 128
+    gen = synth.device_generator(23)
+    n_ent = np.asarray(lengths) // m
+    kv_off = np.concatenate([[0], np.cumsum(n_ent)[:-1]]).astype(np.int64)
+    keys = synth.device_rows(gen, int(n_ent.sum()), d_I, fmt)
+    B = len(lengths)
+    q_idx = synth.device_rows(gen, B * H_I, d_I, fmt).reshape(B, H_I, -1)
+    w = torch.rand((B, H_I), generator=gen, device=DEV, dtype=torch.float32)
+    ld = int(n_ent.max())
+    scores = torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(q_idx, w, B, H_I, d_I, keys, fmt, torch.as_tensor(kv_off, device=DEV),
+                      torch.as_tensor(np.asarray(lengths) - 1, device=DEV), m, scores, ld)
+    got = scores.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        N = int(n_ent[b])
+        kb = OF.decode_rows(keys[kv_off[b]: kv_off[b] + N].cpu().numpy(), fmt, d_I)
+        ref = OM.indexer_scores(OF.decode_rows(q_idx[b].cpu().numpy(), fmt, d_I),
+                                w[b].cpu().numpy().astype(np.float64), kb)
+        err = np.abs(got[b, :N] - ref).max() / max(1.0, np.abs(ref).max())
+        assert err <= 1e-5, f"row {b}: relative score error {err:.3g}"
+        assert np.all(got[b, N:] == -7.0), "scores past N must stay untouched"
+
+
 # ------------------------------------------------------------------ top-k
 @pytest.mark.parametrize("ld,k,tie_levels,n_valid", [
     (16384, 512, 0, None), (16384, 512, 5, None), (5000, 1024, 0, [5000, 4999, 1024, 1000, 1, 0]),
