@@ -49,9 +49,12 @@ BF16_PEAK_TFLOPS = 2500.0
 EPS, BASE = 1e-6, 10000.0
 
 
-def build_workload(cfg_id=2, B=None, L=None, seed=2):
-    c = synth.CONFIGS[cfg_id]
-    inp = synth.config_decode_inputs(cfg_id, seed=seed, B=B, L=L)
+WORKLOAD = "csa_decode_b16_ctx65536"
+
+
+def build_workload(name=WORKLOAD, B=None, L=None, seed=2):
+    c = synth.WORKLOADS[name]
+    inp = synth.workload_decode_inputs(name, seed=seed, B=B, L=L)
     m, D, R, d_I = c["m"], c["D"], c["R"], c["d_I"]
     rng = synth.rng_for(seed + 1000)
     Bn = inp.B
@@ -79,7 +82,7 @@ def build_workload(cfg_id=2, B=None, L=None, seed=2):
 def build_device_workload(L, B=16, seed=7):
     """The same CSA decode step at context L (B sequences), drawn on the
     device (seeded), for the context scan."""
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[WORKLOAD]
     m, D, R, d_I = c["m"], c["D"], c["R"], c["d_I"]
     d = synth.device_decode_inputs(seed, [L] * B, m=m, H=c["H"], D=D, R=R, n_win=128, csa=True,
                                    k=c["k"], H_I=c["H_I"], d_I=d_I)

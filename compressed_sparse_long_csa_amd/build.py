@@ -1,6 +1,6 @@
 """Build libcsa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m compressed_sparse_long_csa_amd.build   (or __graft_entry__.build())
+Usage: python -m compressed_sparse_long_csa_amd.build
 """
 import os
 import subprocess

@@ -6,15 +6,18 @@ normalisation, rotation, scoring, selection or attention.  Storage casts to
 bfloat16 and FP8-E4M3 use torch's dtype conversions (round to nearest even);
 MXFP4 rows are drawn directly as random E2M1 codes and E8M0 scale bytes.
 
-Workload shapes follow the configurations the method is measured on:
-  * cfg1 -- CSA decode, fp32, 1 sequence of 2048 tokens, D=128, 8 heads,
-            indexer 4 x 64, top-k 64, window 128;
-  * cfg2 -- CSA decode, 16 sequences of 65,536 tokens (16,384 entries),
-            D=512 split cache, 64 heads, FP8 indexer 64 x 128, top-k 512;
-  * cfg3 -- HCA decode, 32 sequences of 262,144 tokens, m'=128 (2048 entries);
-  * cfg4 -- CSA prefill chunk: 131,072 cached + 2048 new tokens, top-k 1024;
-  * cfg5 -- ragged CSA (MXFP4 indexer, top-k 1024) + HCA decode, 64
-            sequences with lengths log-uniform in [1024, 1048576].
+Workloads (WORKLOADS, keyed by name):
+  * csa_decode_fp32_b1_ctx2048 -- CSA decode, fp32, 1 sequence of 2048 tokens,
+            D=128, 8 heads, indexer 4 x 64, top-k 64, window 128;
+  * csa_decode_b16_ctx65536 -- CSA decode, 16 sequences of 65,536 tokens
+            (16,384 entries), D=512 split cache, 64 heads, FP8 indexer
+            64 x 128, top-k 512;
+  * hca_decode_b32_ctx262144 -- HCA decode, 32 sequences of 262,144 tokens,
+            m'=128 (2048 entries);
+  * csa_prefill_ctx131072_chunk2048 -- CSA prefill chunk: 131,072 cached +
+            2048 new tokens, top-k 1024;
+  * ragged_csa_hca_b64_ctx1k_1m -- ragged CSA (MXFP4 indexer, top-k 1024) +
+            HCA decode, 64 sequences with lengths log-uniform in [1024, 1048576].
 Hidden values are N(0,1) before quantisation; indexer head weights U(0,1);
 sink logits N(0,1).
 """
@@ -165,29 +168,29 @@ def random_scores(seed, nq, ld, n_valid=None, tie_levels=0, rng=None):
     return s, np.asarray(n_valid, dtype=np.int64)
 
 
-# --------------------------------------------------------------- configs
-CONFIGS = {
-    1: dict(name="csa_decode_fp32_b1_ctx2048", B=1, L=2048, m=4, H=8, D=128, R=64,
+# --------------------------------------------------------------- workloads
+WORKLOADS = {
+    "csa_decode_fp32_b1_ctx2048": dict(seed=1, B=1, L=2048, m=4, H=8, D=128, R=64,
             n_win=128, k=64, H_I=4, d_I=64, kv_fmt=F32, q_fmt=F32, win_fmt=F32,
             idx_fmt=F32, csa=True),
-    2: dict(name="csa_decode_b16_ctx65536", B=16, L=65536, m=4, H=64, D=512, R=64,
+    "csa_decode_b16_ctx65536": dict(seed=2, B=16, L=65536, m=4, H=64, D=512, R=64,
             n_win=128, k=512, H_I=64, d_I=128, kv_fmt=SPLIT, q_fmt=BF16, win_fmt=BF16,
             idx_fmt=FP8, csa=True),
-    3: dict(name="hca_decode_b32_ctx262144", B=32, L=262144, m=128, H=64, D=512, R=64,
+    "hca_decode_b32_ctx262144": dict(seed=3, B=32, L=262144, m=128, H=64, D=512, R=64,
             n_win=128, kv_fmt=SPLIT, q_fmt=BF16, win_fmt=BF16, csa=False),
-    4: dict(name="csa_prefill_ctx131072_chunk2048", cached=131072, chunk=2048, m=4, H=64,
+    "csa_prefill_ctx131072_chunk2048": dict(seed=4, cached=131072, chunk=2048, m=4, H=64,
             D=512, R=64, n_win=128, k=1024, H_I=64, d_I=128, kv_fmt=SPLIT, q_fmt=BF16,
             idx_fmt=FP8),
-    5: dict(name="ragged_csa_hca_b64_ctx1k_1m", B=64, Lmin=1024, Lmax=1048576, m=4, m_hca=128,
+    "ragged_csa_hca_b64_ctx1k_1m": dict(seed=5, B=64, Lmin=1024, Lmax=1048576, m=4, m_hca=128,
             H=64, D=512, R=64, n_win=128, k=1024, H_I=64, d_I=128, kv_fmt=SPLIT,
             q_fmt=BF16, win_fmt=BF16, idx_fmt=MXFP4),
 }
 
 
-def config_decode_inputs(cfg_id, seed=None, B=None, L=None):
-    """Decode inputs for configs 1-3 (optionally with a smaller B or L)."""
-    c = CONFIGS[cfg_id]
-    seed = cfg_id if seed is None else seed
+def workload_decode_inputs(name, seed=None, B=None, L=None):
+    """Decode inputs of a decode workload (optionally with a smaller B or L)."""
+    c = WORKLOADS[name]
+    seed = c["seed"] if seed is None else seed
     B = c["B"] if B is None else B
     L = c["L"] if L is None else L
     lengths = np.full(B, L, dtype=np.int64)

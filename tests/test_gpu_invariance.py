@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _case(cfg, lengths, seed, csa_mode):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     return synth.decode_inputs(seed, lengths, m=c["m"], H=c["H"], D=c["D"], R=c["R"],
                                n_win=c["n_win"], kv_fmt=c["kv_fmt"], q_fmt=c["q_fmt"],
                                win_fmt=c["win_fmt"], csa=csa_mode, k=c.get("k", 512),
@@ -40,12 +40,12 @@ def _attn(inp, bufs, sel_t, rows, variant):
 
 
 @pytest.mark.parametrize("cfg,lengths,csa_mode", [
-    (2, [65536, 9000, 2051, 130, 5, 40000], True),
-    (3, [262144, 40000, 128, 127, 9000], False),
-    (1, [2048, 300, 7], True),
+    ("csa_decode_b16_ctx65536", [65536, 9000, 2051, 130, 5, 40000], True),
+    ("hca_decode_b32_ctx262144", [262144, 40000, 128, 127, 9000], False),
+    ("csa_decode_fp32_b1_ctx2048", [2048, 300, 7], True),
 ])
 def test_attention_bits_independent_of_batch_and_variant(cfg, lengths, csa_mode):
-    inp = _case(cfg, lengths, 70 + cfg, csa_mode)
+    inp = _case(cfg, lengths, 70 + synth.WORKLOADS[cfg]["seed"], csa_mode)
     bufs = upload_decode(inp)
     sel = synth.random_selection(np.random.default_rng(3), inp.n_ent, inp.k) if csa_mode else None
     sel_t = dev(sel) if sel is not None else None
@@ -70,7 +70,7 @@ def test_attention_bits_independent_of_batch_and_variant(cfg, lengths, csa_mode)
 
 
 def test_indexer_and_topk_bits_independent_of_batch():
-    inp = _case(2, [65536, 9000, 2051, 130, 5], 81, True)
+    inp = _case("csa_decode_b16_ctx65536", [65536, 9000, 2051, 130, 5], 81, True)
     bufs = upload_decode(inp)
     B, ld, k = inp.B, int(inp.n_ent.max()), inp.k
 

@@ -299,7 +299,7 @@ def test_topk_edge_rows(case, ld):
 
 # ------------------------------------------------------------------ attention
 def _decode_case(cfg, lengths, seed, csa_mode):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     return synth.decode_inputs(seed, lengths, m=c["m"], H=c["H"], D=c["D"], R=c["R"],
                                n_win=c["n_win"], kv_fmt=c["kv_fmt"], q_fmt=c["q_fmt"],
                                win_fmt=c["win_fmt"], csa=csa_mode, k=c.get("k", 512),
@@ -308,13 +308,13 @@ def _decode_case(cfg, lengths, seed, csa_mode):
 
 
 @pytest.mark.parametrize("cfg,lengths,csa_mode", [
-    (1, [2048, 300, 7], True), (1, [2048], False),
-    (2, [65536, 9000, 2051, 130, 5], True),
-    (3, [262144, 40000, 128, 127], False),
-    (2, [4100, 777], False),
+    ("csa_decode_fp32_b1_ctx2048", [2048, 300, 7], True), ("csa_decode_fp32_b1_ctx2048", [2048], False),
+    ("csa_decode_b16_ctx65536", [65536, 9000, 2051, 130, 5], True),
+    ("hca_decode_b32_ctx262144", [262144, 40000, 128, 127], False),
+    ("csa_decode_b16_ctx65536", [4100, 777], False),
 ])
 def test_attn_decode_matches_oracle(cfg, lengths, csa_mode):
-    inp = _decode_case(cfg, lengths, 40 + cfg, csa_mode)
+    inp = _decode_case(cfg, lengths, 40 + synth.WORKLOADS[cfg]["seed"], csa_mode)
     rng = np.random.default_rng(99)
     sel = synth.random_selection(rng, inp.n_ent, inp.k) if csa_mode else None
     out, _ = run_decode(inp, dev(sel) if sel is not None else None)
@@ -324,6 +324,6 @@ def test_attn_decode_matches_oracle(cfg, lengths, csa_mode):
         s = sel[b][sel[b] >= 0] if sel is not None else None
         ref = oracle_decode_query(inp, b, s)
         if fmt == csa.F32:
-            assert_f32_close(got[b], ref, what=f"cfg{cfg} b{b}")
+            assert_f32_close(got[b], ref, what=f"{cfg} b{b}")
         else:
-            assert_lowp_close(got[b], ref, what=f"cfg{cfg} b{b}")
+            assert_lowp_close(got[b], ref, what=f"{cfg} b{b}")
