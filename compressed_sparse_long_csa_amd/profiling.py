@@ -3,6 +3,10 @@
   python -m compressed_sparse_long_csa_amd.profiling stats RESULTS_DB
       per-kernel launch count and duration (avg / median / min, microseconds)
       from a `rocprofv3 --kernel-trace` database (its `kernels` view).
+      With --split-runs, launches that follow or precede a launch of the same
+      kernel (a loop that launches one kernel again and again, as bench.py's
+      per-kernel timing does) are counted apart from the rest (the graph of
+      the step, where every kernel follows a different one).
 
   python -m compressed_sparse_long_csa_amd.profiling traffic --kernel SUBSTR \\
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-bytes N \\
@@ -25,11 +29,18 @@ import statistics
 import sys
 
 
-def kernel_stats(db):
+def kernel_stats(db, runs=None):
+    """runs=None: every launch; True: only launches next to a launch of the
+    same kernel (in start order); False: only the others."""
     con = sqlite3.connect(db)
-    rows = con.execute("select name, duration from kernels").fetchall()
+    rows = con.execute("select name, duration from kernels order by start").fetchall()
     d = collections.defaultdict(list)
-    for name, dur in rows:
+    for i, (name, dur) in enumerate(rows):
+        if runs is not None:
+            in_run = ((i > 0 and rows[i - 1][0] == name)
+                      or (i + 1 < len(rows) and rows[i + 1][0] == name))
+            if in_run != runs:
+                continue
         d[name].append(dur / 1000.0)
     tot = sum(sum(v) for v in d.values()) or 1.0
     out = []
@@ -55,6 +66,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("db")
+    s.add_argument("--split-runs", action="store_true")
     t = sub.add_parser("traffic")
     for a in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--source", "--out"):
         t.add_argument(a, required=True)
@@ -62,10 +74,15 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy launch")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
-        print(f"{'kernel':90s} {'launches':>8s} {'avg_us':>9s} {'median':>9s} {'min':>9s} {'share':>6s}")
-        for r in kernel_stats(args.db):
-            print(f"{r['kernel'][:90]:90s} {r['launches']:8d} {r['avg_us']:9.2f} {r['median_us']:9.2f} "
-                  f"{r['min_us']:9.2f} {100 * r['share']:5.1f}%")
+        parts = ([("launches next to a launch of the same kernel", True),
+                  ("all other launches", False)] if args.split_runs else [(None, None)])
+        for title, runs in parts:
+            if title:
+                print(f"# {title}")
+            print(f"{'kernel':90s} {'launches':>8s} {'avg_us':>9s} {'median':>9s} {'min':>9s} {'share':>6s}")
+            for r in kernel_stats(args.db, runs):
+                print(f"{r['kernel'][:90]:90s} {r['launches']:8d} {r['avg_us']:9.2f} {r['median_us']:9.2f} "
+                      f"{r['min_us']:9.2f} {100 * r['share']:5.1f}%")
         return
     f_kib, nf = counter_per_dispatch(args.fetch, args.kernel, "FETCH_SIZE")
     w_kib, nw = counter_per_dispatch(args.write, args.kernel, "WRITE_SIZE")
