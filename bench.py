@@ -23,8 +23,11 @@ Prints one JSON line.  `roofline` is measured for the dominant kernel
 (indexer_score, which moves most of the step's bytes) with events around its
 launches on its stream; `kernels` gives every kernel's duration, algorithmic
 bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
-float64 oracle on a bounded sample on the host.  `--copy-probe MIB` only runs
-a plain copy of known size, the reference for rocprofv3 byte counters.
+float64 oracle on a bounded sample on the host.  `context_scan` repeats the
+step at 256K and 1M tokens per sequence; `prefill` times the CSA prefill
+chunk (2,048 tokens after 131,072 cached: compress, indexer, top-k 1,024,
+prefill attention) and the contractions' MFMA rates.  `--copy-probe MIB` only
+runs a plain copy of known size, the reference for rocprofv3 byte counters.
 """
 import argparse
 import hashlib
@@ -413,6 +416,94 @@ def context_scan(contexts, steps, warmup):
     return rows
 
 
+PREFILL = "csa_prefill_ctx131072_chunk2048"
+
+
+def prefill_leg(reps=10):
+    """The CSA prefill workload: a chunk of 2,048 tokens after 131,072 cached,
+    on inputs drawn on the device (seeded).  One pass = csa_compress_batch
+    (the chunk's 512 KV entries, 512 index keys and 2,048 per-token window
+    rows) + indexer_score (2,048 x 33,280 scores) + topk_select (k = 1,024)
+    + hybrid_attn_prefill.  Reports each kernel's device time (events around
+    single launches, less an empty pair), the pass time, and the two
+    contractions' matrix FLOP rates against the BF16 MFMA peak.  Parity of
+    this path is covered by the GPU tests, not re-checked here."""
+    c = synth.WORKLOADS[PREFILL]
+    cached, chunk, H, m, k = c["cached"], c["chunk"], c["H"], c["m"], c["k"]
+    D, R, d_I, H_I, n_win = c["D"], c["R"], c["d_I"], c["H_I"], c["n_win"]
+    gen = synth.device_generator(c["seed"] + 2000)
+    cuda = "cuda"
+    T = cached + chunk
+    n_tot = T // m
+    kv = synth.device_rows(gen, n_tot, D, csa.SPLIT, R)
+    keys = synth.device_rows(gen, n_tot, d_I, csa.FP8)
+    tok_pos0 = cached - n_win + 1
+    tok = synth.device_rows(gen, T - tok_pos0, D, csa.BF16)
+    q = synth.device_rows(gen, chunk * H, D, csa.BF16).reshape(chunk, H, -1)
+    q_idx = synth.device_rows(gen, chunk * H_I, d_I, csa.FP8).reshape(chunk, H_I, -1)
+    w = torch.rand((chunk, H_I), generator=gen, device=cuda, dtype=torch.float32)
+    sinks = torch.randn(H, generator=gen, device=cuda, dtype=torch.float32)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=cuda, dtype=torch.float32)  # noqa: E731
+    kv_tok, kv_gate = rnd(chunk, D).to(torch.bfloat16), rnd(chunk, 1)
+    key_tok, key_gate = rnd(chunk, d_I).to(torch.bfloat16), rnd(chunk, 1)
+    q_pos_h = (cached + np.arange(chunk)).astype(np.int64)
+    n_ent_h = (q_pos_h + 1) // m
+    q_pos = torch.as_tensor(q_pos_h, device=cuda)
+    n_valid = torch.as_tensor(n_ent_h, device=cuda)
+    zeros = torch.zeros(chunk, dtype=torch.int64, device=cuda)
+    tp0 = torch.full((chunk,), tok_pos0, dtype=torch.int64, device=cuda)
+    seg = torch.tensor([0, chunk], dtype=torch.int64, device=cuda)
+    pos0 = torch.tensor([cached], dtype=torch.int64, device=cuda)
+    scores = torch.empty((chunk, n_tot), dtype=torch.float32, device=cuda)
+    idx = torch.empty((chunk, k), dtype=torch.int32, device=cuda)
+    out = torch.empty((chunk, H, D), dtype=torch.bfloat16, device=cuda)
+
+    def job(x, gate, DD, mm, row0, normalize, R_, dst, fmt):
+        return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=chunk, D=DD, m=mm, nseg=1,
+                    seg_tok_off=seg, seg_pos0=pos0, seg_out_row=torch.tensor([row0], dtype=torch.int64, device=cuda),
+                    normalize=normalize, norm_w=None, eps=EPS, rope_dim=R_, rope_base=BASE, out=dst, out_fmt=fmt)
+    jobs = [job(kv_tok, kv_gate, D, m, cached // m, 1, R, kv, csa.SPLIT),
+            job(key_tok, key_gate, d_I, m, cached // m, 0, 0, keys, csa.FP8),
+            job(kv_tok, torch.zeros((chunk, 1), device=cuda), D, 1, cached - tok_pos0, 1, R, tok, csa.BF16)]
+    kernels = [
+        ("csa_compress_batch", lambda: csa.csa_compress_batch(jobs, check=False)),
+        ("indexer_score", lambda: csa.indexer_score(q_idx, w, chunk, H_I, d_I, keys, csa.FP8, zeros, q_pos, m,
+                                                    scores, n_tot, check=False)),
+        ("topk_select", lambda: csa.topk_select(scores, n_tot, chunk, n_valid, k, idx, None, check=False)),
+        ("hybrid_attn_prefill", lambda: csa.hybrid_attn_prefill(
+            q, csa.BF16, chunk, H, D, q_pos, None, EPS, R, BASE, kv, csa.SPLIT, zeros, m, idx, k, tok, csa.BF16,
+            zeros, tp0, n_win, sinks, 1.0 / np.sqrt(D), out, csa.BF16, check=False)),
+    ]
+    for _, f in kernels:
+        f()
+    torch.cuda.synchronize()
+    empty = _event_pairs([lambda: None], reps)
+    us = {n: _event_pairs([f], reps) - empty for n, f in kernels}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for _, f in kernels:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    attended = np.minimum(k, n_ent_h) + np.minimum(n_win, q_pos_h - tok_pos0 + 1)
+    f_idx = 2.0 * n_ent_h.sum() * H_I * d_I
+    f_attn = 4.0 * attended.sum() * H * D
+    tflops = lambda f, t: f / (t * 1e-6) / 1e12  # noqa: E731
+    topk_bytes = int(n_ent_h.sum()) * 4 + chunk * k * 4
+    res = {"workload": PREFILL, "ms_per_chunk": ms, "tokens_per_s": chunk / (ms * 1e-3),
+           "kernels_us": {n: round(v, 1) for n, v in us.items()},
+           "indexer_tflops": tflops(f_idx, us["indexer_score"]),
+           "indexer_mfma_frac": tflops(f_idx, us["indexer_score"]) / BF16_PEAK_TFLOPS,
+           "attn_tflops": tflops(f_attn, us["hybrid_attn_prefill"]),
+           "attn_mfma_frac": tflops(f_attn, us["hybrid_attn_prefill"]) / BF16_PEAK_TFLOPS,
+           "topk_gbps": topk_bytes / (us["topk_select"] * 1e-6) / 1e9}
+    del kv, keys, tok, scores, q, q_idx
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +515,8 @@ def main():
                     help="per-layer state copies stepped in turn (1 = one warm cache)")
     ap.add_argument("--no-context-scan", action="store_true",
                     help="skip the same step at 256K and 1M contexts")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the CSA prefill chunk (2,048 tokens after 131,072)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -489,6 +582,8 @@ def main():
     }
     if not args.no_context_scan:
         line["context_scan"] = context_scan([262144, 1048576], args.steps, args.warmup)
+    if not args.no_prefill:
+        line["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -271,11 +271,21 @@ def test_topk_long_rows_in_a_graph():
 
 
 @pytest.mark.parametrize("ld", [20000, 40000])
-@pytest.mark.parametrize("case", ["all_equal", "two_levels", "with_inf", "huge_range", "negatives"])
+@pytest.mark.parametrize("case", ["all_equal", "two_levels", "with_inf", "huge_range", "negatives",
+                                  "ties_at_kth"])
 def test_topk_edge_rows(case, ld):
     rng = np.random.default_rng(5)
     nq, k = 3, 512
-    if case == "all_equal":
+    nv = np.array([ld, 777, 513], np.int64)
+    if case == "ties_at_kth":
+        # a few copies of each row's k-th largest score: some of them are taken
+        # (the lowest indices), the rest are not
+        s = rng.standard_normal((nq, ld)).astype(np.float32)
+        for i in range(nq):
+            n = int(nv[i])
+            kth = np.sort(s[i, :n])[n - k]
+            s[i, rng.choice(n, size=7, replace=False)] = kth
+    elif case == "all_equal":
         s = np.full((nq, ld), 1.5, np.float32)
     elif case == "two_levels":
         s = np.where(rng.random((nq, ld)) < 0.01, 2.0, 1.0).astype(np.float32)
@@ -287,7 +297,6 @@ def test_topk_edge_rows(case, ld):
         s = (rng.standard_normal((nq, ld)) * 10.0 ** rng.integers(-30, 30, (nq, ld))).astype(np.float32)
     else:
         s = -np.abs(rng.standard_normal((nq, ld))).astype(np.float32)
-    nv = np.array([ld, 777, 513], np.int64)
     idx = torch.empty((nq, k), dtype=torch.int32, device=DEV)
     csa.topk_select(dev(s), ld, nq, dev(nv), k, idx)
     got = idx.cpu().numpy()
