@@ -225,6 +225,168 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
   }
 }
 
+// --------------------------------------------------------------- FP8, d = 128, shared keys
+// A prefill batch holds many queries of one sequence, which read the same key
+// rows.  A workgroup takes kShareQ = 4 consecutive queries (one per wave) and
+// a run of up to kShareGroups 64-key groups.  When the four read the same
+// rows (equal key offsets), each group is loaded once -- wave w loads block w
+// with the lane pattern of the streaming kernel -- widened once into LDS, and
+// every wave multiplies it against its own query.  The operands, MFMA tiles,
+// their order and the head sum are those of the streaming kernel, so a score
+// has the same bits whichever kernel computed it.  Keys past a query's own N
+// are multiplied but their scores are not stored.  A block whose queries read
+// different rows streams each wave's own groups instead.
+constexpr int kShareQ = 4;
+constexpr int kShareGroups = 32;
+constexpr int kShareMinQueries = 1024;   // batches this large take the shared-key kernel
+
+struct SharedKeys {
+  bf16x8 k[2][4][4][64];   // [buffer][block][k-step][lane]
+};
+
+// One 16-key block from widened operands: the per-block step of group_fp8.
+template <int NHB>
+__device__ __forceinline__ void block_bf16(const bf16x8 (&kk)[4], const bf16x8 (&qb)[NHB][4],
+                                           const float (&wr)[NHB][4], f32x4 (&cp)[NHB], int& pend, int nxt,
+                                           buf_rsrc out_rs, uint32_t out_off) {
+  f32x4 cc[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) cc[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
+  const float tot = head_sum<NHB>(cp, wr);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs,
+                                        static_cast<int>(pend >= 0 ? out_off : 0x80000000u),
+                                        pend >= 0 ? pend : 0, 0);
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) cp[hb] = cc[hb];
+  pend = nxt;
+}
+
+template <int NHB>
+__global__ void __launch_bounds__(256) indexer_fp8_shared_kernel(IndexerArgs a, int64_t n_qblk,
+                                                                 int64_t n_kchunk) {
+  constexpr int H = NHB * 16;
+  __shared__ SharedKeys sk;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int g = lane >> 4, j16 = lane & 15;
+  const uint8_t* qall = static_cast<const uint8_t*>(a.q);
+  for (int64_t unit = blockIdx.x; unit < n_qblk * n_kchunk; unit += gridDim.x) {
+    const int i0 = static_cast<int>(unit / n_kchunk) * kShareQ;
+    const uint32_t t0 = static_cast<uint32_t>(unit % n_kchunk) * kShareGroups;
+    const int nqb = a.nq - i0 < kShareQ ? a.nq - i0 : kShareQ;    // queries in the block (uniform)
+    const bool mine = wv < nqb;
+    const int i = mine ? i0 + wv : i0;                  // a wave past the batch reads query i0, stores nothing
+    // this wave's query rows and weights, then the block's positions and key offsets
+    uint4 qraw[NHB][2];
+    float4 wraw[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(i) * H + hb * 16 + j16) * 128 + g * 32);
+      qraw[hb][0] = qp[0];
+      qraw[hb][1] = qp[1];
+      wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
+    }
+    int64_t koff0 = 0, koff_i = 0, N_i = 0, N_max = 0;
+    bool same = true;
+#pragma unroll
+    for (int q = 0; q < kShareQ; ++q) {
+      const int iq = i0 + (q < nqb ? q : 0);
+      const int64_t ko = uniform64(scalar_load(a.key_off, iq));
+      int64_t n = (uniform64(scalar_load(a.q_pos, iq)) + 1) / a.m;
+      n = n > a.ld ? a.ld : n;
+      if (q == 0) koff0 = ko;
+      same = same && ko == koff0;
+      N_max = n > N_max ? n : N_max;
+      if (q == wv) { koff_i = ko; N_i = n; }
+    }
+    const uint32_t G = static_cast<uint32_t>((N_max + kGroupKeys - 1) / kGroupKeys);
+    if (t0 >= G) continue;                               // uniform over the workgroup
+    const uint32_t t1 = G - t0 < static_cast<uint32_t>(kShareGroups) ? G : t0 + kShareGroups;
+    bf16x8 qb[NHB][4];
+    float wr[NHB][4];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      qb[hb][0] = fp8x8_to_bf16(qraw[hb][0].x, qraw[hb][0].y);
+      qb[hb][1] = fp8x8_to_bf16(qraw[hb][0].z, qraw[hb][0].w);
+      qb[hb][2] = fp8x8_to_bf16(qraw[hb][1].x, qraw[hb][1].y);
+      qb[hb][3] = fp8x8_to_bf16(qraw[hb][1].z, qraw[hb][1].w);
+      wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
+    }
+    const buf_rsrc out_rs = make_rsrc(a.scores + static_cast<int64_t>(i) * a.ld,
+                                      mine ? static_cast<uint32_t>(N_i * 4) : 0u);
+    const uint32_t out_off = g == 0 ? static_cast<uint32_t>(j16) * 4u : 0x80000000u;
+    f32x4 cp[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    int pend = -1;
+    if (same) {
+      // wave wv loads block wv of every group: rows t*64 + wv*16 + j16, bytes [32g, 32g+32)
+      const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + koff0 * 128,
+                                    static_cast<uint32_t>(N_max * 128));
+      const uint32_t voff0 = (t0 * kGroupKeys + static_cast<uint32_t>(wv) * 16u + j16) * 128u + g * 32u;
+      // group t -> buffer (t - t0) % 2; its loads went out two groups earlier
+      auto load = [&](uint4 (&kr)[2], uint32_t t) __attribute__((always_inline)) {
+        const uint32_t o = t < t1 ? voff0 + (t - t0) * (kGroupKeys * 128u) : 0x80000000u;   // past t1: no traffic
+        kr[0] = buf_load_x4(rs, o, 0);
+        kr[1] = buf_load_x4(rs, o + 16u, 0);
+      };
+      auto step = [&](uint4 (&kr)[2], uint32_t t, int buf) __attribute__((always_inline)) {
+        bf16x8* dst = &sk.k[buf][wv][0][lane];
+        dst[0] = fp8x8_to_bf16(kr[0].x, kr[0].y);
+        dst[64] = fp8x8_to_bf16(kr[0].z, kr[0].w);
+        dst[128] = fp8x8_to_bf16(kr[1].x, kr[1].y);
+        dst[192] = fp8x8_to_bf16(kr[1].z, kr[1].w);
+        // the buffer holds the whole group once every wave's LDS writes are
+        // done (and every wave has read the group two back from it); the
+        // barrier waits for LDS only, so the key loads stay in flight
+        asm volatile("" : : : "memory");
+        __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" : : : "memory");
+        load(kr, t + 2);                                 // two groups ahead
+        asm volatile("" : : : "memory");                 // (issued before the group's LDS reads)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 kk[4] = {sk.k[buf][kb][0][lane], sk.k[buf][kb][1][lane], sk.k[buf][kb][2][lane],
+                                sk.k[buf][kb][3][lane]};
+          block_bf16<NHB>(kk, qb, wr, cp, pend, static_cast<int>((t * kGroupKeys + kb * 16u) * 4u), out_rs,
+                          out_off);
+        }
+      };
+      uint4 ka[2], kb2[2];
+      load(ka, t0);
+      asm volatile("" : : : "memory");                   // in this order: the loop's waits count on it
+      load(kb2, t0 + 1);
+      for (uint32_t t = t0; t < t1; t += 2) {
+        step(ka, t, 0);
+        if (t + 1 < t1) step(kb2, t + 1, 1);             // uniform over the workgroup
+      }
+    } else {
+      // the wave's own rows, group by group (no barriers: the branch is
+      // uniform over the workgroup and this path has none)
+      const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + koff_i * 128,
+                                    static_cast<uint32_t>(N_i * 128));
+      const uint32_t voff0 = (t0 * kGroupKeys + j16) * 128u + g * 32u;
+      const int ng = static_cast<int>(t1 - t0);
+      uint4 ka[4][2];
+      for (int t = 0; t < ng; ++t) {
+        load_group_fp8(rs, voff0, kGroupKeys * 128u, t, ng, ka);
+        group_fp8<NHB>(ka, qb, wr, cp, pend, static_cast<int>((t0 + static_cast<uint32_t>(t)) * kGroupKeys * 4u),
+                       out_rs, out_off);
+      }
+    }
+    const float tot = head_sum<NHB>(cp, wr);
+    if (pend >= 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off), pend, 0);
+    __syncthreads();                                     // the next unit refills the buffers
+  }
+}
+
 // --------------------------------------------------------------- MXFP4, d = 128
 // Row: 64 bytes of E2M1 codes then 4 E8M0 scales.  Scaled MFMA 16x16x128:
 // lane (row j16, k-block g) supplies 16 code bytes and the scale of block g.
@@ -395,6 +557,21 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     if (il) hipLaunchKernelGGL((K<NB, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);   \
     else hipLaunchKernelGGL((K<NB, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);     \
     break;
+  if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries) {
+    const int64_t n_qblk = (a.nq + kShareQ - 1) / kShareQ;
+    const int64_t n_kchunk = ((a.ld + kGroupKeys - 1) / kGroupKeys + kShareGroups - 1) / kShareGroups;
+    const int64_t units = n_qblk * n_kchunk;
+    const int64_t cap_o = static_cast<int64_t>(device_cu_count()) * (nhb <= 2 ? 4 : 2);   // resident workgroups
+    const unsigned grid_s = static_cast<unsigned>(units < cap_o ? units : cap_o);
+    switch (nhb) {
+      case 1: hipLaunchKernelGGL(indexer_fp8_shared_kernel<1>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
+      case 2: hipLaunchKernelGGL(indexer_fp8_shared_kernel<2>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
+      case 4: hipLaunchKernelGGL(indexer_fp8_shared_kernel<4>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
+      case 8: hipLaunchKernelGGL(indexer_fp8_shared_kernel<8>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (a.fmt == CSA_FP8) {
     switch (nhb) {
       CSA_IDX_CASE(indexer_fp8_kernel, 1)

@@ -213,6 +213,49 @@ def test_indexer_long_contexts(fmt):
         assert np.all(got[b, N:] == -7.0), "scores past N must stay untouched"
 
 
+@pytest.mark.parametrize("H_I", [64, 32])
+def test_indexer_shared_keys_match_streaming_bits(H_I):
+    """Large batches take the shared-key kernel (a workgroup multiplies one
+    loaded key group against four queries of the same sequence).  Its scores
+    must carry the same bits as the streaming kernel's for the same queries in
+    a small batch, and match the oracle.  The batch mixes two sequences (one
+    four-query block straddles them and streams per wave), ragged visible
+    counts inside blocks, and a two-query tail block."""
+    gen = synth.device_generator(61 + H_I)
+    rng = np.random.default_rng(62 + H_I)
+    m, d_I = 4, 128
+    n_a, n_b = 40000, 5000                                   # keys of the two sequences
+    keys = synth.device_rows(gen, n_a + n_b, d_I, csa.FP8)
+    nq_a, nq_b = 701, 401                                    # 1102 queries: block 175 holds both
+    q_pos = np.concatenate([rng.integers(0, n_a * m, nq_a), rng.integers(0, n_b * m, nq_b)]).astype(np.int64)
+    q_pos[:8] = [n_a * m - 1, 3, 64 * m - 1, 64 * m, 2048 * m + 5, n_a * m - 2, 0, 17]
+    key_off = np.concatenate([np.zeros(nq_a), np.full(nq_b, n_a)]).astype(np.int64)
+    nq = nq_a + nq_b
+    q_idx = synth.device_rows(gen, nq * H_I, d_I, csa.FP8).reshape(nq, H_I, -1)
+    w = torch.rand((nq, H_I), generator=gen, device=DEV, dtype=torch.float32)
+    ld = n_a
+    big = torch.full((nq, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(q_idx, w, nq, H_I, d_I, keys, csa.FP8, dev(key_off), dev(q_pos), m, big, ld)
+    picks = np.array([0, 1, 2, 3, 4, 5, 6, 7, 350, 699, 700, 701, 702, 703, 1100, 1101])
+    small = torch.full((len(picks), ld), -7.0, dtype=torch.float32, device=DEV)
+    pk = torch.as_tensor(picks, device=DEV)
+    csa.indexer_score(q_idx[pk].contiguous(), w[pk].contiguous(), len(picks), H_I, d_I, keys, csa.FP8,
+                      dev(key_off[picks]), dev(q_pos[picks]), m, small, ld)
+    got_big = big.cpu().numpy()
+    got_small = small.cpu().numpy()
+    for r, i in enumerate(picks):
+        assert np.array_equal(got_big[i].view(np.uint32), got_small[r].view(np.uint32)), f"query {i}: bits differ"
+    keys_h = keys.cpu().numpy()
+    for i in picks[[0, 1, 4, 8, 10, 11, 15]]:
+        N = min(int((q_pos[i] + 1) // m), ld)
+        kb = OF.decode_rows(keys_h[key_off[i]: key_off[i] + N], csa.FP8, d_I)
+        ref = OM.indexer_scores(OF.decode_rows(q_idx[i].cpu().numpy(), csa.FP8, d_I),
+                                w[i].cpu().numpy().astype(np.float64), kb)
+        err = np.abs(got_big[i, :N] - ref).max() / max(1.0, np.abs(ref).max()) if N else 0.0
+        assert err <= 1e-5, f"query {i}: relative score error {err:.3g}"
+        assert np.all(got_big[i, N:] == -7.0), f"query {i}: scores past N must stay untouched"
+
+
 # ------------------------------------------------------------------ top-k
 @pytest.mark.parametrize("ld,k,tie_levels,n_valid", [
     (16384, 512, 0, None), (16384, 512, 5, None), (5000, 1024, 0, [5000, 4999, 1024, 1000, 1, 0]),
