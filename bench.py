@@ -517,16 +517,23 @@ def main():
                     help="skip the same step at 256K and 1M contexts")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the CSA prefill chunk (2,048 tokens after 131,072)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time the CSA prefill chunk and print its object (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(decode shards by sequence; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (decode would "
+              "shard by sequence, each GPU stepping its own sequences). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe, max(1, args.steps))
+        return
+    if args.prefill_only:
+        csa.load_library()
+        print(json.dumps({"prefill": prefill_leg()}), flush=True)
         return
     csa.load_library()
     W = build_workload()

@@ -54,7 +54,7 @@ extern "C" {
 typedef enum csa_status {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, a mismatch */
-  CSA_ERR_UNSUPPORTED = 2, /* a valid combination this build has no kernel for */
+  CSA_ERR_UNSUPPORTED = 2, /* a valid combination the library has no kernel for */
   CSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
 } csa_status;
 
