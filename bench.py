@@ -24,7 +24,8 @@ Prints one JSON line.  `roofline` is measured for the dominant kernel
 launches on its stream; `kernels` gives every kernel's duration, algorithmic
 bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
 float64 oracle on a bounded sample on the host.  `context_scan` repeats the
-step at 256K and 1M tokens per sequence; `prefill` times the CSA prefill
+step at 256K and 1M tokens per sequence; `hca_decode` the HCA decode step
+(32 x 262,144 tokens, every compressed entry attended); `prefill` the CSA prefill
 chunk (2,048 tokens after 131,072 cached: compress, indexer, top-k 1,024,
 prefill attention) and the contractions' MFMA rates.  `--copy-probe MIB` only
 runs a plain copy of known size, the reference for rocprofv3 byte counters.
@@ -416,6 +417,76 @@ def context_scan(contexts, steps, warmup):
     return rows
 
 
+HCA = "hca_decode_b32_ctx262144"
+
+
+def hca_leg(steps, warmup):
+    """The HCA decode workload: 32 sequences of 262,144 tokens, m' = 128, so
+    2,048 compressed entries per sequence, every one attended (no indexer, no
+    top-k), plus the 128-token window.  One step = csa_compress_batch (the
+    newest 128-token block's entry and the new token's window row) +
+    hybrid_attn_decode.  The state is replicated so that a pass over the
+    copies reads more than 600 MB, and the copies' steps are captured in one
+    graph, as for the CSA line.  Reports ms per step, query-tokens/s and the
+    attention's algorithmic HBM rate and MFMA rate."""
+    c = synth.WORKLOADS[HCA]
+    B, L, m, H, D, R, n_win = c["B"], c["L"], c["m"], c["H"], c["D"], c["R"], c["n_win"]
+    d = synth.device_decode_inputs(c["seed"] + 3000, [L] * B, m=m, H=H, D=D, R=R, n_win=n_win, csa=False)
+    gen = synth.device_generator(c["seed"] + 3001)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)  # noqa: E731
+    n_ent, kv_off_h, q_pos_h = d["n_ent"], d["kv_off"], d["q_pos"]
+    win_len_h = d["win_len"]
+    tc = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int64), device="cuda")  # noqa: E731
+    kv_tok, kv_gate = rnd(B * m, D).to(torch.bfloat16), rnd(B * m, 1)
+    win_tok, win_gate = rnd(B, D).to(torch.bfloat16), torch.zeros((B, 1), device="cuda")
+    seg_off, seg_pos0, seg_row = tc(np.arange(B + 1) * m), tc((n_ent - 1) * m), tc(kv_off_h + n_ent - 1)
+    wseg_off, wpos0 = tc(np.arange(B + 1)), tc(q_pos_h)
+    wrow = tc(np.arange(B) * n_win + win_len_h.astype(np.int64) - 1)
+    q_pos, kv_off = tc(q_pos_h), tc(kv_off_h)
+    win_len = torch.as_tensor(win_len_h, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    state_bytes = d["kv"].numel() + d["win"].numel()
+    n_rep = max(1, -(-600_000_000 // state_bytes))
+    states = [(d["kv"], d["win"])] + [(d["kv"].clone(), d["win"].clone()) for _ in range(n_rep - 1)]
+
+    def make(kv, win):
+        def job(x, gate, mm, off, pos0, rows, dst, fmt):
+            return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=B * mm, D=D, m=mm, nseg=B,
+                        seg_tok_off=off, seg_pos0=pos0, seg_out_row=rows, normalize=1, norm_w=None, eps=EPS,
+                        rope_dim=R, rope_base=BASE, out=dst, out_fmt=fmt)
+        jobs = [job(kv_tok, kv_gate, m, seg_off, seg_pos0, seg_row, kv, csa.SPLIT),
+                job(win_tok, win_gate, 1, wseg_off, wpos0, wrow, win, csa.BF16)]
+        kernels = [("csa_compress_batch", lambda: csa.csa_compress_batch(jobs, check=False)),
+                   ("hybrid_attn_decode", lambda: csa.hybrid_attn_decode(
+                       d["q"], csa.BF16, B, H, D, q_pos, None, EPS, R, BASE, kv, csa.SPLIT, kv_off, m, None, 0,
+                       win, csa.BF16, n_win, win_len, d["sinks"], d["scale"], out, csa.BF16, csa.VARIANT_AUTO,
+                       check=False))]
+
+        def step():
+            for _, f in kernels:
+                f()
+        return step, kernels
+    made = [make(kv, win) for kv, win in states]
+    for st, _ in made:
+        st()
+    torch.cuda.synchronize()
+    ms = time_graph([m_[0] for m_ in made], steps, warmup)
+    per_us, _ = time_kernels([m_[1] for m_ in made], max(20, min(60, steps)))
+    split = (D - R) + 2 * R
+    attended = n_ent.astype(np.int64) + win_len_h.astype(np.int64)
+    a_bytes = int(n_ent.sum()) * split + int(win_len_h.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4
+    a_flops = 4.0 * attended.sum() * H * D
+    t = per_us["hybrid_attn_decode"] * 1e-6
+    res = {"workload": HCA, "ms_per_step": ms, "query_tokens_per_s": B / (ms * 1e-3),
+           "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
+           "attn_bytes": a_bytes, "attn_gbps": a_bytes / t / 1e9, "attn_hbm_frac": a_bytes / t / 1e9 / HBM_PEAK_GBPS,
+           "attn_tflops": a_flops / t / 1e12, "attn_mfma_frac": a_flops / t / 1e12 / BF16_PEAK_TFLOPS,
+           "state_replicas": n_rep}
+    del states, made, d
+    torch.cuda.empty_cache()
+    return res
+
+
 PREFILL = "csa_prefill_ctx131072_chunk2048"
 
 
@@ -515,6 +586,8 @@ def main():
                     help="per-layer state copies stepped in turn (1 = one warm cache)")
     ap.add_argument("--no-context-scan", action="store_true",
                     help="skip the same step at 256K and 1M contexts")
+    ap.add_argument("--no-hca", action="store_true",
+                    help="skip the HCA decode step (32 sequences of 262,144 tokens)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the CSA prefill chunk (2,048 tokens after 131,072)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -589,6 +662,8 @@ def main():
     }
     if not args.no_context_scan:
         line["context_scan"] = context_scan([262144, 1048576], args.steps, args.warmup)
+    if not args.no_hca:
+        line["hca_decode"] = hca_leg(args.steps, args.warmup)
     if not args.no_prefill:
         line["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:

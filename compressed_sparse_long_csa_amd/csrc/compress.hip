@@ -198,7 +198,17 @@ __device__ __forceinline__ void block_small(const CompressArgs& a, int64_t blk, 
   finish_entry(a, y, red, sq, *slot);
 }
 
-// One block, any m and D: values are read inside the block loop.
+// One block, any m and D: values are read inside the block loop.  With one
+// gate logit per token, m <= 256 (HCA's m' = 128) and rows that split into
+// 16-byte chunks (8 BF16 or 4 F32 channels, 16-byte aligned) over at most 256 threads, the
+// block's weights exp(g_t - max) are computed once per token into LDS, and
+// the threads split as (token group, chunk): thread (g, k) sums chunk k over
+// the tokens t = g, g + G, g + 2G, ... in order, all its loads in flight at
+// once (for D = 512 BF16: 4 groups of 32 tokens, the whole 128 KB block in one
+// round trip).  The G partial sums are added into LDS in group order, and the
+// weights' sum runs over the tokens in order, so the bits are fixed.
+constexpr int kMaxChunkTokens = 32;                    // tokens per thread in that path
+
 __device__ __forceinline__ void block_any(const CompressArgs& a, int64_t blk, float* y, float* red,
                                           EntrySlot* slot) {
   const int tid = threadIdx.x, D = a.D, m = a.m;
@@ -206,6 +216,65 @@ __device__ __forceinline__ void block_any(const CompressArgs& a, int64_t blk, fl
   locate(a, t0, slot);
   if (!slot->ok) return;
   float sq = 0.0f;
+  const int per16 = a.x_fmt == CSA_F32 ? 4 : 8;          // channels per 16-byte chunk
+  const int chunks = D % per16 == 0 ? D / per16 : 0;
+  const int groups = chunks > 0 && chunks <= kThreads && kThreads % chunks == 0 ? kThreads / chunks : 0;
+  if (a.gate_cols == 1 && m <= kThreads && groups > 0 && (m + groups - 1) / groups <= kMaxChunkTokens &&
+      (reinterpret_cast<uintptr_t>(a.x) & 15u) == 0) {
+    __shared__ float e_sh[kThreads];
+    float gm = -INFINITY;
+    if (tid < m) gm = a.gate[t0 + tid];
+    gm = wave_max(gm);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = gm;
+    __syncthreads();
+    float gmax = red[0];
+    for (int w = 1; w < kThreads / kWave; ++w) gmax = fmaxf(gmax, red[w]);
+    if (tid < m) e_sh[tid] = expf(a.gate[t0 + tid] - gmax);
+    __syncthreads();                                   // e_sh ready; red free again
+    float den = 0.0f;
+    for (int t = 0; t < m; ++t) den += e_sh[t];
+    const int grp = tid / chunks, k = tid % chunks;
+    const int nt = grp < m ? (m - grp + groups - 1) / groups : 0;   // tokens of this thread
+    const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.x) +
+                                                      (t0 * D) * (a.x_fmt == CSA_F32 ? 4 : 2)) + k;
+    const int64_t row16 = D / per16;                   // 16-byte chunks per token row
+    uint4 raw[kMaxChunkTokens];
+#pragma unroll
+    for (int u = 0; u < kMaxChunkTokens; ++u)
+      if (u < nt) raw[u] = xr[(grp + static_cast<int64_t>(u) * groups) * row16];
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kMaxChunkTokens; ++u) {
+      if (u < nt) {
+        const float e = e_sh[grp + u * groups];
+        const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+        if (per16 == 8) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[2 * j] = fmaf(e, bf16_to_f32(static_cast<uint16_t>(w4[j] & 0xffffu)), acc[2 * j]);
+            acc[2 * j + 1] = fmaf(e, bf16_to_f32(static_cast<uint16_t>(w4[j] >> 16)), acc[2 * j + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = fmaf(e, __uint_as_float(w4[j]), acc[j]);
+        }
+      }
+    }
+    // the groups' partial sums, added into y in group order
+    for (int gg = 0; gg < groups; ++gg) {
+      if (grp == gg) {
+        for (int j = 0; j < per16; ++j) y[k * per16 + j] = gg == 0 ? acc[j] : y[k * per16 + j] + acc[j];
+      }
+      __syncthreads();
+    }
+    for (int c = tid; c < D; c += kThreads) {
+      const float v = y[c] / den;
+      y[c] = v;
+      sq = fmaf(v, v, sq);
+    }
+    finish_entry(a, y, red, sq, *slot);
+    return;
+  }
   for (int c = tid; c < D; c += kThreads) {
     const int gc = a.gate_cols == 1 ? 0 : c;
     float gmax = -INFINITY;

@@ -61,17 +61,25 @@ def _compress_error_bound(x, g, m, y, R, normalize):
     return 2.0 * bound + 2.0 ** -20 * np.abs(y)
 
 
-@pytest.mark.parametrize("m,gate_cols,out_fmt,D,R", [
-    (4, 1, csa.F32, 128, 64), (128, 1, csa.F32, 128, 64), (4, "D", csa.F32, 64, 16),
-    (4, 1, csa.SPLIT, 512, 64), (128, 1, csa.SPLIT, 512, 64), (1, 1, csa.BF16, 512, 64),
-    (4, 1, csa.FP8, 128, 0), (4, 1, csa.MXFP4, 128, 0), (1, 1, csa.MXFP4, 128, 0),
+@pytest.mark.parametrize("m,gate_cols,out_fmt,D,R,x_fmt", [
+    (4, 1, csa.F32, 128, 64, csa.F32), (128, 1, csa.F32, 128, 64, csa.F32), (4, "D", csa.F32, 64, 16, csa.F32),
+    (4, 1, csa.SPLIT, 512, 64, csa.F32), (128, 1, csa.SPLIT, 512, 64, csa.F32), (1, 1, csa.BF16, 512, 64, csa.F32),
+    (4, 1, csa.FP8, 128, 0, csa.F32), (4, 1, csa.MXFP4, 128, 0, csa.F32), (1, 1, csa.MXFP4, 128, 0, csa.F32),
+    # BF16 tokens: m = 128 over 16-byte chunks (four token groups at D = 512), m = 32, per-channel gates
+    (128, 1, csa.SPLIT, 512, 64, csa.BF16), (128, 1, csa.BF16, 128, 64, csa.BF16), (32, 1, csa.FP8, 128, 0, csa.BF16),
+    (128, "D", csa.SPLIT, 256, 64, csa.BF16),
 ])
-def test_compress_matches_oracle(m, gate_cols, out_fmt, D, R):
+def test_compress_matches_oracle(m, gate_cols, out_fmt, D, R, x_fmt):
     gc = D if gate_cols == "D" else gate_cols
     seg_len = [m * 7, m * 3, 0, m * 11]               # ragged segments incl. an empty one
     seg_pos0 = [0, 4 * m, 96 * m, 1000 * m]
     T = sum(seg_len)
     tok = synth.token_inputs(11 + m, T, D, gc)
+    if x_fmt == csa.BF16:                             # the kernel reads BF16; the oracle gets its values
+        x_dev = torch.from_numpy(tok.x).to(DEV).to(torch.bfloat16)
+        tok.x = x_dev.float().cpu().numpy()
+    else:
+        x_dev = dev(tok.x)
     off = np.concatenate([[0], np.cumsum(seg_len)]).astype(np.int64)
     nent = [s // m for s in seg_len]
     out_row = np.array([5, 5 + nent[0], 0, 5 + nent[0] + nent[1]], dtype=np.int64)
@@ -79,7 +87,7 @@ def test_compress_matches_oracle(m, gate_cols, out_fmt, D, R):
     rb = csa.row_bytes(out_fmt, D, R)
     out = torch.zeros(n_rows * rb, dtype=torch.uint8, device=DEV)
     normalize = R > 0
-    csa.csa_compress(dev(tok.x), csa.F32, dev(tok.gate), gc, T, D, m, 4, dev(off),
+    csa.csa_compress(x_dev, x_fmt, dev(tok.gate), gc, T, D, m, 4, dev(off),
                      dev(np.array(seg_pos0, np.int64)), dev(out_row), normalize, None, EPS, R,
                      ROPE_BASE, out, out_fmt)
     raw = out.cpu().numpy().reshape(n_rows, rb)
