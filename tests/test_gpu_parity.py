@@ -283,6 +283,10 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
     csa.topk_select(dev(s), ld, nq, dev(nv), k, idx, tops)
     got = idx.cpu().numpy()
     gs = tops.cpu().numpy()
+    # without the score output (rows placed from the compacted pass): the same indices
+    idx2 = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(dev(s), ld, nq, dev(nv), k, idx2)
+    assert np.array_equal(idx2.cpu().numpy(), got)
     for i in range(nq):
         n = int(nv[i])
         want = OM.top_k(s[i, :n].astype(np.float64), k)
