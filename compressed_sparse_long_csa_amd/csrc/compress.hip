@@ -295,6 +295,10 @@ __device__ __forceinline__ void block_any(const CompressArgs& a, int64_t blk, fl
 // Block shapes with a register-resident body; kAny covers the rest.
 enum BlockKind { kM4C1, kM4C2, kM1C1, kM1C2, kM1C4, kAny };
 
+// kWithAny = false leaves the general-m body out (its token-group path holds
+// 32 16-byte loads in registers, which would lower every block shape's
+// occupancy); launches whose jobs include a general-m block use true.
+template <bool kWithAny = true>
 __device__ __forceinline__ void run_block(const CompressArgs& a, int kind, int64_t blk, float* y,
                                           float* red, EntrySlot* slot) {
   switch (kind) {
@@ -303,7 +307,9 @@ __device__ __forceinline__ void run_block(const CompressArgs& a, int kind, int64
     case kM1C1: block_small<1, 1>(a, blk, y, red, slot); break;
     case kM1C2: block_small<1, 2>(a, blk, y, red, slot); break;
     case kM1C4: block_small<1, 4>(a, blk, y, red, slot); break;
-    default: block_any(a, blk, y, red, slot); break;
+    default:
+      if (kWithAny) block_any(a, blk, y, red, slot);
+      break;
   }
 }
 
@@ -317,6 +323,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a, int6
 
 // Several independent compress calls in one launch: global block b belongs
 // to the job j with blk0[j] <= b < blk0[j + 1] (uniform over the workgroup).
+template <bool kWithAny>
 __global__ void __launch_bounds__(kThreads) compress_jobs_kernel(CompressJobs J) {
   extern __shared__ float y[];
   __shared__ EntrySlot slot;
@@ -325,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) compress_jobs_kernel(CompressJobs J)
     int j = 0;
     while (j + 1 < J.n && b >= J.blk0[j + 1]) ++j;
     const CompressArgs& a = J.a[j];
-    run_block(a, J.kind[j], b - J.blk0[j], y, y + a.D, &slot);
+    run_block<kWithAny>(a, J.kind[j], b - J.blk0[j], y, y + a.D, &slot);
   }
 }
 
@@ -365,11 +372,13 @@ hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t str
   J.n = 0;
   J.blk0[0] = 0;
   int maxD = 1;
+  bool any = false;
   for (int i = 0; i < n; ++i) {
     const int64_t nb = jobs[i].n_tok / jobs[i].m;
     if (nb == 0) continue;
     J.a[J.n] = jobs[i];
     J.kind[J.n] = block_kind(jobs[i]);
+    any = any || J.kind[J.n] == kAny;
     J.blk0[J.n + 1] = J.blk0[J.n] + nb;
     maxD = jobs[i].D > maxD ? jobs[i].D : maxD;
     ++J.n;
@@ -377,8 +386,12 @@ hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t str
   if (J.n == 0) return hipSuccess;
   const int64_t total = J.blk0[J.n];
   const int64_t grid = total < 65536 ? total : 65536;
-  hipLaunchKernelGGL(compress_jobs_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     shm_bytes(maxD), stream, J);
+  if (any)
+    hipLaunchKernelGGL(compress_jobs_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       shm_bytes(maxD), stream, J);
+  else
+    hipLaunchKernelGGL(compress_jobs_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       shm_bytes(maxD), stream, J);
   return hipGetLastError();
 }
 
