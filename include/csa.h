@@ -19,10 +19,11 @@
  *     kernels on `stream` and returns; nothing is synchronised.  On any status
  *     other than CSA_OK nothing was enqueued, except CSA_ERR_HIP, which reports
  *     a failed launch.  csa_last_error() returns a thread-local message.
- *   - The caller owns every buffer.  The library allocates nothing, frees
- *     nothing, keeps no pointer after returning and never writes `const`
- *     inputs.  Calls on different streams touching disjoint outputs may run
- *     concurrently.
+ *   - The caller owns every buffer.  The library keeps no pointer after
+ *     returning and never writes `const` inputs; it allocates nothing except
+ *     topk_select's per-device workspace for rows longer than 33792 scores
+ *     (see there).  Calls on different streams touching disjoint outputs may
+ *     run concurrently.
  *   - Row formats (csa_fmt), for a row of D values:
  *       CSA_F32    4*D bytes, float32
  *       CSA_BF16   2*D bytes, bfloat16
@@ -67,10 +68,13 @@ typedef enum csa_fmt {
 } csa_fmt;
 
 typedef enum csa_variant {
-  CSA_VARIANT_AUTO = 0,     /* pick by the number of workgroups the batch gives */
-  CSA_VARIANT_HIGH_OCC = 1, /* one workgroup per (query, 16 heads): for a full GPU */
-  CSA_VARIANT_LOW_OCC = 2   /* also split the output dims over workgroups: for an
-                               under-filled GPU.  All variants give the same bits. */
+  CSA_VARIANT_AUTO = 0,     /* the fewest workgroups per (query, 16 heads) -- 2, 4
+                               or 8 -- that still give every CU one */
+  CSA_VARIANT_HIGH_OCC = 1, /* two workgroups per (query, 16 heads), 256 output
+                               dims each: for a batch that fills the GPU */
+  CSA_VARIANT_LOW_OCC = 2   /* eight, 64 output dims each: for a small batch.
+                               All variants give the same bits (the fp32 path
+                               has one kernel and ignores the variant). */
 } csa_variant;
 
 int csa_abi_version(void);
@@ -189,7 +193,10 @@ csa_status csa_compress_batch(const csa_compress_job* jobs /*[host]*/, int n_job
  *   key_off [nq] int64, q_pos [nq] int64
  *   scores  [nq, ld] float32
  * Supported: F32 any n_heads <= 64, d_idx <= 256; FP8 / MXFP4 with n_heads a
- * multiple of 16 (<= 128) and d_idx == 128.  Else UNSUPPORTED.
+ * multiple of 16 (<= 128) and d_idx == 128.  Else UNSUPPORTED.  FP8 batches
+ * of 1024 queries or more (prefill chunks) run a kernel in which four
+ * queries with the same key_off share each load of their keys; a score has
+ * the same bits from either kernel.
  * Errors: INVALID_ARG for ld < 1 or ld > 2^24 (16.7M entries, 64M tokens at
  * m = 4), m < 1, nq < 0, null pointers, a format other than the three above.
  */
