@@ -19,6 +19,10 @@
 //  * MXFP4 keys: scaled FP4 MFMA (E2M1 x E2M1 with per-32 E8M0 scales), whose
 //    result is exact for these operands.
 //  * F32: plain fp32 FMAs in dim order.
+// Prefill batches (1024 queries or more, FP8) run a shared-key kernel: four
+// queries of one sequence per workgroup, each key group loaded and widened
+// once into LDS and multiplied by every wave against its own query, with the
+// streaming kernel's operands, tiles and head sum (the same bits).
 // The dims of one 128-dim vector are assigned to k-steps so that each lane
 // reads 32 contiguous bytes; the same permutation is applied to queries and
 // keys, so each dot product is the same sum.  The MFMA output is heads x
