@@ -169,7 +169,11 @@ def test_compress_batch_matches_single_calls(n_jobs):
     (csa.F32, 4, 64, [2048, 777, 5]),
     (csa.FP8, 64, 128, [65536, 4099, 1000, 3]),
     (csa.FP8, 16, 128, [5000]),
+    (csa.FP8, 128, 128, [20000, 70]),
     (csa.MXFP4, 64, 128, [40000, 1024, 9]),
+    (csa.MXFP4, 32, 128, [9000, 300]),
+    (csa.MXFP4, 16, 128, [3000]),
+    (csa.F32, 64, 256, [1500, 64]),
 ])
 def test_indexer_matches_oracle(fmt, H_I, d_I, lengths):
     inp = synth.decode_inputs(21, lengths, m=4, H=16, D=128 if fmt == csa.F32 else 512, R=64,
@@ -221,7 +225,7 @@ def test_indexer_long_contexts(fmt):
         assert np.all(got[b, N:] == -7.0), "scores past N must stay untouched"
 
 
-@pytest.mark.parametrize("H_I", [64, 32])
+@pytest.mark.parametrize("H_I", [64, 32, 16, 128])
 def test_indexer_shared_keys_match_streaming_bits(H_I):
     """Large batches take the shared-key kernel (a workgroup multiplies one
     loaded key group against four queries of the same sequence).  Its scores
