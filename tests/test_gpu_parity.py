@@ -395,3 +395,24 @@ def test_attn_decode_matches_oracle(cfg, lengths, csa_mode):
             assert_f32_close(got[b], ref, what=f"{cfg} b{b}")
         else:
             assert_lowp_close(got[b], ref, what=f"{cfg} b{b}")
+
+
+@pytest.mark.parametrize("H,csa_mode,k", [(16, True, 512), (128, True, 1024), (32, False, 0)])
+def test_attn_decode_head_counts(H, csa_mode, k):
+    """The MFMA path at other query-head counts (tiles of 16 heads), CSA with
+    top-512 / top-1024 and HCA, in every variant (same bits)."""
+    m = 4 if csa_mode else 128
+    lengths = [40000, 3000, 130] if csa_mode else [262144, 5000]
+    inp = synth.decode_inputs(46 + H, lengths, m=m, H=H, D=512, R=64, n_win=128, kv_fmt=csa.SPLIT,
+                              q_fmt=csa.BF16, win_fmt=csa.BF16, csa=False, k=max(k, 1))
+    sel = synth.random_selection(np.random.default_rng(47), inp.n_ent, k) if csa_mode else None
+    idx_t = dev(sel) if sel is not None else None
+    out, bufs = run_decode(inp, idx_t)
+    got = decode_out(out, csa.BF16, inp.B, H, 512)
+    for b in range(inp.B):
+        s = sel[b][sel[b] >= 0] if sel is not None else None
+        assert_lowp_close(got[b], oracle_decode_query(inp, b, s), what=f"H={H} b{b}")
+    base = out.cpu().numpy()
+    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+        o2, _ = run_decode(inp, idx_t, v, bufs)
+        assert np.array_equal(o2.cpu().numpy(), base), f"H={H}: variant {v} changed the bits"
