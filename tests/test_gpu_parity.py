@@ -416,3 +416,49 @@ def test_attn_decode_head_counts(H, csa_mode, k):
     for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
         o2, _ = run_decode(inp, idx_t, v, bufs)
         assert np.array_equal(o2.cpu().numpy(), base), f"H={H}: variant {v} changed the bits"
+
+
+def test_degenerate_queries_and_empty_calls():
+    """Queries with no visible entry (positions below m - 1: window only),
+    one entry, and a partial first group, through indexer -> top-k ->
+    attention against the oracle; then every entry point with an empty batch,
+    which must enqueue nothing and write nothing."""
+    m, H, D, R, k = 4, 16, 512, 64, 64
+    lengths = [1, 3, 4, 5, 129]                       # N = 0, 0, 1, 1, 32
+    inp = synth.decode_inputs(91, lengths, m=m, H=H, D=D, R=R, n_win=128, kv_fmt=csa.SPLIT,
+                              q_fmt=csa.BF16, win_fmt=csa.BF16, csa=True, k=k, H_I=64, d_I=128)
+    B = inp.B
+    ld = max(1, int(inp.n_ent.max()))
+    scores = torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(dev(inp.q_idx), dev(inp.w), B, 64, 128, dev(inp.keys), csa.FP8, dev(inp.kv_off),
+                      dev(inp.q_pos), m, scores, ld)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(scores, ld, B, dev(inp.n_ent), k, idx)
+    got_s, got_i = scores.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        N = int(inp.n_ent[b])
+        assert np.all(got_s[b, N:] == -7.0)
+        if N:
+            ref = oracle_scores(inp, b)
+            assert np.abs(got_s[b, :N] - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+        assert np.array_equal(np.sort(got_i[b][got_i[b] >= 0]), np.arange(N)), "N <= k keeps every entry"
+        assert np.all(got_i[b, N:] == -1)
+    out, _ = run_decode(inp, idx)
+    got = decode_out(out, csa.BF16, B, H, D)
+    for b in range(B):
+        sel = got_i[b][got_i[b] >= 0]
+        assert_lowp_close(got[b], oracle_decode_query(inp, b, sel), what=f"length {lengths[b]}")
+    # empty calls: nothing written
+    sentinel = torch.full((4,), -3.0, dtype=torch.float32, device=DEV)
+    e64 = torch.zeros(0, dtype=torch.int64, device=DEV)
+    csa.indexer_score(dev(inp.q_idx), dev(inp.w), 0, 64, 128, dev(inp.keys), csa.FP8, e64, e64, m, sentinel, 1)
+    csa.topk_select(sentinel, 1, 0, None, 4, torch.zeros(0, dtype=torch.int32, device=DEV))
+    obuf = torch.full((64,), 0x5a, dtype=torch.uint8, device=DEV)
+    csa.hybrid_attn_decode(dev(inp.q), csa.BF16, 0, H, D, e64, None, EPS, R, ROPE_BASE, dev(inp.kv), csa.SPLIT,
+                           e64, m, None, 0, dev(inp.win), csa.BF16, 128,
+                           torch.zeros(0, dtype=torch.int32, device=DEV), dev(inp.sinks), inp.scale, obuf, csa.BF16)
+    csa.csa_compress(torch.zeros(4, device=DEV), csa.F32, torch.zeros(1, device=DEV), 1, 0, 4, 1, 1,
+                     torch.zeros(2, dtype=torch.int64, device=DEV), e64.new_zeros(1), e64.new_zeros(1),
+                     0, None, EPS, 0, ROPE_BASE, obuf, csa.F32)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == -3.0) and torch.all(obuf == 0x5a)
