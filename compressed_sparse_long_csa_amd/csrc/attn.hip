@@ -14,20 +14,25 @@
 //  * attn_f32_kernel -- everything float32 (reference-precision path): one
 //    wave per (query, head), entries in list order, exact-order wave sums.
 //  * attn_mfma_kernel -- q BF16, cache SPLIT (448 FP8 dims + 64 BF16 RoPE
-//    dims, D = 512), window BF16, out BF16.  One workgroup (4 waves) per
-//    (query, 16-head tile, slice of the output dims).  Entries stream through
-//    LDS in tiles of 64: every wave computes the logits of 16 entries of the
-//    tile for the 16 heads, the tile max / sum are combined across the 4 waves
-//    in a fixed order, and each wave accumulates P.V for its own output dims.
-//    Tiles arrive in LDS as the raw stored rows through direct global->LDS
-//    loads, double-buffered.  Logits use BF16 MFMA (FP8 -> BF16 is exact; FP8
-//    MFMA accumulation is too coarse for logits, whose sum cancels).  For
-//    P.V the 448 FP8 dims multiply the raw bytes on FP8 MFMA with the
-//    probabilities split into an FP8 high part and an FP8 residual (~8
-//    significant bits); the RoPE dims and the window use BF16 MFMA.  V
-//    operands are read transposed from the row-major tile with
+//    dims, D = 512), window BF16, out BF16.  One workgroup of 8 waves (two
+//    per SIMD) per (query, 16-head tile, slice of the output dims: DVS = 2,
+//    4 or 8 workgroups share a tile, 512 / DVS dims each).  The prologue
+//    normalises and rotates the tile's 16 query heads once (each wave two
+//    heads, shared through LDS).  Each wave then owns a fixed interleaved
+//    part of the attended list -- list positions [128 s + 16 w, +16) of the
+//    compressed entries in its step s, then window rows [64 t + 8 w, +8) --
+//    streams those rows into its own double-buffered LDS with direct
+//    global->LDS loads (one instruction per row), and keeps its own online
+//    softmax state (log2 domain; the sink enters through wave 0); there is no
+//    workgroup barrier in the entry loop.  At the end the eight waves' states
+//    are merged in wave order.  Logits use BF16 MFMA on the exactly widened
+//    FP8 rows (FP8 MFMA accumulation is too coarse for logits, whose sum
+//    cancels).  For P.V the 448 FP8 dims multiply the raw bytes on FP8 MFMA
+//    with the probabilities split into an FP8 high part and an FP8 residual
+//    (~8 significant bits); the RoPE dims and the window use BF16 MFMA.  V
+//    operands are read transposed from the row-major step buffer with
 //    ds_read_tr8 / ds_read_tr16.
-//    Every variant runs the same per-tile instruction sequence for a given
+//    Every variant runs the same per-step instruction sequence for a given
 //    (query, head); variants only change which workgroup owns which output
 //    dims, so the output bits are the same.
 #include "kernels.hpp"
