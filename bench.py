@@ -25,7 +25,9 @@ launches on its stream; `kernels` gives every kernel's duration, algorithmic
 bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
 float64 oracle on a bounded sample on the host.  `context_scan` repeats the
 step at 256K and 1M tokens per sequence; `hca_decode` the HCA decode step
-(32 x 262,144 tokens, every compressed entry attended); `prefill` the CSA prefill
+(32 x 262,144 tokens, every compressed entry attended); `ragged` a CSA layer
+(MXFP4 indexer, top-1,024) and an HCA layer over 64 sequences of 1K to 1M
+tokens; `prefill` the CSA prefill
 chunk (2,048 tokens after 131,072 cached: compress, indexer, top-k 1,024,
 prefill attention) and the contractions' MFMA rates.  `--copy-probe MIB` only
 runs a plain copy of known size, the reference for rocprofv3 byte counters.
@@ -487,6 +489,89 @@ def hca_leg(steps, warmup):
     return res
 
 
+RAGGED = "ragged_csa_hca_b64_ctx1k_1m"
+
+
+def ragged_leg(steps, warmup):
+    """The ragged workload: 64 sequences with lengths log-uniform in [1K, 1M]
+    tokens (seeded), one CSA layer (m = 4, MXFP4 indexer 64 x 128, top-1,024)
+    and one HCA layer (m' = 128, every entry) per step.  CSA layer =
+    csa_compress_batch (KV entry, MXFP4 key, window row) + indexer_score +
+    topk_select + hybrid_attn_decode; HCA layer = csa_compress_batch (KV entry,
+    window row) + hybrid_attn_decode; both captured in one graph.  The CSA
+    state alone exceeds 600 MB, so it is not replicated.  Reports ms per step
+    (both layers), query-tokens/s and each kernel's time, and the MXFP4
+    indexer's algorithmic HBM rate."""
+    c = synth.WORKLOADS[RAGGED]
+    B, m, mh, H, D, R, n_win, k = c["B"], c["m"], c["m_hca"], c["H"], c["D"], c["R"], c["n_win"], c["k"]
+    H_I, d_I = c["H_I"], c["d_I"]
+    lengths = synth.log_uniform_lengths(synth.rng_for(c["seed"]), B, c["Lmin"], c["Lmax"])
+    dc = synth.device_decode_inputs(c["seed"] + 4000, lengths, m=m, H=H, D=D, R=R, n_win=n_win, csa=True,
+                                    k=k, idx_fmt=csa.MXFP4, H_I=H_I, d_I=d_I)
+    dh = synth.device_decode_inputs(c["seed"] + 4001, lengths, m=mh, H=H, D=D, R=R, n_win=n_win, csa=False)
+    gen = synth.device_generator(c["seed"] + 4002)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)  # noqa: E731
+    tc = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int64), device="cuda")  # noqa: E731
+
+    def layer(d, mm, with_index):
+        n_ent, kv_off, q_pos, win_len = d["n_ent"], d["kv_off"], d["q_pos"], d["win_len"]
+        st = dict(kv_tok=rnd(B * mm, D).to(torch.bfloat16), kv_gate=rnd(B * mm, 1),
+                  key_tok=rnd(B * mm, d_I).to(torch.bfloat16), key_gate=rnd(B * mm, 1),
+                  win_tok=rnd(B, D).to(torch.bfloat16), win_gate=torch.zeros((B, 1), device="cuda"),
+                  seg_off=tc(np.arange(B + 1) * mm), seg_pos0=tc((n_ent - 1) * mm), seg_row=tc(kv_off + n_ent - 1),
+                  wseg_off=tc(np.arange(B + 1)), wpos0=tc(q_pos), wrow=tc(np.arange(B) * n_win + win_len - 1),
+                  q_pos=tc(q_pos), kv_off=tc(kv_off), n_valid=tc(n_ent), win_len=torch.as_tensor(win_len, device="cuda"))
+
+        def job(x, gate, DD, m_, off, pos0, rows, normalize, R_, dst, fmt):
+            return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=B * m_, D=DD, m=m_, nseg=B,
+                        seg_tok_off=off, seg_pos0=pos0, seg_out_row=rows, normalize=normalize, norm_w=None,
+                        eps=EPS, rope_dim=R_, rope_base=BASE, out=dst, out_fmt=fmt)
+        jobs = [job(st["kv_tok"], st["kv_gate"], D, mm, st["seg_off"], st["seg_pos0"], st["seg_row"], 1, R,
+                    d["kv"], csa.SPLIT),
+                job(st["win_tok"], st["win_gate"], D, 1, st["wseg_off"], st["wpos0"], st["wrow"], 1, R,
+                    d["win"], csa.BF16)]
+        ld = int(n_ent.max())
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+        kern = []
+        if with_index:
+            jobs.insert(1, job(st["key_tok"], st["key_gate"], d_I, mm, st["seg_off"], st["seg_pos0"], st["seg_row"],
+                               0, 0, d["keys"], csa.MXFP4))
+            scores = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+            idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+            kern = [("indexer_score", lambda: csa.indexer_score(d["q_idx"], d["w"], B, H_I, d_I, d["keys"], csa.MXFP4,
+                                                                 st["kv_off"], st["q_pos"], mm, scores, ld, check=False)),
+                    ("topk_select", lambda: csa.topk_select(scores, ld, B, st["n_valid"], k, idx, None, check=False))]
+        else:
+            idx = None
+        pre = "csa" if with_index else "hca"
+        kern = ([(pre + "_compress_batch", lambda: csa.csa_compress_batch(jobs, check=False))] + kern +
+                [(pre + "_attn_decode", lambda: csa.hybrid_attn_decode(
+                    d["q"], csa.BF16, B, H, D, st["q_pos"], None, EPS, R, BASE, d["kv"], csa.SPLIT, st["kv_off"], mm,
+                    idx, k if with_index else 0, d["win"], csa.BF16, n_win, st["win_len"], d["sinks"], d["scale"],
+                    out, csa.BF16, csa.VARIANT_AUTO, check=False))])
+        return kern
+    kern = layer(dc, m, True) + layer(dh, mh, False)
+
+    def step():
+        for _, f in kern:
+            f()
+    step()
+    torch.cuda.synchronize()
+    ms = time_graph([step], steps, warmup)
+    per_us, _ = time_kernels([kern], max(20, min(60, steps)))
+    n_ent = dc["n_ent"].astype(np.int64)
+    idx_bytes = int(n_ent.sum()) * (68 + 4) + B * H_I * (68 + 4)
+    res = {"workload": RAGGED, "lengths_min_median_max": [int(lengths.min()), int(np.median(lengths)),
+                                                          int(lengths.max())],
+           "ms_per_step": ms, "query_tokens_per_s": B / (ms * 1e-3),
+           "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
+           "mxfp4_indexer_gbps": idx_bytes / (per_us["indexer_score"] * 1e-6) / 1e9,
+           "mxfp4_indexer_hbm_frac": idx_bytes / (per_us["indexer_score"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    del dc, dh, kern
+    torch.cuda.empty_cache()
+    return res
+
+
 PREFILL = "csa_prefill_ctx131072_chunk2048"
 
 
@@ -588,6 +673,8 @@ def main():
                     help="skip the same step at 256K and 1M contexts")
     ap.add_argument("--no-hca", action="store_true",
                     help="skip the HCA decode step (32 sequences of 262,144 tokens)")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged CSA (MXFP4) + HCA step (64 sequences, 1K to 1M tokens)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the CSA prefill chunk (2,048 tokens after 131,072)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -664,6 +751,8 @@ def main():
         line["context_scan"] = context_scan([262144, 1048576], args.steps, args.warmup)
     if not args.no_hca:
         line["hca_decode"] = hca_leg(args.steps, args.warmup)
+    if not args.no_ragged:
+        line["ragged"] = ragged_leg(args.steps, args.warmup)
     if not args.no_prefill:
         line["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:
