@@ -1,14 +1,17 @@
 """Benchmark of the CSA decode hot path on one MI355X.
 
 One step = one decode token for each of the B sequences through the whole
-path, every kernel from libcsa:
-  1. csa_compress_batch -- one launch of three compress jobs: fold the newest
-                      block of m tokens of every sequence into its cache entry
-                      (split FP8/BF16 row, RMSNorm, RoPE), the matching indexer
-                      key (FP8), and the new token's sliding-window row (m = 1)
-  2. indexer_score -- ReLU multi-head scores over every visible entry
-  3. topk_select   -- the k best entries, ascending
-  4. hybrid_attn_decode -- sink MQA over the selected entries + window
+path, every kernel from libcsa, in three launches:
+  1. csa_compress_score -- three compress jobs (fold the newest block of m
+                      tokens of every sequence into its cache entry: split
+                      FP8/BF16 row, RMSNorm, RoPE; the matching indexer key,
+                      FP8; the new token's sliding-window row, m = 1) and the
+                      ReLU multi-head indexer scores over every visible entry,
+                      the new keys scored by the workgroups that write them
+  2. topk_select   -- the k best entries, ascending
+  3. hybrid_attn_decode -- sink MQA over the selected entries + window
+`four_launches` times the same step with csa_compress_batch and
+indexer_score as two launches.
 Inputs are seeded synthetic tensors already resident in HBM.  The per-layer
 state a step reads (KV cache, index keys, window rows) exists in R copies
 (default 13, about 2.4 GB) stepped in turn, so that it cannot stay in the
@@ -19,9 +22,9 @@ steps, then exactly K timed steps between two synchronised events.  The workload
 sequences of 65,536 tokens (16,384 compressed entries each, top-k 512, FP8
 indexer 64 x 128, 64 query heads, head dim 512).
 
-Prints one JSON line.  `roofline` is measured for the dominant kernel
-(indexer_score, which moves most of the step's bytes) with events around its
-launches on its stream; `kernels` gives every kernel's duration, algorithmic
+Prints one JSON line.  `roofline` is measured for the dominant launch
+(csa_compress_score, whose indexer part moves most of the step's bytes) with
+events around its launches on its stream; `kernels` gives every kernel's duration, algorithmic
 bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
 float64 oracle on a bounded sample on the host.  `context_scan` repeats the
 step at 256K and 1M tokens per sequence; `hca_decode` the HCA decode step
@@ -140,7 +143,7 @@ def make_replicas(W, R):
     return reps
 
 
-def make_step(W, check=False):
+def make_step(W, check=False, fused=True):
     c, inp = W["c"], W["inp"]
     B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
 
@@ -159,6 +162,10 @@ def make_step(W, check=False):
     def k_compress():
         csa.csa_compress_batch(jobs, check=check)
 
+    def k_compress_score():
+        csa.csa_compress_score(jobs, W["q_idx"], W["w"], B, c["H_I"], d_I, W["keys"], csa.FP8, W["kv_off"],
+                               W["q_pos"], m, W["scores"], W["ld"], check=check)
+
     def k_indexer():
         csa.indexer_score(W["q_idx"], W["w"], B, c["H_I"], d_I, W["keys"], csa.FP8, W["kv_off"],
                           W["q_pos"], m, W["scores"], W["ld"], check=check)
@@ -172,8 +179,12 @@ def make_step(W, check=False):
                                inp.n_win, W["win_len"], W["sinks"], inp.scale, W["out"], csa.BF16,
                                csa.VARIANT_AUTO, check=check)
 
-    kernels = [("csa_compress_batch", k_compress), ("indexer_score", k_indexer),
-               ("topk_select", k_topk), ("hybrid_attn_decode", k_attn)]
+    if fused:
+        kernels = [("csa_compress_score", k_compress_score), ("topk_select", k_topk),
+                   ("hybrid_attn_decode", k_attn)]
+    else:
+        kernels = [("csa_compress_batch", k_compress), ("indexer_score", k_indexer),
+                   ("topk_select", k_topk), ("hybrid_attn_decode", k_attn)]
 
     def step():
         for _, f in kernels:
@@ -198,6 +209,7 @@ def algorithmic_bytes(W):
         "hybrid_attn_decode": int((sel * split).sum()) + int(inp.win_len.sum()) * 2 * D
         + B * k * 4 + B * H * D * 2 * 2 + H * 4,
     }
+    per_kernel["csa_compress_score"] = per_kernel["csa_compress_batch"] + per_kernel["indexer_score"]
     step_bytes = (int((N * d_I).sum()) + B * c["H_I"] * (d_I + 4) + int((sel * split).sum())
                   + int(inp.win_len.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4)
     return step_bytes, per_kernel
@@ -208,7 +220,8 @@ def algorithmic_flops(W):
     inp, c = W["inp"], W["c"]
     N = inp.n_ent.astype(np.int64)
     sel = np.minimum(c["k"], N) + inp.win_len.astype(np.int64)
-    return {"indexer_score": int(2 * N.sum() * c["H_I"] * W["d_I"]),
+    idx = int(2 * N.sum() * c["H_I"] * W["d_I"])
+    return {"indexer_score": idx, "csa_compress_score": idx,
             "hybrid_attn_decode": int(2 * 2 * sel.sum() * c["H"] * W["D"])}
 
 
@@ -376,14 +389,14 @@ def cpu_baseline(W, budget_s=12.0):
 
 def traffic_record(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (null otherwise)."""
+    taken on the current kernel sources (null otherwise)."""
+    from compressed_sparse_long_csa_amd.profiling import sources_sha256
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    src = os.path.join(ROOT, "compressed_sparse_long_csa_amd", "csrc", "indexer.hip")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()
+        srcs = rec["source"] if isinstance(rec["source"], list) else [rec["source"]]
+        h = sources_sha256([os.path.join(ROOT, p) for p in srcs])
         return rec["bytes_per_launch"] if rec.get("source_sha256") == h else None
     except Exception:
         return None
@@ -408,11 +421,11 @@ def context_scan(contexts, steps, warmup):
         torch.cuda.synchronize()
         ms = time_graph([m[0] for m in made], steps, warmup)
         per_us, _ = time_kernels([m[1] for m in made], max(20, min(60, steps)))
-        idx_gbps = kbytes["indexer_score"] / (per_us["indexer_score"] * 1e-6) / 1e9
+        idx_gbps = kbytes["csa_compress_score"] / (per_us["csa_compress_score"] * 1e-6) / 1e9
         rows.append({"context": L, "ms_per_step": ms, "query_tokens_per_s": W["B"] / (ms * 1e-3),
                      "step_hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
                      "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
-                     "indexer_gbps": idx_gbps, "indexer_hbm_frac": idx_gbps / HBM_PEAK_GBPS,
+                     "compress_score_gbps": idx_gbps, "compress_score_hbm_frac": idx_gbps / HBM_PEAK_GBPS,
                      "state_replicas": n_rep})
         del W, reps, made
         torch.cuda.empty_cache()
@@ -705,20 +718,29 @@ def main():
     ms_warm = time_graph([made[0][0]], args.steps, args.warmup)
     ms = time_graph([m[0] for m in made], args.steps, args.warmup)
     per_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)))
+    # the same step as four launches (compress, then the indexer), for comparison
+    made4 = [make_step(Wr, check=False, fused=False) for Wr in reps]
+    ms4 = time_graph([m[0] for m in made4], args.steps, args.warmup)
+    per_us4, _ = time_kernels([m[1] for m in made4], max(20, min(100, args.steps)))
     made[0][0]()                             # replica 0 last, for the spot check
     torch.cuda.synchronize()
     step_bytes, kbytes = algorithmic_bytes(W)
     err = spot_check(W)
     B = W["B"]
-    dom = "indexer_score"                    # the kernel that moves most of the step's bytes
+    dom = "csa_compress_score"               # the launch that moves most of the step's bytes
     flops = algorithmic_flops(W)
-    kern = {}
-    for n in per_us:
-        t = per_us[n] * 1e-6
-        kern[n] = {"us": per_us[n], "bytes": kbytes[n], "gbps": kbytes[n] / t / 1e9,
-                   "hbm_frac": kbytes[n] / t / 1e9 / HBM_PEAK_GBPS}
-        if n in flops:
-            kern[n].update({"tflops": flops[n] / t / 1e12, "mfma_frac": flops[n] / t / 1e12 / BF16_PEAK_TFLOPS})
+
+    def table(us):
+        kern = {}
+        for n in us:
+            t = us[n] * 1e-6
+            kern[n] = {"us": us[n], "bytes": kbytes[n], "gbps": kbytes[n] / t / 1e9,
+                       "hbm_frac": kbytes[n] / t / 1e9 / HBM_PEAK_GBPS}
+            if n in flops:
+                kern[n].update({"tflops": flops[n] / t / 1e12,
+                                "mfma_frac": flops[n] / t / 1e12 / BF16_PEAK_TFLOPS})
+        return kern
+    kern = table(per_us)
     ach = kern[dom]["gbps"]
     line = {
         "metric": METRIC,
@@ -743,6 +765,8 @@ def main():
                      "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_record(dom),
                      "kernel": dom, "bytes_per_launch": kbytes[dom], "us_per_launch": per_us[dom]},
         "kernels": kern,
+        "four_launches": {"ms_per_step": ms4, "query_tokens_per_s": B / (ms4 * 1e-3),
+                          "kernels": table(per_us4)},
         "event_pair_floor_us": event_floor_us,
         "copy_probe_gbps": copy_gbps(),
         "check_max_err_over_rms": err,

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
-           "csa_compress", "csa_compress_batch", "indexer_score", "topk_select", "hybrid_attn_decode",
-           "hybrid_attn_prefill")
+           "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score", "topk_select",
+           "hybrid_attn_decode", "hybrid_attn_prefill")
 
 _lib = None
 
@@ -53,6 +53,9 @@ def load_library():
     lib.csa_compress.argtypes = [P, I, P, I, I64, I, I, I, P, P, P, I, P, F, I, F, P, I, P]
     lib.csa_compress_batch.restype = I
     lib.csa_compress_batch.argtypes = [ctypes.POINTER(CompressJob), I, P]
+    lib.csa_compress_score.restype = I
+    lib.csa_compress_score.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, P, P, I, P,
+                                       I64, P]
     lib.indexer_score.restype = I
     lib.indexer_score.argtypes = [P, P, I, I, I, P, I, P, P, I, P, I64, P]
     lib.topk_select.restype = I
@@ -157,9 +160,7 @@ COMPRESS_JOB_FIELDS = ("x", "x_fmt", "gate", "gate_cols", "n_tok", "D", "m", "ns
 MAX_COMPRESS_JOBS = 4
 
 
-def csa_compress_batch(jobs, stream=None, check=True):
-    """jobs: sequence of dicts with csa_compress's arguments (COMPRESS_JOB_FIELDS)."""
-    lib = load_library()
+def _job_array(jobs, check):
     arr = (CompressJob * max(1, len(jobs)))()
     for i, j in enumerate(jobs):
         _compress_checks(j["x"], j["x_fmt"], j["gate"], j["gate_cols"], j["n_tok"], j["D"], j["m"],
@@ -173,12 +174,34 @@ def csa_compress_batch(jobs, stream=None, check=True):
             elif v is None:
                 v = None
             setattr(c, f, int(v) if f == "normalize" else v)
-    _check(lib.csa_compress_batch(arr, len(jobs), _stream(stream)))
+    return arr
+
+
+def csa_compress_batch(jobs, stream=None, check=True):
+    """jobs: sequence of dicts with csa_compress's arguments (COMPRESS_JOB_FIELDS)."""
+    lib = load_library()
+    _check(lib.csa_compress_batch(_job_array(jobs, check), len(jobs), _stream(stream)))
+
+
+def csa_compress_score(jobs, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld,
+                       stream=None, check=True):
+    """csa_compress_batch(jobs) then indexer_score(...), in one launch where it can."""
+    lib = load_library()
+    arr = _job_array(jobs, check)
+    _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check)
+    _check(lib.csa_compress_score(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(keys), fmt,
+                                  _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
 def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld,
                   stream=None, check=True):
     lib = load_library()
+    _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check)
+    _check(lib.indexer_score(_ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(keys), fmt,
+                             _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
+
+
+def _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check):
     rb = row_bytes(fmt, d_idx)
     _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
     _need(w, "w", torch.float32, min_numel=nq * n_heads)
@@ -192,8 +215,6 @@ def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, sc
         end = _host(key_off)[:nq] + N
         if int(_host(key_off)[:nq].min()) < 0 or int(end.max()) * rb > keys.numel() * keys.element_size():
             raise ValueError("a query's visible keys run past the end of `keys`")
-    _check(lib.indexer_score(_ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(keys), fmt,
-                             _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
 def topk_select(scores, ld, nq, n_valid, k, idx, top_scores=None, stream=None, check=True):

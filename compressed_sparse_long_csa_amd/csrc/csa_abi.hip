@@ -131,54 +131,132 @@ csa_status csa_compress(const void* x, csa_fmt x_fmt, const float* gate, int gat
   return launched(launch_compress(a, stream), "csa_compress");
 }
 
+}  // extern "C"
+
+namespace {
+csa_status batch_args(const char* what, const csa_compress_job* jobs, int n_jobs, int key,
+                      CompressArgs* a, int* n, int* map_key);
+}  // namespace
+
+extern "C" {
+
 csa_status csa_compress_batch(const csa_compress_job* jobs, int n_jobs, hipStream_t stream) {
-  if (n_jobs < 0 || n_jobs > CSA_COMPRESS_MAX_JOBS)
-    return fail(CSA_ERR_INVALID_ARG, "csa_compress_batch: n_jobs must be in [0, %d]",
-                CSA_COMPRESS_MAX_JOBS);
-  if (n_jobs > 0 && !jobs) return fail(CSA_ERR_INVALID_ARG, "csa_compress_batch: null jobs");
   CompressArgs a[CSA_COMPRESS_MAX_JOBS];
-  int n = 0;
-  for (int i = 0; i < n_jobs; ++i) {
-    const csa_compress_job& j = jobs[i];
-    char what[48];
-    snprintf(what, sizeof(what), "csa_compress_batch: job %d", i);
-    bool empty = false;
-    const csa_status st = compress_args(what, j.x, j.x_fmt, j.gate, j.gate_cols, j.n_tok, j.D, j.m,
-                                        j.nseg, j.seg_tok_off, j.seg_pos0, j.seg_out_row,
-                                        j.normalize, j.norm_w, j.eps, j.rope_dim, j.rope_base,
-                                        j.out, j.out_fmt, &a[n], &empty);
-    if (st != CSA_OK) return st;
-    if (!empty) ++n;
-  }
+  int n = 0, unused = -1;
+  const csa_status st = batch_args("csa_compress_batch", jobs, n_jobs, -1, a, &n, &unused);
+  if (st != CSA_OK) return st;
   if (n == 0) { g_err[0] = '\0'; return CSA_OK; }
   return launched(launch_compress_jobs(a, n, stream), "csa_compress_batch");
 }
+
+}  // extern "C"
+
+namespace {
+// Argument checks of one indexer call; `empty` is set for nq == 0.
+csa_status indexer_args(const char* what, const void* q_idx, const float* w, int nq, int n_heads,
+                        int d_idx, const void* keys, csa_fmt fmt, const int64_t* key_off,
+                        const int64_t* q_pos, int m, float* scores, int64_t ld, IndexerArgs* a,
+                        bool* empty) {
+  *empty = false;
+  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "%s: nq < 0", what);
+  if (n_heads < 1 || d_idx < 1) return fail(CSA_ERR_INVALID_ARG, "%s: n_heads, d_idx must be >= 1", what);
+  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "%s: m must be >= 1", what);
+  if (ld < 1 || ld > (int64_t{1} << 24))
+    return fail(CSA_ERR_INVALID_ARG, "%s: ld must be in [1, 2^24]", what);
+  if (fmt != CSA_F32 && fmt != CSA_FP8 && fmt != CSA_MXFP4)
+    return fail(CSA_ERR_INVALID_ARG, "%s: fmt must be CSA_F32, CSA_FP8 or CSA_MXFP4", what);
+  if (fmt == CSA_F32) {
+    if (n_heads > 64 || d_idx > 256)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: F32 path supports n_heads <= 64, d_idx <= 256", what);
+  } else {
+    if (d_idx != 128 || n_heads % 16 != 0 || n_heads > 128)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: FP8/MXFP4 paths need d_idx == 128 and n_heads in {16,32,64,128}", what);
+    if (n_heads == 48 || n_heads == 80 || n_heads == 96 || n_heads == 112)
+      return fail(CSA_ERR_UNSUPPORTED, "%s: n_heads must be 16, 32, 64 or 128", what);
+  }
+  if (nq == 0) { *empty = true; return CSA_OK; }
+  if (!q_idx || !w || !keys || !key_off || !q_pos || !scores)
+    return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", what);
+  *a = IndexerArgs{q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld};
+  return CSA_OK;
+}
+
+// Checks of a csa_compress_batch job list; the non-empty jobs go to a[0 .. *n).
+// *map_key receives the index in a[] of the input job `key` (-1 if it is empty).
+csa_status batch_args(const char* what, const csa_compress_job* jobs, int n_jobs, int key,
+                      CompressArgs* a, int* n, int* map_key) {
+  if (n_jobs < 0 || n_jobs > CSA_COMPRESS_MAX_JOBS)
+    return fail(CSA_ERR_INVALID_ARG, "%s: n_jobs must be in [0, %d]", what, CSA_COMPRESS_MAX_JOBS);
+  if (n_jobs > 0 && !jobs) return fail(CSA_ERR_INVALID_ARG, "%s: null jobs", what);
+  *n = 0;
+  *map_key = -1;
+  for (int i = 0; i < n_jobs; ++i) {
+    const csa_compress_job& j = jobs[i];
+    char w[64];
+    snprintf(w, sizeof(w), "%s: job %d", what, i);
+    bool empty = false;
+    const csa_status st = compress_args(w, j.x, j.x_fmt, j.gate, j.gate_cols, j.n_tok, j.D, j.m,
+                                        j.nseg, j.seg_tok_off, j.seg_pos0, j.seg_out_row,
+                                        j.normalize, j.norm_w, j.eps, j.rope_dim, j.rope_base,
+                                        j.out, j.out_fmt, &a[*n], &empty);
+    if (st != CSA_OK) return st;
+    if (!empty) {
+      if (i == key) *map_key = *n;
+      ++*n;
+    }
+  }
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
 
 csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
                          const void* keys, csa_fmt fmt, const int64_t* key_off,
                          const int64_t* q_pos, int m, float* scores, int64_t ld,
                          hipStream_t stream) {
-  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "indexer_score: nq < 0");
-  if (n_heads < 1 || d_idx < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: n_heads, d_idx must be >= 1");
-  if (m < 1) return fail(CSA_ERR_INVALID_ARG, "indexer_score: m must be >= 1");
-  if (ld < 1 || ld > (int64_t{1} << 24))
-    return fail(CSA_ERR_INVALID_ARG, "indexer_score: ld must be in [1, 2^24]");
-  if (fmt != CSA_F32 && fmt != CSA_FP8 && fmt != CSA_MXFP4)
-    return fail(CSA_ERR_INVALID_ARG, "indexer_score: fmt must be CSA_F32, CSA_FP8 or CSA_MXFP4");
-  if (fmt == CSA_F32) {
-    if (n_heads > 64 || d_idx > 256)
-      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: F32 path supports n_heads <= 64, d_idx <= 256");
-  } else {
-    if (d_idx != 128 || n_heads % 16 != 0 || n_heads > 128)
-      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: FP8/MXFP4 paths need d_idx == 128 and n_heads in {16,32,64,128}");
-    if (n_heads == 48 || n_heads == 80 || n_heads == 96 || n_heads == 112)
-      return fail(CSA_ERR_UNSUPPORTED, "indexer_score: n_heads must be 16, 32, 64 or 128");
-  }
-  if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
-  if (!q_idx || !w || !keys || !key_off || !q_pos || !scores)
-    return fail(CSA_ERR_INVALID_ARG, "indexer_score: null pointer");
-  IndexerArgs a{q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld};
+  IndexerArgs a{};
+  bool empty = false;
+  const csa_status st = indexer_args("indexer_score", q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off,
+                                     q_pos, m, scores, ld, &a, &empty);
+  if (st != CSA_OK) return st;
+  if (empty) { g_err[0] = '\0'; return CSA_OK; }
   return launched(launch_indexer(a, stream), "indexer_score");
+}
+
+csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                              const float* w, int nq, int n_heads, int d_idx, const void* keys,
+                              csa_fmt fmt, const int64_t* key_off, const int64_t* q_pos, int m,
+                              float* scores, int64_t ld, hipStream_t stream) {
+  const char* what = "csa_compress_score";
+  IndexerArgs ia{};
+  bool no_queries = false;
+  csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores,
+                               ld, &ia, &no_queries);
+  if (st != CSA_OK) return st;
+  int key = -1;
+  if (n_jobs > 0 && jobs) {
+    for (int i = 0; i < n_jobs && i < CSA_COMPRESS_MAX_JOBS; ++i) {
+      if (!keys || jobs[i].out != keys) continue;
+      if (key >= 0) return fail(CSA_ERR_INVALID_ARG, "%s: jobs %d and %d both write `keys`", what, key, i);
+      key = i;
+    }
+  }
+  if (key >= 0 && !no_queries) {
+    const csa_compress_job& kjob = jobs[key];
+    if (kjob.out_fmt != fmt || kjob.D != d_idx || kjob.rope_dim != 0 || kjob.nseg != nq)
+      return fail(CSA_ERR_INVALID_ARG,
+                  "%s: job %d writes `keys`, so it needs out_fmt == fmt, D == d_idx, rope_dim == 0 "
+                  "and one segment per query (nseg == nq)", what, key);
+  }
+  CompressArgs a[CSA_COMPRESS_MAX_JOBS];
+  int n = 0, map_key = -1;
+  st = batch_args(what, jobs, n_jobs, key, a, &n, &map_key);
+  if (st != CSA_OK) return st;
+  hipError_t e = hipSuccess;
+  if (no_queries) e = n > 0 ? launch_compress_jobs(a, n, stream) : hipSuccess;
+  else e = launch_compress_score(a, n, map_key, ia, stream);
+  return launched(e, what);
 }
 
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,

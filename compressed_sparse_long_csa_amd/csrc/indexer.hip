@@ -28,7 +28,7 @@
 // keys, so each dot product is the same sum.  The MFMA output is heads x
 // keys, so the head sum runs inside a lane (a fixed tree over the lane's 16
 // heads) and then over the four row groups in a fixed order.
-#include "kernels.hpp"
+#include "compress_dev.hpp"
 
 namespace csa {
 
@@ -142,15 +142,29 @@ __device__ __forceinline__ void group_fp8(const uint4 (&kr)[4][2], const bf16x8 
   }
 }
 
-template <int NHB, bool IL>   // head blocks of 16; interleaved shares
-__global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
-                                                          int64_t n_chunk, int R) {
+// Key rows that the same launch writes (compress_score_kernel): segment i
+// of the key job holds query i's new tokens, and a row that job writes is,
+// for query i, its last visible row.  Its score is computed by the workgroup
+// that compresses it; the streaming waves store every other score.  nseg = 0
+// when the launch writes no key.
+struct NewKeys {
+  const int64_t* seg_tok_off;
+  const int64_t* seg_out_row;
+  int64_t n_tok;
+  int nseg;
+  int m;
+};
+
+// NB: groups in flight per wave (2; 3 where shares of three groups are common)
+template <int NHB, bool IL, bool kNew, int NB = 2>   // head blocks of 16; interleaved shares; keys written alongside
+__device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items, int64_t n_chunk, int R,
+                                          int64_t item0, int64_t item_step, const NewKeys& nk) {
   constexpr int H = NHB * 16;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
   const uint8_t* qall = static_cast<const uint8_t*>(a.q);
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+  for (int64_t item = item0; item < n_items; item += item_step) {
     // query i; item `chunk` holds four of the query's waves
     const int i = static_cast<int>(item / n_chunk);
     const int64_t chunk = item % n_chunk;
@@ -169,27 +183,50 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
       wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
     }
     const int64_t qpos = scalar_load(a.q_pos, i), koff = scalar_load(a.key_off, i);
-    asm volatile("" : : "s"(qpos), "s"(koff) : "memory");   // one round trip; the loads above stay above
+    int64_t lo = 0, hi = 0, row0 = 0;                  // query i's segment of the key job
+    if (kNew && i < nk.nseg) {
+      lo = scalar_load(nk.seg_tok_off, i);
+      hi = scalar_load(nk.seg_tok_off, i + 1);
+      row0 = scalar_load(nk.seg_out_row, i);
+    }
+    asm volatile("" : : "s"(qpos), "s"(koff), "s"(lo), "s"(hi), "s"(row0) : "memory");   // one round trip; the loads above stay above
     int64_t N = (uniform64(qpos) + 1) / a.m;
     if (N > a.ld) N = a.ld;
+    // scores this wave may store: all N, less the last when the launch
+    // compresses that row (the rule by which csa_compress places block j of
+    // a segment at row seg_out_row + j)
+    int64_t Ns = N;
+    if (kNew && N >= 1 && i < nk.nseg) {
+      const int64_t j = uniform64(koff) + N - 1 - uniform64(row0);
+      const int64_t end = uniform64(lo) + (j + 1) * nk.m;
+      if (j >= 0 && uniform64(lo) % nk.m == 0 && end <= uniform64(hi) && end <= nk.n_tok) Ns = N - 1;
+    }
     // (N <= 2^24, so group counts fit 32 bits)
     const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;                     // waves of this query
     const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);   // this wave's turn
     const uint32_t G = static_cast<uint32_t>((N + kGroupKeys - 1) / kGroupKeys);
     const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * 128,
                                   static_cast<uint32_t>(N * 128));
-    // the wave's groups: first, first + step, ...
-    const uint32_t first = IL ? wq : wq * static_cast<uint32_t>(R);
+    // the wave's groups: first, first + step, ...  Contiguous shares split
+    // the ld / 64 groups of a row as evenly as the W waves allow (at most R each)
+    const uint32_t Gp = static_cast<uint32_t>((a.ld + kGroupKeys - 1) / kGroupKeys);
+    const uint32_t first = IL ? wq : static_cast<uint32_t>(static_cast<uint64_t>(wq) * Gp / W);
     const uint32_t step = IL ? W : 1u;
     if (first >= G) continue;                            // uniform over the wave (no barriers)
-    const uint32_t mine = (G - first + step - 1u) / step;
+    uint32_t mine;
+    if (IL) {
+      mine = (G - first + step - 1u) / step;
+    } else {
+      const uint32_t end = static_cast<uint32_t>(static_cast<uint64_t>(wq + 1u) * Gp / W);
+      mine = (end < G ? end : G) - first;
+    }
     const int ng = mine < static_cast<uint32_t>(R) ? static_cast<int>(mine) : R;
     const uint32_t s0 = first * kGroupKeys;              // first key of the wave's first group
     const uint32_t stride = step * (kGroupKeys * 128u);
     const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * 128u + g * 32u;
-    uint4 ka[4][2], kb[4][2];
-    load_group_fp8(rs, voff0, stride, 0, ng, ka);
-    load_group_fp8(rs, voff0, stride, 1, ng, kb);
+    uint4 kr[NB][4][2];                                  // NB groups in flight
+#pragma unroll
+    for (int u = 0; u < NB; ++u) load_group_fp8(rs, voff0, stride, u, ng, kr[u]);
     // the query is used only from here on: its conversion must not be
     // scheduled above the key loads (it would wait for the query first)
 #pragma unroll
@@ -209,7 +246,7 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     }
     // scores: a descriptor over the query's N valid scores drops stores past
     // N; lanes other than row group 0 (which hold the same totals) aim past it
-    const buf_rsrc out_rs = make_rsrc(a.scores + static_cast<int64_t>(i) * a.ld, static_cast<uint32_t>(N * 4));
+    const buf_rsrc out_rs = make_rsrc(a.scores + static_cast<int64_t>(i) * a.ld, static_cast<uint32_t>(Ns * 4));
     const uint32_t out_off = g == 0 ? static_cast<uint32_t>(s0 + j16) * 4u : 0x80000000u;
     f32x4 cp[NHB];
     for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -217,16 +254,106 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
     const int out_stride = static_cast<int>(step * kGroupKeys * 4u);
     // groups in pairs, both always processed (a group past the wave's share
     // holds zeros and keeps no score)
-    for (int t = 0; t < ng; t += 2) {
-      group_fp8<NHB>(ka, qb, wr, cp, pend, t * out_stride, out_rs, out_off);
-      load_group_fp8(rs, voff0, stride, t + 2, ng, ka);
-      group_fp8<NHB>(kb, qb, wr, cp, pend, t + 1 < ng ? (t + 1) * out_stride : -1, out_rs, out_off);
-      load_group_fp8(rs, voff0, stride, t + 3, ng, kb);
+    for (int t = 0; t < ng; t += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        group_fp8<NHB>(kr[u], qb, wr, cp, pend, t + u < ng ? (t + u) * out_stride : -1, out_rs, out_off);
+        load_group_fp8(rs, voff0, stride, t + u + NB, ng, kr[u]);
+      }
     }
     const float tot = head_sum<NHB>(cp, wr);
     if (pend >= 0)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rs, static_cast<int>(out_off), pend, 0);
   }
+}
+
+template <int NHB, bool IL>
+__global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
+                                                          int64_t n_chunk, int R) {
+  fp8_items<NHB, IL, false>(a, n_items, n_chunk, R, blockIdx.x, gridDim.x, NewKeys{});
+}
+
+// Score of a key row the launch has just compressed (the FP8 rounding of
+// y[0 .. 128), as stored) for query s, when that row is the query's last
+// visible row.  Wave 0 repeats the streaming kernel's arithmetic for this one
+// key: the key sits in the MFMA column the streaming kernel gives it
+// ((N - 1) mod 16), with the same dim order, products, chain and head sum,
+// so the score has the same bits.
+template <int NHB>
+__device__ __forceinline__ void score_new_key(const IndexerArgs& a, const float* y, int s, int64_t row) {
+  constexpr int H = NHB * 16;
+  if (threadIdx.x >= 64 || s >= a.nq) return;          // wave 0; uniform
+  const int lane = threadIdx.x, g = lane >> 4, j16 = lane & 15;
+  const uint8_t* qall = static_cast<const uint8_t*>(a.q);
+  uint4 qraw[NHB][2];
+  float4 wraw[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const uint4* qp = reinterpret_cast<const uint4*>(qall + (static_cast<int64_t>(s) * H + hb * 16 + j16) * 128 + g * 32);
+    qraw[hb][0] = qp[0];
+    qraw[hb][1] = qp[1];
+    wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(s) * H + hb * 16 + g * 4);
+  }
+  const int64_t qpos = scalar_load(a.q_pos, s), koff = scalar_load(a.key_off, s);
+  int64_t N = (uniform64(qpos) + 1) / a.m;
+  if (N > a.ld) N = a.ld;
+  if (N < 1 || uniform64(koff) + N - 1 != row) return;
+  // lane (column j16, k-slot g) holds dims [32g + 8ks, +8) at k-step ks
+  bf16x8 kk[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint32_t w4[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w4[e >> 2] |= f32_to_e4m3(y[32 * g + 8 * ks + e]) << (8 * (e & 3));
+    kk[ks] = fp8x8_to_bf16(w4[0], w4[1]);
+  }
+  bf16x8 qb[NHB][4];
+  float wr[NHB][4];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    qb[hb][0] = fp8x8_to_bf16(qraw[hb][0].x, qraw[hb][0].y);
+    qb[hb][1] = fp8x8_to_bf16(qraw[hb][0].z, qraw[hb][0].w);
+    qb[hb][2] = fp8x8_to_bf16(qraw[hb][1].x, qraw[hb][1].y);
+    qb[hb][3] = fp8x8_to_bf16(qraw[hb][1].z, qraw[hb][1].w);
+    wr[hb][0] = wraw[hb].x; wr[hb][1] = wraw[hb].y; wr[hb][2] = wraw[hb].z; wr[hb][3] = wraw[hb].w;
+  }
+  f32x4 cc[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) cc[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+      cc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][ks], kk[ks], cc[hb], 0, 0, 0);
+  const float tot = head_sum<NHB>(cc, wr);
+  if (g == 0 && j16 == static_cast<int>((N - 1) & 15)) a.scores[static_cast<int64_t>(s) * a.ld + N - 1] = tot;
+}
+
+// A decode step's compress jobs and its indexer scores in one launch.
+// Workgroups [0, n_cwg) compress (the job kernel's loop over the jobs'
+// blocks); the workgroup of a new key row also scores it for the query whose
+// last visible row it is.  The rest stream every other score.  No workgroup
+// waits for another: a query's rows other than its last are not written by
+// the launch, and its last row is scored by exactly one side.
+template <int NHB, bool IL, bool kWithAny, int NB>
+__global__ void __launch_bounds__(256) compress_score_kernel(CompressJobs J, int key_job, NewKeys nk,
+                                                             IndexerArgs a, int64_t n_items, int64_t n_chunk,
+                                                             int R, int n_cwg) {
+  if (static_cast<int>(blockIdx.x) < n_cwg) {
+    extern __shared__ float y[];
+    __shared__ cmp::EntrySlot slot;
+    const int64_t total = J.blk0[J.n];
+    for (int64_t b = blockIdx.x; b < total; b += n_cwg) {
+      int j = 0;
+      while (j + 1 < J.n && b >= J.blk0[j + 1]) ++j;
+      const CompressArgs& c = J.a[j];
+      cmp::run_block<kWithAny>(c, J.kind[j], b - J.blk0[j], y, y + c.D, &slot);
+      if (j == key_job && slot.ok) score_new_key<NHB>(a, y, slot.seg, slot.row);
+      __syncthreads();                                  // y and slot are reused by the next block
+    }
+    return;
+  }
+  fp8_items<NHB, IL, true, NB>(a, n_items, n_chunk, R, blockIdx.x - n_cwg, gridDim.x - n_cwg, nk);
 }
 
 // --------------------------------------------------------------- FP8, d = 128, shared keys
@@ -531,7 +658,97 @@ __global__ void __launch_bounds__(256) indexer_f32_kernel(IndexerArgs a, int64_t
   a.scores[static_cast<int64_t>(i) * a.ld + s] = tot;
 }
 
+// Work split of the streaming kernels: enough 64-key groups per wave (the
+// share R) that one round of two waves per SIMD covers the batch, at least 2
+// (two groups in flight), at most 32; an item is four waves of one query.
+struct StreamPlan {
+  int64_t R, n_chunk, n_items;
+  unsigned grid;
+};
+
+StreamPlan plan_stream(const IndexerArgs& a) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  const int64_t groups = static_cast<int64_t>(a.nq) * ((a.ld + kGroupKeys - 1) / kGroupKeys);
+  const int64_t waves = static_cast<int64_t>(device_cu_count()) * 8;
+  int64_t R = (groups + waves - 1) / waves;
+  R = R < 2 ? 2 : (R > 32 ? 32 : R);
+  const int64_t item_keys = 4 * R * kGroupKeys;
+  const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
+  const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
+  return StreamPlan{R, n_chunk, n_items, static_cast<unsigned>(n_items < cap ? n_items : cap)};
+}
+
+static_assert(sizeof(CompressJobs) + sizeof(NewKeys) + sizeof(IndexerArgs) + 64 <= 4096,
+              "kernel arguments are limited to 4 KiB");
+
 }  // namespace
+
+hipError_t launch_compress_score(const CompressArgs* jobs, int n, int key_job, const IndexerArgs& a,
+                                 hipStream_t stream) {
+  if (a.fmt != CSA_FP8 || a.nq == 0 || a.nq >= kShareMinQueries) {
+    const hipError_t e = launch_compress_jobs(jobs, n, stream);
+    return e != hipSuccess ? e : launch_indexer(a, stream);
+  }
+  CompressJobs J{};
+  NewKeys nk{};
+  int kj = -1, maxD = 1;
+  bool any = false;
+  J.blk0[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nb = jobs[i].n_tok / jobs[i].m;
+    if (nb == 0) continue;
+    if (i == key_job) {
+      kj = J.n;
+      nk = NewKeys{jobs[i].seg_tok_off, jobs[i].seg_out_row, jobs[i].n_tok, jobs[i].nseg, jobs[i].m};
+    }
+    J.a[J.n] = jobs[i];
+    J.kind[J.n] = cmp::block_kind(jobs[i]);
+    any = any || J.kind[J.n] == cmp::kAny;
+    J.blk0[J.n + 1] = J.blk0[J.n] + nb;
+    maxD = jobs[i].D > maxD ? jobs[i].D : maxD;
+    ++J.n;
+  }
+  if (J.n == 0) return launch_indexer(a, stream);
+  StreamPlan p = plan_stream(a);
+  const bool il = p.R > 2;                             // interleaved shares (long rows)
+  const int64_t total = J.blk0[J.n];
+  const int n_cwg = static_cast<int>(total < 65536 ? total : 65536);
+  // The compress workgroups take resident slots (two workgroups per CU at
+  // this kernel's register count).  When the plan's contiguous shares fill
+  // every slot, fewer items of slightly longer shares let the whole launch
+  // run in one round instead of leaving n_cwg items for a second one.
+  const int64_t slots = static_cast<int64_t>(device_cu_count()) * 2;
+  if (p.R <= 2 && p.n_items + n_cwg > slots && slots - n_cwg >= a.nq) {
+    const int64_t gp = (a.ld + kGroupKeys - 1) / kGroupKeys;
+    p.n_chunk = (slots - n_cwg) / a.nq;
+    p.n_items = static_cast<int64_t>(a.nq) * p.n_chunk;
+    p.R = (gp + 4 * p.n_chunk - 1) / (4 * p.n_chunk);
+    p.grid = static_cast<unsigned>(p.n_items);
+  }
+  const dim3 grid(static_cast<unsigned>(n_cwg) + p.grid), block(256);
+  const size_t shm = cmp::shm_bytes(maxD);
+  const int r = static_cast<int>(p.R);
+  const bool three = !il && p.R == 3;                 // every group of a three-group share in flight
+#define CSA_CS_LAUNCH(NB, IL, ANY, BUF)                                                                    \
+  hipLaunchKernelGGL((compress_score_kernel<NB, IL, ANY, BUF>), grid, block, shm, stream, J, kj, nk, a,   \
+                     p.n_items, p.n_chunk, r, n_cwg)
+#define CSA_CS_CASE(NB)                                                                                   \
+  case NB:                                                                                                \
+    if (il) { if (any) CSA_CS_LAUNCH(NB, true, true, 2); else CSA_CS_LAUNCH(NB, true, false, 2); }       \
+    else if (three) { if (any) CSA_CS_LAUNCH(NB, false, true, 3); else CSA_CS_LAUNCH(NB, false, false, 3); } \
+    else { if (any) CSA_CS_LAUNCH(NB, false, true, 2); else CSA_CS_LAUNCH(NB, false, false, 2); }        \
+    break;
+  switch (a.H / 16) {
+    CSA_CS_CASE(1)
+    CSA_CS_CASE(2)
+    CSA_CS_CASE(4)
+    CSA_CS_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA_CS_CASE
+#undef CSA_CS_LAUNCH
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
   if (a.nq == 0) return hipSuccess;
@@ -543,19 +760,11 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int nhb = a.H / 16;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-  // share length: enough 64-key groups per wave that one round of two waves
-  // per SIMD covers the batch, at least 2 (two groups in flight), at most 32
-  const int64_t groups = static_cast<int64_t>(a.nq) * ((a.ld + kGroupKeys - 1) / kGroupKeys);
-  const int64_t waves = static_cast<int64_t>(device_cu_count()) * 8;
-  int64_t R = (groups + waves - 1) / waves;
-  R = R < 2 ? 2 : (R > 32 ? 32 : R);
-  const int64_t item_keys = 4 * R * kGroupKeys;
-  const int64_t n_chunk = (a.ld + item_keys - 1) / item_keys;
-  const int64_t n_items = static_cast<int64_t>(a.nq) * n_chunk;
-  const unsigned grid = static_cast<unsigned>(n_items < cap ? n_items : cap);
-  const int r = static_cast<int>(R);
-  const bool il = R > 2;
+  const StreamPlan p = plan_stream(a);
+  const int64_t n_items = p.n_items, n_chunk = p.n_chunk;
+  const unsigned grid = p.grid;
+  const int r = static_cast<int>(p.R);
+  const bool il = p.R > 2;
 #define CSA_IDX_CASE(K, NB)                                                                              \
   case NB:                                                                                               \
     if (il) hipLaunchKernelGGL((K<NB, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);   \

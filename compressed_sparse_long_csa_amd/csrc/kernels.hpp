@@ -42,6 +42,11 @@ struct IndexerArgs {
   const int64_t* key_off; const int64_t* q_pos; int m; float* scores; int64_t ld;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
+// jobs (n <= kMaxCompressJobs, none empty) and the indexer in one launch when
+// the keys are FP8 and the batch takes the streaming kernel, else the two
+// launches one after the other.  key_job: the job that writes a.keys, or -1.
+hipError_t launch_compress_score(const CompressArgs* jobs, int n, int key_job, const IndexerArgs& a,
+                                 hipStream_t stream);
 
 struct TopkArgs {
   const float* scores; int64_t ld; int nq; const int64_t* n_valid; int k;

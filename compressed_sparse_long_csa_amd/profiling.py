@@ -10,14 +10,15 @@
 
   python -m compressed_sparse_long_csa_amd.profiling traffic --kernel SUBSTR \\
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-bytes N \\
-      --source FILE --out JSON
+      --source FILE [--source FILE ...] --out JSON
       HBM bytes per launch of the kernels whose name contains SUBSTR, from two
       `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per
       dispatch).  Each counter is scaled by what it reads for a plain copy
       kernel that moves a known number of bytes (N read, N written), so the
       figure does not depend on the counter's unit or channel coverage.  The
-      record keeps the sha256 of the kernel's source file: a reader can tell
-      whether the counters were taken on the current kernel.
+      record keeps the sha256 of the kernel's source files (concatenated in
+      the order given): a reader can tell whether the counters were taken on
+      the current kernel.
 """
 import argparse
 import collections
@@ -50,6 +51,14 @@ def kernel_stats(db, runs=None):
     return out
 
 
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def counter_per_dispatch(path, substr, counter):
     vals = collections.defaultdict(float)
     with open(path) as f:
@@ -68,8 +77,9 @@ def main(argv=None):
     s.add_argument("db")
     s.add_argument("--split-runs", action="store_true")
     t = sub.add_parser("traffic")
-    for a in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--source", "--out"):
+    for a in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--out"):
         t.add_argument(a, required=True)
+    t.add_argument("--source", action="append", required=True)
     t.add_argument("--copy-kernel", default="elementwise")
     t.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy launch")
     args = ap.parse_args(argv)
@@ -92,8 +102,7 @@ def main(argv=None):
     w_scale = args.copy_bytes / (cw_kib * 1024.0)
     fetch_b = f_kib * 1024.0 * f_scale
     write_b = w_kib * 1024.0 * w_scale
-    with open(args.source, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = sources_sha256(args.source)
     rec = dict(kernel=args.kernel, dispatches=[nf, nw], fetch_kib_per_dispatch=f_kib,
                write_kib_per_dispatch=w_kib, copy_bytes=args.copy_bytes,
                copy_fetch_kib=cf_kib, copy_write_kib=cw_kib, fetch_scale=f_scale,

@@ -206,6 +206,48 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
                          hipStream_t stream);
 
 /*
+ * csa_compress_score -- a decode step's compress jobs and its indexer scores
+ * in one call.
+ *
+ * Source: the passages of csa_compress and indexer_score.  In a decode step
+ * the new tokens' index key must be compressed before the indexer can score
+ * it; this call does both (and any other compress job of the step, such as
+ * the KV entry and the window row) with one kernel launch, so the step pays
+ * for one launch instead of two.
+ *
+ * Results: exactly those of csa_compress_batch(jobs, n_jobs) followed by
+ * indexer_score(q_idx, ..., ld) -- the same bytes in every output row and
+ * the same bits in every score -- provided that:
+ *   - at most one job writes the indexer keys (the job whose `out` equals
+ *     `keys`; none is allowed), and that job has out_fmt == fmt, D == d_idx,
+ *     rope_dim == 0 and one segment per query (nseg == nq): segment i holds
+ *     query i's new tokens;
+ *   - every key row that job writes in segment i is seen by query i alone,
+ *     as its last visible row (row key_off[i] + N_i - 1): a decode step with
+ *     one query per sequence, where a sequence completes at most one block;
+ *   - no other job writes memory that the indexer reads.
+ * Inside the launch, the workgroup that compresses a new key row also scores
+ * it for its query, with the indexer's own arithmetic; the indexer's
+ * workgroups score every other row.  When the precondition does not hold
+ * the scores of the rows being written are undefined (no access leaves the
+ * buffers named by the arguments).  FP8 keys with nq < 1024 take the single
+ * launch; other formats and larger batches run the two launches in order.
+ *
+ * Arguments: `jobs` / n_jobs as for csa_compress_batch (host array, read
+ * during the call only); the rest as for indexer_score.
+ * Errors: those of csa_compress_batch and indexer_score (same checks, names
+ * of this entry point in csa_last_error()); INVALID_ARG when two jobs write
+ * `keys` or the key job breaks the shape rules above.  Nothing is launched
+ * when a check fails.  nq = 0 runs the jobs alone (csa_compress_batch, with
+ * no rule on the key job).
+ */
+csa_status csa_compress_score(const csa_compress_job* jobs /*[host]*/, int n_jobs,
+                              const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                              const void* keys, csa_fmt fmt, const int64_t* key_off,
+                              const int64_t* q_pos, int m, float* scores, int64_t ld,
+                              hipStream_t stream);
+
+/*
  * topk_select -- the top-k selector.
  *
  * Source: 硅星人 article, CSA paragraph (keep the 512 most relevant compressed

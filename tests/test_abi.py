@@ -144,3 +144,34 @@ def test_indexer_argument_errors(lib):
     assert call(ld=0) == INVALID
     assert call(ld=(1 << 24) + 1) == INVALID          # key rows must stay under 2^31 bytes
     assert call(nq=0) == OK
+
+
+def test_compress_score_argument_errors(lib):
+    """csa_compress_score's host checks: those of both calls it stands for,
+    plus the shape of the job that writes the indexer keys."""
+    p, keys = _fake(), _fake(2)
+
+    def key_job(**kw):
+        j = binding.CompressJob(x=p.value, x_fmt=csa.BF16, gate=p.value, gate_cols=1, n_tok=8, D=128,
+                                m=4, nseg=2, seg_tok_off=p.value, seg_pos0=p.value, seg_out_row=p.value,
+                                normalize=0, norm_w=None, eps=1e-6, rope_dim=0, rope_base=1e4,
+                                out=keys.value, out_fmt=csa.FP8)
+        for k, v in kw.items():
+            setattr(j, k, v)
+        return j
+
+    def call(jobs, nq=2, fmt=csa.FP8, H=64, d=128, ld=1024):
+        arr = (binding.CompressJob * max(1, len(jobs)))(*jobs)
+        return lib.csa_compress_score(arr, len(jobs), p, p, nq, H, d, keys, fmt, p, p, 4, p,
+                                      ctypes.c_int64(ld), None)
+    for bad in (dict(nseg=1), dict(D=64), dict(out_fmt=csa.MXFP4), dict(rope_dim=2)):
+        assert call([key_job(**bad)]) == INVALID, bad
+        assert "csa_compress_score" in _last_error(lib)
+    assert call([key_job(), key_job()]) == INVALID               # two jobs write `keys`
+    assert "both write" in _last_error(lib)
+    assert call([key_job(m=0)]) == INVALID                       # the job's own checks
+    assert "job 0" in _last_error(lib)
+    assert call([key_job()], d=96) == UNSUPPORTED                # the indexer's own checks
+    assert call([key_job()], ld=0) == INVALID
+    assert lib.csa_compress_score(None, 0, p, p, 0, 64, 128, keys, csa.FP8, p, p, 4, p,
+                                  ctypes.c_int64(1024), None) == OK   # nothing to do

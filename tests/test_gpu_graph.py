@@ -1,8 +1,9 @@
 """The whole decode step -- csa_compress_batch (KV entry, indexer key, window
-row), indexer_score, topk_select, hybrid_attn_decode -- captured in one HIP
-graph and replayed: every replay, with eager work and synchronisation
-between replays, gives the bits of the eager step.  Also the CSA prefill
-indexer (shared-key kernel) and top-k captured together."""
+row), indexer_score, topk_select, hybrid_attn_decode, or the same step with
+csa_compress_score in place of the first two -- captured in one HIP graph and
+replayed: every replay, with eager work and synchronisation between replays,
+gives the bits of the eager step.  Also the CSA prefill indexer (shared-key
+kernel) and top-k captured together."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +22,7 @@ def _lib():
     csa.load_library()
 
 
-def _decode_step(lengths, seed):
+def _decode_step(lengths, seed, fused=False):
     m, H, D, R, k, n_win, d_I, H_I = 4, 64, 512, 64, 512, 128, 128, 64
     d = synth.device_decode_inputs(seed, lengths, m=m, H=H, D=D, R=R, n_win=n_win, csa=True, k=k,
                                    H_I=H_I, d_I=d_I)
@@ -52,9 +53,13 @@ def _decode_step(lengths, seed):
                 d["win"], csa.BF16)]
 
     def run(scores, idx, out, check):
-        csa.csa_compress_batch(jobs, check=check)
-        csa.indexer_score(d["q_idx"], d["w"], B, H_I, d_I, d["keys"], csa.FP8, st["kv_off"], st["q_pos"], m,
-                          scores, ld, check=check)
+        if fused:
+            csa.csa_compress_score(jobs, d["q_idx"], d["w"], B, H_I, d_I, d["keys"], csa.FP8, st["kv_off"],
+                                   st["q_pos"], m, scores, ld, check=check)
+        else:
+            csa.csa_compress_batch(jobs, check=check)
+            csa.indexer_score(d["q_idx"], d["w"], B, H_I, d_I, d["keys"], csa.FP8, st["kv_off"], st["q_pos"],
+                              m, scores, ld, check=check)
         csa.topk_select(scores, ld, B, st["n_valid"], k, idx, None, check=check)
         csa.hybrid_attn_decode(d["q"], csa.BF16, B, H, D, st["q_pos"], None, EPS, R, ROPE_BASE, d["kv"],
                                csa.SPLIT, st["kv_off"], m, idx, k, d["win"], csa.BF16, n_win, st["win_len"],
@@ -98,8 +103,9 @@ def _replay_matches(run, bufs):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
-def test_decode_step_in_a_graph():
-    run, bufs = _decode_step([65536, 20000, 4100, 129, 70000], seed=81)
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_step_in_a_graph(fused):
+    run, bufs = _decode_step([65536, 20000, 4100, 129, 70000], seed=81, fused=fused)
     _replay_matches(run, bufs)
 
 
