@@ -7,5 +7,6 @@ input generator (synth).  Build the library with
 """
 from .binding import (BF16, F32, FP8, MXFP4, SPLIT, VARIANT_AUTO, VARIANT_HIGH_OCC,  # noqa: F401
                       VARIANT_LOW_OCC, CsaError, csa_compress, csa_compress_batch, csa_compress_score,
-                      hybrid_attn_decode,
-                      hybrid_attn_prefill, indexer_score, load_library, row_bytes, topk_select)
+                      hybrid_attn_decode, hybrid_attn_decode_paged,
+                      hybrid_attn_prefill, indexer_score, indexer_score_paged, load_library, row_bytes,
+                      topk_select)

@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
-           "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score", "topk_select",
-           "hybrid_attn_decode", "hybrid_attn_prefill")
+           "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
+           "indexer_score_paged", "topk_select", "hybrid_attn_decode", "hybrid_attn_decode_paged",
+           "hybrid_attn_prefill")
 
 _lib = None
 
@@ -56,6 +57,11 @@ def load_library():
     lib.csa_compress_score.restype = I
     lib.csa_compress_score.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, P, P, I, P,
                                        I64, P]
+    lib.indexer_score_paged.restype = I
+    lib.indexer_score_paged.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I, P, I, P, I64, P]
+    lib.hybrid_attn_decode_paged.restype = I
+    lib.hybrid_attn_decode_paged.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, I64, P, I64, I, I, P, I, P, I, I,
+                                             P, P, F, P, I, I, P]
     lib.indexer_score.restype = I
     lib.indexer_score.argtypes = [P, P, I, I, I, P, I, P, P, I, P, I64, P]
     lib.topk_select.restype = I
@@ -201,6 +207,37 @@ def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, sc
                              _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
+def _paged_checks(table, nq, blocks_per_seq, block_rows, pool, pool_rows, rb, q_pos, m, ld, check):
+    """Host-side checks of a block table: its shape, and with check=True that
+    every block a query uses is inside the pool."""
+    _need(table, "block_table", torch.int32, min_numel=nq * blocks_per_seq)
+    _need(pool, "pool", min_bytes=pool_rows * rb)
+    if check and nq > 0:
+        N = torch.clamp((_host(q_pos)[:nq] + 1) // m, max=ld)
+        if int(N.max()) > blocks_per_seq * block_rows:
+            raise ValueError("a query sees more rows than its block-table row holds")
+        t = _host(table)[: nq * blocks_per_seq].view(nq, blocks_per_seq)
+        nb = (N + block_rows - 1) // block_rows
+        for i in range(nq):
+            used = t[i, : int(nb[i])]
+            if used.numel() and (int(used.min()) < 0 or (int(used.max()) + 1) * block_rows > pool_rows):
+                raise ValueError(f"query {i} uses a block outside the pool")
+
+
+def indexer_score_paged(q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table, blocks_per_seq,
+                        block_rows, q_pos, m, scores, ld, stream=None, check=True):
+    lib = load_library()
+    rb = row_bytes(fmt, d_idx)
+    _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
+    _need(w, "w", torch.float32, min_numel=nq * n_heads)
+    _need(q_pos, "q_pos", torch.int64, min_numel=nq)
+    _need(scores, "scores", torch.float32, min_numel=nq * ld)
+    _paged_checks(block_table, nq, blocks_per_seq, block_rows, key_pool, pool_rows, rb, q_pos, m, ld, check)
+    _check(lib.indexer_score_paged(_ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool), fmt, pool_rows,
+                                   _ptr(block_table), blocks_per_seq, block_rows, _ptr(q_pos), m, _ptr(scores),
+                                   ld, _stream(stream)))
+
+
 def _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check):
     rb = row_bytes(fmt, d_idx)
     _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
@@ -258,6 +295,28 @@ def hybrid_attn_decode(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_b
                                   rope_dim, rope_base, _ptr(kv), kv_fmt, _ptr(kv_off), m, _ptr(idx),
                                   k, _ptr(win), win_fmt, n_win, _ptr(win_len), _ptr(sinks), scale,
                                   _ptr(out), out_fmt, variant, _stream(stream)))
+
+
+def hybrid_attn_decode_paged(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt,
+                             pool_rows, block_table, blocks_per_seq, block_rows, m, idx, k, win, win_fmt, n_win,
+                             win_len, sinks, scale, out, out_fmt, variant=VARIANT_AUTO, stream=None, check=True):
+    lib = load_library()
+    rb = row_bytes(kv_fmt, D, rope_dim)
+    _need(q, "q", min_bytes=B * H * row_bytes(q_fmt, D, rope_dim))
+    _need(q_pos, "q_pos", torch.int64, min_numel=B)
+    _need(q_norm_w, "q_norm_w", torch.float32, min_numel=D, allow_none=True)
+    _need(idx, "idx", torch.int32, min_numel=B * k)
+    _need(sinks, "sinks", torch.float32, min_numel=H)
+    _need(out, "out", min_bytes=B * H * row_bytes(out_fmt, D, rope_dim))
+    _paged_checks(block_table, B, blocks_per_seq, block_rows, kv_pool, pool_rows, rb, q_pos, m, 1 << 62, check)
+    if n_win > 0:
+        _need(win, "win", min_bytes=B * n_win * row_bytes(win_fmt, D, rope_dim))
+        _need(win_len, "win_len", torch.int32, min_numel=B)
+    _check(lib.hybrid_attn_decode_paged(_ptr(q), q_fmt, B, H, D, _ptr(q_pos), _ptr(q_norm_w), eps, rope_dim,
+                                        rope_base, _ptr(kv_pool), kv_fmt, pool_rows, _ptr(block_table),
+                                        blocks_per_seq, block_rows, m, _ptr(idx), k, _ptr(win), win_fmt, n_win,
+                                        _ptr(win_len), _ptr(sinks), scale, _ptr(out), out_fmt, variant,
+                                        _stream(stream)))
 
 
 def hybrid_attn_prefill(q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt,

@@ -542,7 +542,8 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
   const double theta = a.rope_theta[tid < kR / 2 ? tid : 0];
   const float sink = a.sinks[ht * 16 + j16];
-  const int64_t p_ld = a.q_pos[b], kv0_ld = a.kv_off[b];
+  const bool paged = a.blk_table != nullptr;
+  const int64_t p_ld = a.q_pos[b], kv0_ld = paged ? 0 : a.kv_off[b];
   const int wl_ld = a.win_mode == 1 ? a.win_len[b] : 0;
   const int64_t tp0_ld = a.win_mode == 2 ? a.tok_pos0[b] : 0, toff_ld = a.win_mode == 2 ? a.tok_off[b] : 0;
   const int32_t* idx_q = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
@@ -564,8 +565,9 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   w.n_list = a.idx != nullptr ? (w.N > 0 ? a.k : 0) : static_cast<int>(w.N);
   w.ns = (w.n_list + kWaves * kStepE - 1) / (kWaves * kStepE);
   w.n_steps = w.ns + (w.win_count + kWaves * kStepW - 1) / (kWaves * kStepW);
-  const uint64_t kv_bytes = static_cast<uint64_t>(w.N) * kRowSplit;
-  w.kv_rs = make_rsrc(static_cast<const uint8_t*>(a.kv) + kv0 * kRowSplit,
+  // paged: one descriptor over the pool (rows addressed by physical row)
+  const uint64_t kv_bytes = static_cast<uint64_t>(paged ? a.pool_rows : w.N) * kRowSplit;
+  w.kv_rs = make_rsrc(static_cast<const uint8_t*>(a.kv) + (paged ? 0 : kv0 * kRowSplit),
                       kv_bytes < 0xffffffffull ? static_cast<uint32_t>(kv_bytes) : 0xffffffffu);
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                        static_cast<uint32_t>(w.win_count) * kRowBf16);
@@ -577,6 +579,21 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     const bool ok = w.idx != nullptr && step < w.ns && pos < w.n_list && e_ld[t] >= 0 && e_ld[t] < w.N;
     tab.e[t] = ok ? e_ld[t] : 0;
     tab.valid[t] = __ballot(ok);
+  }
+  if (paged) {
+    // logical entry -> pool row through the query's block table (one more
+    // dependent round trip before the first rows go out); a slot without an
+    // entry maps entry 0 and stays masked
+    const int sh = a.blk_shift;
+    const buf_rsrc trs = make_rsrc(a.blk_table + static_cast<int64_t>(b) * a.blk_stride,
+                                   static_cast<uint32_t>(a.blk_stride * 4));
+    int32_t blk[kTabSteps / 4];
+#pragma unroll
+    for (int t = 0; t < kTabSteps / 4; ++t)
+      blk[t] = __builtin_amdgcn_raw_buffer_load_b32(trs, (tab.e[t] >> sh) * 4, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kTabSteps / 4; ++t)
+      tab.e[t] = static_cast<int>((static_cast<uint32_t>(blk[t]) << sh) | (static_cast<uint32_t>(tab.e[t]) & ((1u << sh) - 1u)));
   }
   // the first step's rows go out before the query is prepared
   uint32_t vmask0 = 0u;

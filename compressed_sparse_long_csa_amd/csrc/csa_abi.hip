@@ -224,6 +224,35 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
   return launched(launch_indexer(a, stream), "indexer_score");
 }
 
+csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                               const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                               const int32_t* block_table, int64_t blocks_per_seq, int block_rows,
+                               const int64_t* q_pos, int m, float* scores, int64_t ld, hipStream_t stream) {
+  const char* what = "indexer_score_paged";
+  if (fmt == CSA_F32) return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path takes FP8 or MXFP4 keys", what);
+  IndexerArgs a{};
+  bool empty = false;
+  // (block_table stands in for key_off in the shared null-pointer check)
+  const csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, key_pool, fmt,
+                                     reinterpret_cast<const int64_t*>(block_table), q_pos, m, scores, ld, &a,
+                                     &empty);
+  if (st != CSA_OK) return st;
+  if (block_rows < 16 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
+    return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [16, 2^20]", what);
+  if (blocks_per_seq < 1 || blocks_per_seq > (int64_t{1} << 26))
+    return fail(CSA_ERR_INVALID_ARG, "%s: blocks_per_seq must be in [1, 2^26]", what);
+  if (pool_rows < 1) return fail(CSA_ERR_INVALID_ARG, "%s: pool_rows must be >= 1", what);
+  if (static_cast<uint64_t>(pool_rows) * row_bytes(fmt, d_idx, 0) > 0xffffffffull)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: the key pool must be smaller than 4 GiB", what);
+  if (empty) { g_err[0] = '\0'; return CSA_OK; }
+  a.key_off = nullptr;
+  a.blk_table = block_table;
+  a.blk_stride = blocks_per_seq;
+  a.blk_shift = __builtin_ctz(static_cast<unsigned>(block_rows));
+  a.pool_rows = pool_rows;
+  return launched(launch_indexer(a, stream), what);
+}
+
 csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
                               const float* w, int nq, int n_heads, int d_idx, const void* keys,
                               csa_fmt fmt, const int64_t* key_off, const int64_t* q_pos, int m,
@@ -309,7 +338,7 @@ static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream)
                 "%s: supported formats are all-F32, or q/win/out BF16 with a SPLIT cache", name);
   }
   if (a.nq == 0) { g_err[0] = '\0'; return CSA_OK; }
-  if (!a.q || !a.q_pos || !a.kv || !a.kv_off || !a.sinks || !a.out)
+  if (!a.q || !a.q_pos || !a.kv || (!a.kv_off && !a.blk_table) || !a.sinks || !a.out)
     return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", name);
   if (a.n_win > 0 && !a.win) return fail(CSA_ERR_INVALID_ARG, "%s: null window pointer", name);
   fill_rope_theta(a.rope_theta, a.rope_dim, a.rope_base);
@@ -330,6 +359,36 @@ csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
              idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
              scale, out, out_fmt, static_cast<int>(variant), {}};
   return attn_common("hybrid_attn_decode", a, stream);
+}
+
+csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, int D,
+                                    const int64_t* q_pos, const float* q_norm_w, float eps,
+                                    int rope_dim, float rope_base, const void* kv_pool, csa_fmt kv_fmt,
+                                    int64_t pool_rows, const int32_t* block_table, int64_t blocks_per_seq,
+                                    int block_rows, int m, const int32_t* idx, int k,
+                                    const void* win, csa_fmt win_fmt, int n_win,
+                                    const int32_t* win_len, const float* sinks, float scale,
+                                    void* out, csa_fmt out_fmt, csa_variant variant,
+                                    hipStream_t stream) {
+  const char* what = "hybrid_attn_decode_paged";
+  if (B > 0 && n_win > 0 && !win_len) return fail(CSA_ERR_INVALID_ARG, "%s: null win_len", what);
+  if (!(q_fmt == CSA_BF16 && kv_fmt == CSA_SPLIT && win_fmt == CSA_BF16 && out_fmt == CSA_BF16))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path is the MFMA path (BF16 q / window / out, SPLIT cache)",
+                what);
+  if (k < 1 || k > 1024) return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path takes 1 <= k <= 1024", what);
+  if (block_rows < 1 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
+    return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [1, 2^20]", what);
+  if (blocks_per_seq < 1 || blocks_per_seq > (int64_t{1} << 26))
+    return fail(CSA_ERR_INVALID_ARG, "%s: blocks_per_seq must be in [1, 2^26]", what);
+  if (pool_rows < 1) return fail(CSA_ERR_INVALID_ARG, "%s: pool_rows must be >= 1", what);
+  if (static_cast<uint64_t>(pool_rows) * row_bytes(CSA_SPLIT, D, rope_dim) > 0xffffffffull)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: the entry pool must be smaller than 4 GiB", what);
+  if (B > 0 && (!block_table || !idx)) return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", what);
+  AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt, nullptr, m,
+             idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
+             scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,
+             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows};
+  return attn_common(what, a, stream);
 }
 
 csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int D,

@@ -108,6 +108,61 @@ __device__ __forceinline__ void load_group_fp8(buf_rsrc rs, uint32_t voff0, uint
   }
 }
 
+// ---------------------------------------------------------------- paged keys
+// A paged key cache: query i's rows come in blocks of BR = 2^sh rows (BR >=
+// 16, so that a 16-key MFMA block lies in one block); its logical block j is
+// physical block blk_table[i * blk_stride + j] of the pool.  A wave reads the
+// table entries of its share once, in the round trip of the query's position
+// (two per lane: at most 32 groups of 64 keys, at most four blocks each), and
+// takes them with readlane.  Keys are addressed through one descriptor over
+// the pool, all of the offset in the per-lane part, so the range check sees
+// the whole offset; table entries past the row read as 0 and rows past N are
+// multiplied but never stored.
+struct PagedTab {
+  int32_t e[2];
+  int bpg_shift;                                         // log2(blocks per 64-key group)
+};
+
+__device__ __forceinline__ void paged_tab_load(const IndexerArgs& a, int i, uint32_t first, uint32_t step,
+                                               int R, int lane, PagedTab& pt) {
+  const int sh = a.blk_shift;
+  pt.bpg_shift = sh >= 6 ? 0 : 6 - sh;
+  const buf_rsrc trs = make_rsrc(a.blk_table + static_cast<int64_t>(i) * a.blk_stride,
+                                 static_cast<uint32_t>(a.blk_stride * 4));
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t e = static_cast<uint32_t>(s * 64 + lane);
+    const uint32_t u = e >> pt.bpg_shift, q = e & ((1u << pt.bpg_shift) - 1u);
+    const uint32_t lb = (((first + u * step) * static_cast<uint32_t>(kGroupKeys)) >> sh) + q;
+    const uint32_t off = u < static_cast<uint32_t>(R) && lb < static_cast<uint32_t>(a.blk_stride) ? lb * 4u
+                                                                                                   : 0x80000000u;
+    pt.e[s] = __builtin_amdgcn_raw_buffer_load_b32(trs, static_cast<int>(off), 0, 0);
+  }
+}
+
+// Pool row of the first key of 16-key block kb of the wave's group u (uniform).
+__device__ __forceinline__ uint32_t paged_row(const PagedTab& pt, int sh, uint32_t first, uint32_t step, int u,
+                                              int kb) {
+  const uint32_t key = (first + static_cast<uint32_t>(u) * step) * static_cast<uint32_t>(kGroupKeys) +
+                       static_cast<uint32_t>(kb) * 16u;
+  const int e = (u << pt.bpg_shift) + ((kb * 16) >> sh);
+  const int32_t blk = e < 64 ? __builtin_amdgcn_readlane(pt.e[0], e) : __builtin_amdgcn_readlane(pt.e[1], e - 64);
+  return (static_cast<uint32_t>(blk) << sh) | (key & ((1u << sh) - 1u));
+}
+
+__device__ __forceinline__ void load_group_fp8_paged(buf_rsrc rs, const PagedTab& pt, int sh, uint32_t first,
+                                                     uint32_t step, int t, int ng, int j16, int g,
+                                                     uint4 (&kr)[4][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t voff = t < ng ? (paged_row(pt, sh, first, step, t, kb) + static_cast<uint32_t>(j16)) * 128u +
+                                       static_cast<uint32_t>(g) * 32u
+                                 : 0x80000000u;
+    kr[kb][0] = buf_load_x4(rs, voff, 0);
+    kr[kb][1] = buf_load_x4(rs, voff + 16u, 0);
+  }
+}
+
 // MFMAs of one group's blocks; the head sum of the block before (held in
 // cp) is computed and stored while a block multiplies.  `pend` is the score
 // offset (bytes, relative to the lane's first score) of the block in cp, or
@@ -156,7 +211,7 @@ struct NewKeys {
 };
 
 // NB: groups in flight per wave (2; 3 where shares of three groups are common)
-template <int NHB, bool IL, bool kNew, int NB = 2>   // head blocks of 16; interleaved shares; keys written alongside
+template <int NHB, bool IL, bool kNew, int NB = 2, bool kPaged = false>   // head blocks of 16; interleaved shares; keys written alongside; paged keys
 __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items, int64_t n_chunk, int R,
                                           int64_t item0, int64_t item_step, const NewKeys& nk) {
   constexpr int H = NHB * 16;
@@ -182,7 +237,16 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
       qraw[hb][1] = qp[1];
       wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
     }
-    const int64_t qpos = scalar_load(a.q_pos, i), koff = scalar_load(a.key_off, i);
+    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;                     // waves of this query
+    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);   // this wave's turn
+    // the wave's groups: first, first + step, ...  Contiguous shares split
+    // the ld / 64 groups of a row as evenly as the W waves allow (at most R each)
+    const uint32_t Gp = static_cast<uint32_t>((a.ld + kGroupKeys - 1) / kGroupKeys);
+    const uint32_t first = IL ? wq : static_cast<uint32_t>(static_cast<uint64_t>(wq) * Gp / W);
+    const uint32_t step = IL ? W : 1u;
+    PagedTab pt{};
+    if (kPaged) paged_tab_load(a, i, first, step, R, lane, pt);
+    const int64_t qpos = scalar_load(a.q_pos, i), koff = kPaged ? 0 : scalar_load(a.key_off, i);
     int64_t lo = 0, hi = 0, row0 = 0;                  // query i's segment of the key job
     if (kNew && i < nk.nseg) {
       lo = scalar_load(nk.seg_tok_off, i);
@@ -202,16 +266,12 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
       if (j >= 0 && uniform64(lo) % nk.m == 0 && end <= uniform64(hi) && end <= nk.n_tok) Ns = N - 1;
     }
     // (N <= 2^24, so group counts fit 32 bits)
-    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;                     // waves of this query
-    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);   // this wave's turn
     const uint32_t G = static_cast<uint32_t>((N + kGroupKeys - 1) / kGroupKeys);
-    const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * 128,
-                                  static_cast<uint32_t>(N * 128));
-    // the wave's groups: first, first + step, ...  Contiguous shares split
-    // the ld / 64 groups of a row as evenly as the W waves allow (at most R each)
-    const uint32_t Gp = static_cast<uint32_t>((a.ld + kGroupKeys - 1) / kGroupKeys);
-    const uint32_t first = IL ? wq : static_cast<uint32_t>(static_cast<uint64_t>(wq) * Gp / W);
-    const uint32_t step = IL ? W : 1u;
+    const uint64_t pool_bytes = static_cast<uint64_t>(a.pool_rows) * 128u;
+    const buf_rsrc rs = kPaged ? make_rsrc(a.keys, pool_bytes < 0xffffffffull ? static_cast<uint32_t>(pool_bytes)
+                                                                             : 0xffffffffu)
+                               : make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * 128,
+                                           static_cast<uint32_t>(N * 128));
     if (first >= G) continue;                            // uniform over the wave (no barriers)
     uint32_t mine;
     if (IL) {
@@ -225,8 +285,12 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
     const uint32_t stride = step * (kGroupKeys * 128u);
     const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * 128u + g * 32u;
     uint4 kr[NB][4][2];                                  // NB groups in flight
+    auto load = [&](int t, uint4 (&dst)[4][2]) __attribute__((always_inline)) {
+      if (kPaged) load_group_fp8_paged(rs, pt, a.blk_shift, first, step, t, ng, j16, g, dst);
+      else load_group_fp8(rs, voff0, stride, t, ng, dst);
+    };
 #pragma unroll
-    for (int u = 0; u < NB; ++u) load_group_fp8(rs, voff0, stride, u, ng, kr[u]);
+    for (int u = 0; u < NB; ++u) load(u, kr[u]);
     // the query is used only from here on: its conversion must not be
     // scheduled above the key loads (it would wait for the query first)
 #pragma unroll
@@ -258,7 +322,7 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         group_fp8<NHB>(kr[u], qb, wr, cp, pend, t + u < ng ? (t + u) * out_stride : -1, out_rs, out_off);
-        load_group_fp8(rs, voff0, stride, t + u + NB, ng, kr[u]);
+        load(t + u + NB, kr[u]);
       }
     }
     const float tot = head_sum<NHB>(cp, wr);
@@ -267,10 +331,10 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
   }
 }
 
-template <int NHB, bool IL>
+template <int NHB, bool IL, bool kPaged = false>
 __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t n_items,
                                                           int64_t n_chunk, int R) {
-  fp8_items<NHB, IL, false>(a, n_items, n_chunk, R, blockIdx.x, gridDim.x, NewKeys{});
+  fp8_items<NHB, IL, false, 2, kPaged>(a, n_items, n_chunk, R, blockIdx.x, gridDim.x, NewKeys{});
 }
 
 // Score of a key row the launch has just compressed (the FP8 rounding of
@@ -537,6 +601,18 @@ __device__ __forceinline__ void load_group_fp4(buf_rsrc rs, uint32_t voff0, uint
   }
 }
 
+__device__ __forceinline__ void load_group_fp4_paged(buf_rsrc rs, const PagedTab& pt, int sh, uint32_t first,
+                                                     uint32_t step, int t, int ng, int j16, uint32_t g,
+                                                     uint4 (&kc)[4], uint32_t (&ks)[4]) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint32_t base = t < ng ? (paged_row(pt, sh, first, step, t, kb) + static_cast<uint32_t>(j16)) * kRowFp4
+                                 : 0x80000000u;
+    kc[kb] = buf_load_x4(rs, base + 16u * g, 0);
+    ks[kb] = __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>(base + 64u + g), 0, 0);
+  }
+}
+
 template <int NHB>
 __device__ __forceinline__ void group_fp4(const uint4 (&kc)[4], const uint32_t (&ks)[4], const i32x8 (&qop)[NHB],
                                           const int (&qsc)[NHB], const float (&wr)[NHB][4], f32x4 (&cp)[NHB],
@@ -560,7 +636,7 @@ __device__ __forceinline__ void group_fp4(const uint4 (&kc)[4], const uint32_t (
   }
 }
 
-template <int NHB, bool IL>
+template <int NHB, bool IL, bool kPaged = false>
 __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64_t n_items,
                                                             int64_t n_chunk, int R) {
   constexpr int H = NHB * 16;
@@ -585,17 +661,22 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
       qsc[hb] = row[64 + g];
       wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(i) * H + hb * 16 + g * 4);
     }
-    const int64_t qpos = scalar_load(a.q_pos, i), koff = scalar_load(a.key_off, i);
+    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;
+    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);
+    const uint32_t first = IL ? wq : wq * static_cast<uint32_t>(R);
+    const uint32_t step = IL ? W : 1u;
+    PagedTab pt{};
+    if (kPaged) paged_tab_load(a, i, first, step, R, lane, pt);
+    const int64_t qpos = scalar_load(a.q_pos, i), koff = kPaged ? 0 : scalar_load(a.key_off, i);
     asm volatile("" : : "s"(qpos), "s"(koff) : "memory");   // one round trip; the loads above stay above
     int64_t N = (uniform64(qpos) + 1) / a.m;
     if (N > a.ld) N = a.ld;
-    const uint32_t W = static_cast<uint32_t>(n_chunk) * 4u;
-    const uint32_t wq = static_cast<uint32_t>(chunk) * 4u + static_cast<uint32_t>(wv);
     const uint32_t G = static_cast<uint32_t>((N + kGroupKeys - 1) / kGroupKeys);
-    const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * kRowFp4,
-                                  static_cast<uint32_t>(N * kRowFp4));
-    const uint32_t first = IL ? wq : wq * static_cast<uint32_t>(R);
-    const uint32_t step = IL ? W : 1u;
+    const uint64_t pool_bytes = static_cast<uint64_t>(a.pool_rows) * kRowFp4;
+    const buf_rsrc rs = kPaged ? make_rsrc(a.keys, pool_bytes < 0xffffffffull ? static_cast<uint32_t>(pool_bytes)
+                                                                             : 0xffffffffu)
+                               : make_rsrc(static_cast<const uint8_t*>(a.keys) + uniform64(koff) * kRowFp4,
+                                           static_cast<uint32_t>(N * kRowFp4));
     if (first >= G) continue;                            // uniform over the wave (no barriers)
     const uint32_t mine = (G - first + step - 1u) / step;
     const int ng = mine < static_cast<uint32_t>(R) ? static_cast<int>(mine) : R;
@@ -604,8 +685,12 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
     const uint32_t voff0 = static_cast<uint32_t>(s0 + j16) * kRowFp4;
     uint4 kca[4], kcb[4];
     uint32_t ksa[4], ksb[4];
-    load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, 0, ng, kca, ksa);
-    load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, 1, ng, kcb, ksb);
+    auto load = [&](int t, uint4 (&kc)[4], uint32_t (&ks)[4]) __attribute__((always_inline)) {
+      if (kPaged) load_group_fp4_paged(rs, pt, a.blk_shift, first, step, t, ng, j16, static_cast<uint32_t>(g), kc, ks);
+      else load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, t, ng, kc, ks);
+    };
+    load(0, kca, ksa);
+    load(1, kcb, ksb);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
       asm volatile("" : "+v"(wraw[hb].x), "+v"(wraw[hb].y), "+v"(wraw[hb].z), "+v"(wraw[hb].w) : : "memory");
@@ -622,9 +707,9 @@ __global__ void __launch_bounds__(256) indexer_mxfp4_kernel(IndexerArgs a, int64
     const int out_stride = static_cast<int>(step * kGroupKeys * 4u);
     for (int t = 0; t < ng; t += 2) {
       group_fp4<NHB>(kca, ksa, qop, qsc, wr, cp, pend, t * out_stride, out_rs, out_off);
-      load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, t + 2, ng, kca, ksa);
+      load(t + 2, kca, ksa);
       group_fp4<NHB>(kcb, ksb, qop, qsc, wr, cp, pend, t + 1 < ng ? (t + 1) * out_stride : -1, out_rs, out_off);
-      load_group_fp4(rs, voff0, static_cast<uint32_t>(g), stride, t + 3, ng, kcb, ksb);
+      load(t + 3, kcb, ksb);
     }
     const float tot = head_sum<NHB>(cp, wr);
     if (pend >= 0)
@@ -761,16 +846,22 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
   }
   const int nhb = a.H / 16;
   const StreamPlan p = plan_stream(a);
+  const bool paged = a.blk_table != nullptr;
   const int64_t n_items = p.n_items, n_chunk = p.n_chunk;
   const unsigned grid = p.grid;
   const int r = static_cast<int>(p.R);
   const bool il = p.R > 2;
 #define CSA_IDX_CASE(K, NB)                                                                              \
   case NB:                                                                                               \
-    if (il) hipLaunchKernelGGL((K<NB, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);   \
-    else hipLaunchKernelGGL((K<NB, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r);     \
+    if (paged) {                                                                                         \
+      if (il) hipLaunchKernelGGL((K<NB, true, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); \
+      else hipLaunchKernelGGL((K<NB, false, true>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); \
+    } else {                                                                                             \
+      if (il) hipLaunchKernelGGL((K<NB, true, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); \
+      else hipLaunchKernelGGL((K<NB, false, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); \
+    }                                                                                                    \
     break;
-  if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries) {
+  if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries && !paged) {
     const int64_t n_qblk = (a.nq + kShareQ - 1) / kShareQ;
     const int64_t n_kchunk = ((a.ld + kGroupKeys - 1) / kGroupKeys + kShareGroups - 1) / kShareGroups;
     const int64_t units = n_qblk * n_kchunk;

@@ -40,6 +40,9 @@ hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t str
 struct IndexerArgs {
   const void* q; const float* w; int nq; int H; int d; const void* keys; csa_fmt fmt;
   const int64_t* key_off; const int64_t* q_pos; int m; float* scores; int64_t ld;
+  // paged keys (blk_table != nullptr; key_off unused): row s of query i is pool
+  // row blk_table[i * blk_stride + (s >> blk_shift)] * 2^blk_shift + (s mod 2^blk_shift)
+  const int32_t* blk_table; int64_t blk_stride; int blk_shift; int64_t pool_rows;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 // jobs (n <= kMaxCompressJobs, none empty) and the indexer in one launch when
@@ -74,6 +77,10 @@ struct AttnArgs {
   const int64_t* tok_off; const int64_t* tok_pos0;      // prefill
   const float* sinks; float scale; void* out; csa_fmt out_fmt; int variant;
   double rope_theta[kMaxRopePairs];
+  // paged cache (blk_table != nullptr, selected-entry decode only; kv_off
+  // unused): entry e of query b is pool row
+  // blk_table[b * blk_stride + (e >> blk_shift)] * 2^blk_shift + (e mod 2^blk_shift)
+  const int32_t* blk_table; int64_t blk_stride; int blk_shift; int64_t pool_rows;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

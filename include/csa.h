@@ -248,6 +248,38 @@ csa_status csa_compress_score(const csa_compress_job* jobs /*[host]*/, int n_job
                               hipStream_t stream);
 
 /*
+ * indexer_score_paged -- indexer_score over a paged key cache.
+ *
+ * Source: the passages of indexer_score; 硅星人 article, classic-cache
+ * paragraph (the compressed caches are kept in fixed blocks of 128 raw tokens,
+ * which hold 32 CSA entries and one HCA entry, so that nothing fragments).
+ *
+ * The keys of query i are not a contiguous run of rows: logical row s (s <
+ * N_i, N_i as for indexer_score) is row
+ *   block_table[i * blocks_per_seq + (s / block_rows)] * block_rows + s % block_rows
+ * of key_pool (pool_rows rows of d_idx values in `fmt`).  block_rows = 32 is
+ * one 128-token block of CSA keys.  The scores are those indexer_score gives
+ * for the same keys laid out contiguously (the same bits).
+ *
+ *   block_table  [nq, blocks_per_seq] int32 physical block numbers
+ * Preconditions: blocks_per_seq * block_rows >= N_i for every query, and
+ * every block a query uses lies inside the pool (otherwise a table entry
+ * past the row reads as block 0 and a row past the pool as zeros: wrong
+ * scores, no fault).
+ * Supported: FP8 / MXFP4 keys with indexer_score's head and dim rules,
+ * block_rows a power of two in [16, 2^20], a pool smaller than 4 GiB
+ * (UNSUPPORTED otherwise).  Every batch size runs the streaming kernel.
+ * Errors: those of indexer_score (block_table takes key_off's place in the
+ * null-pointer check); INVALID_ARG for bad block_rows / blocks_per_seq /
+ * pool_rows.
+ */
+csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                               const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                               const int32_t* block_table, int64_t blocks_per_seq, int block_rows,
+                               const int64_t* q_pos, int m, float* scores, int64_t ld,
+                               hipStream_t stream);
+
+/*
  * topk_select -- the top-k selector.
  *
  * Source: 硅星人 article, CSA paragraph (keep the 512 most relevant compressed
@@ -320,6 +352,39 @@ csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
                               const int32_t* win_len, const float* sinks, float scale,
                               void* out, csa_fmt out_fmt, csa_variant variant,
                               hipStream_t stream);
+
+/*
+ * hybrid_attn_decode_paged -- hybrid_attn_decode over a paged entry cache.
+ *
+ * Source: the passages of hybrid_attn_decode; 硅星人 article, classic-cache
+ * paragraph (fixed 128-token blocks: 32 CSA entries or one HCA entry each).
+ *
+ * Entry e of query b (e < N_b) is row
+ *   block_table[b * blocks_per_seq + (e / block_rows)] * block_rows + e % block_rows
+ * of kv_pool (pool_rows SPLIT rows).  Everything else -- the selected list
+ * idx (logical entry numbers, ascending), the window, the sinks, the
+ * reduction order -- is that of hybrid_attn_decode, and so are the output
+ * bits: a query gives the same bits whether its entries are paged or
+ * contiguous.
+ *
+ * Supported: the MFMA path (BF16 q / window / out, SPLIT cache, D = 512,
+ * rope_dim = 64, H a multiple of 16) with a selected list (idx non-NULL,
+ * 1 <= k <= 1024); block_rows a power of two in [1, 2^20]; a pool smaller than
+ * 4 GiB.  HCA (idx NULL) and the F32 path: UNSUPPORTED.
+ * Preconditions as for indexer_score_paged (blocks_per_seq * block_rows >=
+ * N_b; used blocks inside the pool).
+ * Errors: those of hybrid_attn_decode; INVALID_ARG for bad block_rows /
+ * blocks_per_seq / pool_rows or a NULL block_table / idx.
+ */
+csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, int D,
+                                    const int64_t* q_pos, const float* q_norm_w, float eps,
+                                    int rope_dim, float rope_base, const void* kv_pool, csa_fmt kv_fmt,
+                                    int64_t pool_rows, const int32_t* block_table, int64_t blocks_per_seq,
+                                    int block_rows, int m, const int32_t* idx, int k,
+                                    const void* win, csa_fmt win_fmt, int n_win,
+                                    const int32_t* win_len, const float* sinks, float scale,
+                                    void* out, csa_fmt out_fmt, csa_variant variant,
+                                    hipStream_t stream);
 
 /*
  * hybrid_attn_prefill -- the same attention for a chunk of causal queries.

@@ -1,0 +1,138 @@
+"""Paged caches: indexer_score_paged and hybrid_attn_decode_paged read a
+query's keys / entries through a block table (硅星人 article, classic-cache
+paragraph: fixed 128-token blocks of 32 CSA entries).  The same rows, paged
+in shuffled blocks of a pool, must give the bits of the contiguous calls --
+scores, selected sets and attention outputs -- for every block size."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_long_csa_amd as csa
+from compressed_sparse_long_csa_amd import synth
+from gpu_common import DEV, EPS, ROPE_BASE, dev, gpu_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+def _paginate(rows, n_ent, off, BR, rng, spare=3):
+    """Pool of shuffled blocks holding each query's rows, and the block table.
+    Unused pool rows hold random bytes; unused table entries name random
+    blocks of the pool."""
+    n_ent = np.asarray(n_ent, np.int64)
+    nb = (n_ent + BR - 1) // BR
+    bps = int(max(1, nb.max()))
+    total = int(nb.sum()) + spare
+    perm = rng.permutation(total).astype(np.int32)
+    rb = rows.shape[1]
+    pool = rng.integers(0, 256, size=(total * BR, rb), dtype=np.uint8)
+    table = rng.integers(0, total, size=(len(n_ent), bps)).astype(np.int32)
+    nxt = 0
+    for i, n in enumerate(n_ent):
+        for j in range(int(nb[i])):
+            phys = int(perm[nxt])
+            nxt += 1
+            table[i, j] = phys
+            lo = int(off[i]) + j * BR
+            cnt = min(BR, int(n) - j * BR)
+            pool[phys * BR: phys * BR + cnt] = rows[lo: lo + cnt]
+    return pool, table, bps, total * BR
+
+
+def _indexer_pair(inp, BR, seed):
+    B, ld = inp.B, int(max(1, inp.n_ent.max()))
+    keys = inp.keys.reshape(-1, synth.row_bytes(inp.idx_fmt, inp.d_I))
+    pool, table, bps, pool_rows = _paginate(keys, inp.n_ent, inp.kv_off, BR, np.random.default_rng(seed))
+    q_idx, w, q_pos = dev(inp.q_idx), dev(inp.w), dev(inp.q_pos)
+    a = torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV)
+    b = torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(q_idx, w, B, inp.H_I, inp.d_I, dev(inp.keys), inp.idx_fmt, dev(inp.kv_off), q_pos,
+                      inp.m, a, ld)
+    csa.indexer_score_paged(q_idx, w, B, inp.H_I, inp.d_I, dev(pool), inp.idx_fmt, pool_rows, dev(table), bps,
+                            BR, q_pos, inp.m, b, ld)
+    torch.cuda.synchronize()
+    return a, b
+
+
+@pytest.mark.parametrize("idx_fmt,H_I,BR", [(csa.FP8, 64, 32), (csa.FP8, 64, 16), (csa.FP8, 16, 256),
+                                            (csa.FP8, 128, 64), (csa.MXFP4, 64, 32), (csa.MXFP4, 32, 128)])
+def test_indexer_paged_matches_contiguous_bits(idx_fmt, H_I, BR):
+    lengths = [65536, 9001, 2052, 130, 5, 3, 40000, 4096]
+    inp = synth.decode_inputs(600 + BR + H_I, lengths, m=4, H=16, D=512, R=64, idx_fmt=idx_fmt, H_I=H_I)
+    a, b = _indexer_pair(inp, BR, 7)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_indexer_paged_long_rows_interleaved_shares():
+    """Rows long enough that the waves of a query take its groups in turn."""
+    lengths = [262144, 262144, 100000, 262144, 50000, 262144, 8, 180000]
+    inp = synth.decode_inputs(611, lengths, m=4, H=16, D=512, R=64, idx_fmt=csa.FP8, H_I=64)
+    a, b = _indexer_pair(inp, 32, 8)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def _attn_pair(inp, sel, BR, seed, variant):
+    B, H, D = inp.B, inp.H, inp.D
+    rb = synth.row_bytes(csa.SPLIT, D, inp.R)
+    pool, table, bps, pool_rows = _paginate(inp.kv.reshape(-1, rb), inp.n_ent, inp.kv_off, BR,
+                                            np.random.default_rng(seed))
+    q, q_pos, win, win_len, sinks = dev(inp.q), dev(inp.q_pos), dev(inp.win), dev(inp.win_len), dev(inp.sinks)
+    idx = dev(sel)
+    outs = []
+    for paged in (False, True):
+        out = gpu_bytes(B * H * D * 2)
+        if paged:
+            csa.hybrid_attn_decode_paged(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(pool),
+                                         csa.SPLIT, pool_rows, dev(table), bps, BR, inp.m, idx, inp.k, win,
+                                         csa.BF16, inp.n_win, win_len, sinks, inp.scale, out, csa.BF16, variant)
+        else:
+            csa.hybrid_attn_decode(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(inp.kv),
+                                   csa.SPLIT, dev(inp.kv_off), inp.m, idx, inp.k, win, csa.BF16, inp.n_win,
+                                   win_len, sinks, inp.scale, out, csa.BF16, variant)
+        outs.append(out)
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("BR,k,variant", [(32, 512, csa.VARIANT_AUTO), (1, 512, csa.VARIANT_LOW_OCC),
+                                          (128, 1024, csa.VARIANT_HIGH_OCC), (32, 64, csa.VARIANT_AUTO)])
+def test_attention_paged_matches_contiguous_bits(BR, k, variant):
+    lengths = [65536, 9001, 2052, 130, 5, 3, 40000]
+    inp = synth.decode_inputs(620 + BR, lengths, m=4, H=64, D=512, R=64, k=k)
+    sel = synth.random_selection(np.random.default_rng(9), inp.n_ent, k)
+    a, b = _attn_pair(inp, sel, BR, 10, variant)
+    assert torch.equal(a, b)
+
+
+def test_paged_step_matches_contiguous_step():
+    """indexer -> top-k -> attention over paged caches (blocks of 32 entries:
+    one 128-token block of CSA entries) against the same step on contiguous
+    caches: the same selected sets and output bits."""
+    lengths = [65536, 20000, 4100, 129, 70000, 3]
+    inp = synth.decode_inputs(631, lengths, m=4, H=64, D=512, R=64, k=512)
+    B, ld, k = inp.B, int(inp.n_ent.max()), inp.k
+    a, b = _indexer_pair(inp, 32, 11)
+    nv = dev(inp.n_ent)
+    ia = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    ib = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(a, ld, B, nv, k, ia)
+    csa.topk_select(b, ld, B, nv, k, ib)
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ib)
+    oa, ob = _attn_pair(inp, ia.cpu().numpy(), 32, 12, csa.VARIANT_AUTO)
+    assert torch.equal(oa, ob)
+
+
+def test_paged_argument_errors():
+    inp = synth.decode_inputs(640, [4096, 2052], m=4, H=16, D=512, R=64, H_I=64)
+    B, ld = inp.B, int(inp.n_ent.max())
+    keys = dev(inp.keys)
+    table = torch.zeros((B, 200), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, ld), dtype=torch.float32, device=DEV)
+    args = (dev(inp.q_idx), dev(inp.w), B, 64, 128, keys, csa.FP8, int(inp.n_ent.sum()), table, 200)
+    with pytest.raises(csa.CsaError):                       # block_rows not a power of two
+        csa.indexer_score_paged(*args, 24, dev(inp.q_pos), 4, scores, ld, check=False)
+    with pytest.raises(csa.CsaError):                       # below 16 rows per block
+        csa.indexer_score_paged(*args, 8, dev(inp.q_pos), 4, scores, ld, check=False)
+    with pytest.raises(ValueError):                         # a query sees more rows than its table row holds
+        csa.indexer_score_paged(dev(inp.q_idx), dev(inp.w), B, 64, 128, keys, csa.FP8, int(inp.n_ent.sum()),
+                                table[:, :1].contiguous(), 1, 16, dev(inp.q_pos), 4, scores, ld)
