@@ -435,6 +435,92 @@ def context_scan(contexts, steps, warmup):
 HCA = "hca_decode_b32_ctx262144"
 
 
+PAGED_BLOCK_ROWS = 32          # one 128-token block of CSA entries
+
+
+def paged_replica(Wr, seed):
+    """The replica's KV cache and index keys moved into pools of shuffled
+    32-entry blocks (a block table per sequence), and the step's new entry
+    rows mapped to their pool rows."""
+    inp, BR = Wr["inp"], PAGED_BLOCK_ROWS
+    n_ent = np.asarray(inp.n_ent, np.int64)
+    off = np.asarray(inp.kv_off, np.int64)
+    nb = (n_ent + BR - 1) // BR
+    bps = int(nb.max())
+    total = int(nb.sum())
+    perm = np.random.default_rng(seed).permutation(total).astype(np.int64)
+    table = np.zeros((Wr["B"], bps), np.int32)
+    src_rows, dst_rows = [], []
+    j0 = 0
+    for i in range(Wr["B"]):
+        for j in range(int(nb[i])):
+            phys = int(perm[j0 + j])
+            table[i, j] = phys
+            cnt = min(BR, int(n_ent[i]) - j * BR)
+            src_rows.append(np.arange(cnt) + off[i] + j * BR)
+            dst_rows.append(np.arange(cnt) + phys * BR)
+        j0 += int(nb[i])
+    src = torch.from_numpy(np.concatenate(src_rows)).cuda()
+    dst = torch.from_numpy(np.concatenate(dst_rows)).cuda()
+    Wp = dict(Wr)
+    for name, rb in (("kv", Wr["kv"].shape[-1]), ("keys", Wr["keys"].shape[-1])):
+        flat = Wr[name].reshape(-1, rb)
+        pool = torch.zeros((total * BR, rb), dtype=flat.dtype, device="cuda")
+        pool[dst] = flat[src]
+        Wp[name] = pool
+    last = n_ent - 1
+    Wp["seg_row"] = torch.from_numpy(table[np.arange(Wr["B"]), last // BR].astype(np.int64) * BR
+                                     + last % BR).cuda()
+    Wp["table"] = torch.from_numpy(table).cuda()
+    Wp["bps"], Wp["pool_rows"] = bps, total * BR
+    return Wp
+
+
+def make_paged_step(Wp):
+    """The decode step over paged caches: csa_compress_batch (the new rows go
+    to their pool rows), indexer_score_paged, topk_select,
+    hybrid_attn_decode_paged."""
+    c, inp = Wp["c"], Wp["inp"]
+    B, m, D, R, d_I, H, k = Wp["B"], Wp["m"], Wp["D"], Wp["R"], Wp["d_I"], c["H"], c["k"]
+    _, kern = make_step(Wp, check=False, fused=False)
+    k_compress, k_topk = kern[0][1], kern[2][1]
+    BR = PAGED_BLOCK_ROWS
+
+    def k_indexer():
+        csa.indexer_score_paged(Wp["q_idx"], Wp["w"], B, c["H_I"], d_I, Wp["keys"], csa.FP8, Wp["pool_rows"],
+                                Wp["table"], Wp["bps"], BR, Wp["q_pos"], m, Wp["scores"], Wp["ld"], check=False)
+
+    def k_attn():
+        csa.hybrid_attn_decode_paged(Wp["q"], csa.BF16, B, H, D, Wp["q_pos"], None, EPS, R, BASE, Wp["kv"],
+                                     csa.SPLIT, Wp["pool_rows"], Wp["table"], Wp["bps"], BR, m, Wp["idx"], k,
+                                     Wp["win"], csa.BF16, inp.n_win, Wp["win_len"], Wp["sinks"], inp.scale,
+                                     Wp["out"], csa.BF16, csa.VARIANT_AUTO, check=False)
+    kernels = [("csa_compress_batch", k_compress), ("indexer_score_paged", k_indexer), ("topk_select", k_topk),
+               ("hybrid_attn_decode_paged", k_attn)]
+
+    def step():
+        for _, f in kernels:
+            f()
+    return step, kernels
+
+
+def paged_leg(reps, steps, warmup):
+    """The headline step with its KV cache and index keys paged in 32-entry
+    blocks: ms per step and each kernel's time, against the contiguous step."""
+    pr = [paged_replica(Wr, 100 + j) for j, Wr in enumerate(reps)]
+    made = [make_paged_step(Wp) for Wp in pr]
+    for st, _ in made:
+        st()
+    torch.cuda.synchronize()
+    ms = time_graph([m_[0] for m_ in made], steps, warmup)
+    us, _ = time_kernels([m_[1] for m_ in made], max(20, min(100, steps)))
+    out = {"block_rows": PAGED_BLOCK_ROWS, "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
+           "kernels_us": {n: round(v, 2) for n, v in us.items()}}
+    del pr, made
+    torch.cuda.empty_cache()
+    return out
+
+
 def hca_leg(steps, warmup):
     """The HCA decode workload: 32 sequences of 262,144 tokens, m' = 128, so
     2,048 compressed entries per sequence, every one attended (no indexer, no
@@ -688,6 +774,8 @@ def main():
                     help="skip the HCA decode step (32 sequences of 262,144 tokens)")
     ap.add_argument("--no-ragged", action="store_true",
                     help="skip the ragged CSA (MXFP4) + HCA step (64 sequences, 1K to 1M tokens)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the headline step over paged caches (32-entry blocks)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the CSA prefill chunk (2,048 tokens after 131,072)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -771,6 +859,8 @@ def main():
         "copy_probe_gbps": copy_gbps(),
         "check_max_err_over_rms": err,
     }
+    if not args.no_paged:
+        line["paged"] = paged_leg(reps, args.steps, args.warmup)
     if not args.no_context_scan:
         line["context_scan"] = context_scan([262144, 1048576], args.steps, args.warmup)
     if not args.no_hca:
