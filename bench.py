@@ -471,6 +471,17 @@ def paged_replica(Wr, seed):
     last = n_ent - 1
     Wp["seg_row"] = torch.from_numpy(table[np.arange(Wr["B"]), last // BR].astype(np.int64) * BR
                                      + last % BR).cuda()
+    # the window as each request's ring (random start); the newest row goes
+    # to its ring slot
+    n_win = inp.n_win
+    wl = np.asarray(inp.win_len, np.int64)
+    start = np.random.default_rng(seed + 1).integers(0, n_win, size=Wr["B"]).astype(np.int64)
+    slots = (start[:, None] + np.arange(n_win)[None, :]) % n_win             # ring slot of window row t
+    ring = torch.empty_like(Wr["win"])
+    ring[torch.arange(Wr["B"]).cuda()[:, None], torch.from_numpy(slots).cuda()] = Wr["win"]
+    Wp["win"] = ring
+    Wp["win_start"] = torch.from_numpy(start.astype(np.int32)).cuda()
+    Wp["win_row"] = torch.from_numpy(np.arange(Wr["B"]) * n_win + (start + wl - 1) % n_win).cuda()
     Wp["table"] = torch.from_numpy(table).cuda()
     Wp["bps"], Wp["pool_rows"] = bps, total * BR
     return Wp
@@ -478,8 +489,8 @@ def paged_replica(Wr, seed):
 
 def make_paged_step(Wp):
     """The decode step over paged caches: csa_compress_batch (the new rows go
-    to their pool rows), indexer_score_paged, topk_select,
-    hybrid_attn_decode_paged."""
+    to their pool rows and window ring slots), indexer_score_paged,
+    topk_select, hybrid_attn_decode_paged."""
     c, inp = Wp["c"], Wp["inp"]
     B, m, D, R, d_I, H, k = Wp["B"], Wp["m"], Wp["D"], Wp["R"], Wp["d_I"], c["H"], c["k"]
     _, kern = make_step(Wp, check=False, fused=False)
@@ -494,7 +505,7 @@ def make_paged_step(Wp):
         csa.hybrid_attn_decode_paged(Wp["q"], csa.BF16, B, H, D, Wp["q_pos"], None, EPS, R, BASE, Wp["kv"],
                                      csa.SPLIT, Wp["pool_rows"], Wp["table"], Wp["bps"], BR, m, Wp["idx"], k,
                                      Wp["win"], csa.BF16, inp.n_win, Wp["win_len"], Wp["sinks"], inp.scale,
-                                     Wp["out"], csa.BF16, csa.VARIANT_AUTO, check=False)
+                                     Wp["out"], csa.BF16, csa.VARIANT_AUTO, check=False, win_start=Wp["win_start"])
     kernels = [("csa_compress_batch", k_compress), ("indexer_score_paged", k_indexer), ("topk_select", k_topk),
                ("hybrid_attn_decode_paged", k_attn)]
 
@@ -506,7 +517,8 @@ def make_paged_step(Wp):
 
 def paged_leg(reps, steps, warmup):
     """The headline step with its KV cache and index keys paged in 32-entry
-    blocks: ms per step and each kernel's time, against the contiguous step."""
+    blocks and its window kept as a ring: ms per step and each kernel's
+    time."""
     pr = [paged_replica(Wr, 100 + j) for j, Wr in enumerate(reps)]
     made = [make_paged_step(Wp) for Wp in pr]
     for st, _ in made:
@@ -514,7 +526,7 @@ def paged_leg(reps, steps, warmup):
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
     us, _ = time_kernels([m_[1] for m_ in made], max(20, min(100, steps)))
-    out = {"block_rows": PAGED_BLOCK_ROWS, "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
+    out = {"block_rows": PAGED_BLOCK_ROWS, "window": "ring", "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
            "kernels_us": {n: round(v, 2) for n, v in us.items()}}
     del pr, made
     torch.cuda.empty_cache()

@@ -61,7 +61,7 @@ def load_library():
     lib.indexer_score_paged.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I, P, I, P, I64, P]
     lib.hybrid_attn_decode_paged.restype = I
     lib.hybrid_attn_decode_paged.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, I64, P, I64, I, I, P, I, P, I, I,
-                                             P, P, F, P, I, I, P]
+                                             P, P, P, F, P, I, I, P]
     lib.indexer_score.restype = I
     lib.indexer_score.argtypes = [P, P, I, I, I, P, I, P, P, I, P, I64, P]
     lib.topk_select.restype = I
@@ -299,7 +299,8 @@ def hybrid_attn_decode(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_b
 
 def hybrid_attn_decode_paged(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt,
                              pool_rows, block_table, blocks_per_seq, block_rows, m, idx, k, win, win_fmt, n_win,
-                             win_len, sinks, scale, out, out_fmt, variant=VARIANT_AUTO, stream=None, check=True):
+                             win_len, sinks, scale, out, out_fmt, variant=VARIANT_AUTO, stream=None, check=True,
+                             win_start=None):
     lib = load_library()
     rb = row_bytes(kv_fmt, D, rope_dim)
     _need(q, "q", min_bytes=B * H * row_bytes(q_fmt, D, rope_dim))
@@ -312,11 +313,12 @@ def hybrid_attn_decode_paged(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, 
     if n_win > 0:
         _need(win, "win", min_bytes=B * n_win * row_bytes(win_fmt, D, rope_dim))
         _need(win_len, "win_len", torch.int32, min_numel=B)
+        _need(win_start, "win_start", torch.int32, min_numel=B, allow_none=True)
     _check(lib.hybrid_attn_decode_paged(_ptr(q), q_fmt, B, H, D, _ptr(q_pos), _ptr(q_norm_w), eps, rope_dim,
                                         rope_base, _ptr(kv_pool), kv_fmt, pool_rows, _ptr(block_table),
                                         blocks_per_seq, block_rows, m, _ptr(idx), k, _ptr(win), win_fmt, n_win,
-                                        _ptr(win_len), _ptr(sinks), scale, _ptr(out), out_fmt, variant,
-                                        _stream(stream)))
+                                        _ptr(win_start), _ptr(win_len), _ptr(sinks), scale, _ptr(out), out_fmt,
+                                        variant, _stream(stream)))
 
 
 def hybrid_attn_prefill(q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv, kv_fmt,

@@ -243,6 +243,7 @@ __device__ __forceinline__ float row_sum4(float v) {
 struct Work {
   int64_t p, N;
   int n_list, win_count, ns, n_steps, k;
+  int ring_start, ring_n;          // window ring: first slot, slots (ring_n = 0: rows in order)
   const int32_t* idx;              // this query's selected list (CSA) or nullptr
   buf_rsrc kv_rs, win_rs;
 };
@@ -312,10 +313,23 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
     return vmask;
   }
   const int j0 = (step - w.ns) * (kWaves * kStepW) + wv * kStepW;
+  if (w.ring_n > 0) {
+    // ring: window row j sits in slot (ring_start + j) mod n_win; a row past
+    // the window loads the first row again (finite data, masked: the ring's
+    // other slots may hold anything)
 #pragma unroll
-  for (int r = 0; r < kStepW; ++r)       // rows past the window read as zeros
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(w.win_rs, (lds_void*)(lds_ptr(dst + r * kPitchWin)),
-                                             16, lane * 16, (j0 + r) * kRowBf16, 0, 0);
+    for (int r = 0; r < kStepW; ++r) {
+      const int j = j0 + r < w.win_count ? j0 + r : 0;
+      const int slot = w.ring_start + j >= w.ring_n ? w.ring_start + j - w.ring_n : w.ring_start + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.win_rs, (lds_void*)(lds_ptr(dst + r * kPitchWin)), 16,
+                                               lane * 16, slot * kRowBf16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kStepW; ++r)       // rows past the window read as zeros
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.win_rs, (lds_void*)(lds_ptr(dst + r * kPitchWin)),
+                                               16, lane * 16, (j0 + r) * kRowBf16, 0, 0);
+  }
   const int nv = w.win_count - j0;
   return nv >= kStepW ? (1u << kStepW) - 1u : (nv <= 0 ? 0u : (1u << nv) - 1u);
 }
@@ -545,6 +559,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const bool paged = a.blk_table != nullptr;
   const int64_t p_ld = a.q_pos[b], kv0_ld = paged ? 0 : a.kv_off[b];
   const int wl_ld = a.win_mode == 1 ? a.win_len[b] : 0;
+  const int ws_ld = a.win_mode == 1 && a.win_start != nullptr ? a.win_start[b] : 0;
   const int64_t tp0_ld = a.win_mode == 2 ? a.tok_pos0[b] : 0, toff_ld = a.win_mode == 2 ? a.tok_off[b] : 0;
   const int32_t* idx_q = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
   int e_ld[kTabSteps / 4];
@@ -569,8 +584,13 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const uint64_t kv_bytes = static_cast<uint64_t>(paged ? a.pool_rows : w.N) * kRowSplit;
   w.kv_rs = make_rsrc(static_cast<const uint8_t*>(a.kv) + (paged ? 0 : kv0 * kRowSplit),
                       kv_bytes < 0xffffffffull ? static_cast<uint32_t>(kv_bytes) : 0xffffffffu);
+  w.ring_n = a.win_mode == 1 && a.win_start != nullptr && w.win_count > 0 ? a.n_win : 0;
+  {
+    const int ws = __builtin_amdgcn_readfirstlane(ws_ld);
+    w.ring_start = ws < 0 ? 0 : (ws >= a.n_win ? 0 : ws);   // out-of-range starts read from slot 0
+  }
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
-                       static_cast<uint32_t>(w.win_count) * kRowBf16);
+                       static_cast<uint32_t>(w.ring_n > 0 ? w.ring_n : w.win_count) * kRowBf16);
   EntryTab tab;
 #pragma unroll
   for (int t = 0; t < kTabSteps / 4; ++t) {

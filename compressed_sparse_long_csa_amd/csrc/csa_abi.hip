@@ -367,8 +367,8 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
                                     int64_t pool_rows, const int32_t* block_table, int64_t blocks_per_seq,
                                     int block_rows, int m, const int32_t* idx, int k,
                                     const void* win, csa_fmt win_fmt, int n_win,
-                                    const int32_t* win_len, const float* sinks, float scale,
-                                    void* out, csa_fmt out_fmt, csa_variant variant,
+                                    const int32_t* win_start, const int32_t* win_len, const float* sinks,
+                                    float scale, void* out, csa_fmt out_fmt, csa_variant variant,
                                     hipStream_t stream) {
   const char* what = "hybrid_attn_decode_paged";
   if (B > 0 && n_win > 0 && !win_len) return fail(CSA_ERR_INVALID_ARG, "%s: null win_len", what);
@@ -387,7 +387,7 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
   AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt, nullptr, m,
              idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
              scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,
-             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows};
+             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows, win_start};
   return attn_common(what, a, stream);
 }
 

@@ -81,6 +81,9 @@ struct AttnArgs {
   // unused): entry e of query b is pool row
   // blk_table[b * blk_stride + (e >> blk_shift)] * 2^blk_shift + (e mod 2^blk_shift)
   const int32_t* blk_table; int64_t blk_stride; int blk_shift; int64_t pool_rows;
+  // decode window kept as a ring (win_start != nullptr, MFMA path): window
+  // row t of query b is row b * n_win + (win_start[b] + t) mod n_win of win
+  const int32_t* win_start;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

@@ -361,11 +361,20 @@ csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
  *
  * Entry e of query b (e < N_b) is row
  *   block_table[b * blocks_per_seq + (e / block_rows)] * block_rows + e % block_rows
- * of kv_pool (pool_rows SPLIT rows).  Everything else -- the selected list
- * idx (logical entry numbers, ascending), the window, the sinks, the
- * reduction order -- is that of hybrid_attn_decode, and so are the output
- * bits: a query gives the same bits whether its entries are paged or
- * contiguous.
+ * of kv_pool (pool_rows SPLIT rows).  The window is the request's state
+ * cache, kept as a ring of n_win rows per query (硅星人 article,
+ * state-cache paragraph: the 128-token window KV is part of each request's
+ * state): window row t (t < win_len[b], oldest first) is row
+ *   b * n_win + (win_start[b] + t) mod n_win
+ * of win, so the newest token overwrites the oldest slot in place; win_start
+ * NULL means 0 (rows in order), and a win_start[b] outside [0, n_win) is
+ * taken as 0.  Everything else -- the selected list idx (logical entry
+ * numbers, ascending), the sinks, the reduction order -- is that of
+ * hybrid_attn_decode, and so are the output bits: a query gives the same
+ * bits whether its entries are paged or contiguous and its window a ring or
+ * in order.
+ *
+ *   win_start  [B] int32 or NULL
  *
  * Supported: the MFMA path (BF16 q / window / out, SPLIT cache, D = 512,
  * rope_dim = 64, H a multiple of 16) with a selected list (idx non-NULL,
@@ -382,8 +391,8 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
                                     int64_t pool_rows, const int32_t* block_table, int64_t blocks_per_seq,
                                     int block_rows, int m, const int32_t* idx, int k,
                                     const void* win, csa_fmt win_fmt, int n_win,
-                                    const int32_t* win_len, const float* sinks, float scale,
-                                    void* out, csa_fmt out_fmt, csa_variant variant,
+                                    const int32_t* win_start, const int32_t* win_len, const float* sinks,
+                                    float scale, void* out, csa_fmt out_fmt, csa_variant variant,
                                     hipStream_t stream);
 
 /*

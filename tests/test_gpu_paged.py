@@ -70,20 +70,37 @@ def test_indexer_paged_long_rows_interleaved_shares():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-def _attn_pair(inp, sel, BR, seed, variant):
+def _ring(win, win_len, rng):
+    """The window rows of every query moved into a ring at a random start;
+    the ring's other slots hold random bytes."""
+    B, n_win, rb = win.shape
+    ring = rng.integers(0, 256, size=win.shape, dtype=np.uint8)
+    start = rng.integers(0, n_win, size=B).astype(np.int32)
+    for b in range(B):
+        for t in range(int(win_len[b])):
+            ring[b, (start[b] + t) % n_win] = win[b, t]
+    return ring, start
+
+
+def _attn_pair(inp, sel, BR, seed, variant, ring=False):
     B, H, D = inp.B, inp.H, inp.D
     rb = synth.row_bytes(csa.SPLIT, D, inp.R)
-    pool, table, bps, pool_rows = _paginate(inp.kv.reshape(-1, rb), inp.n_ent, inp.kv_off, BR,
-                                            np.random.default_rng(seed))
+    rng = np.random.default_rng(seed)
+    pool, table, bps, pool_rows = _paginate(inp.kv.reshape(-1, rb), inp.n_ent, inp.kv_off, BR, rng)
     q, q_pos, win, win_len, sinks = dev(inp.q), dev(inp.q_pos), dev(inp.win), dev(inp.win_len), dev(inp.sinks)
+    pwin, pstart = win, None
+    if ring:
+        r, st = _ring(inp.win, inp.win_len, rng)
+        pwin, pstart = dev(r), dev(st)
     idx = dev(sel)
     outs = []
     for paged in (False, True):
         out = gpu_bytes(B * H * D * 2)
         if paged:
             csa.hybrid_attn_decode_paged(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(pool),
-                                         csa.SPLIT, pool_rows, dev(table), bps, BR, inp.m, idx, inp.k, win,
-                                         csa.BF16, inp.n_win, win_len, sinks, inp.scale, out, csa.BF16, variant)
+                                         csa.SPLIT, pool_rows, dev(table), bps, BR, inp.m, idx, inp.k, pwin,
+                                         csa.BF16, inp.n_win, win_len, sinks, inp.scale, out, csa.BF16, variant,
+                                         win_start=pstart)
         else:
             csa.hybrid_attn_decode(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(inp.kv),
                                    csa.SPLIT, dev(inp.kv_off), inp.m, idx, inp.k, win, csa.BF16, inp.n_win,
@@ -100,6 +117,17 @@ def test_attention_paged_matches_contiguous_bits(BR, k, variant):
     inp = synth.decode_inputs(620 + BR, lengths, m=4, H=64, D=512, R=64, k=k)
     sel = synth.random_selection(np.random.default_rng(9), inp.n_ent, k)
     a, b = _attn_pair(inp, sel, BR, 10, variant)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("variant", [csa.VARIANT_AUTO, csa.VARIANT_LOW_OCC])
+def test_attention_window_ring_matches_rows_in_order(variant):
+    """The request's window kept as a ring (random start, random bytes in the
+    free slots) gives the bits of the window stored in order."""
+    lengths = [65536, 9001, 2052, 130, 5, 3, 40000, 100]
+    inp = synth.decode_inputs(650, lengths, m=4, H=64, D=512, R=64, k=512)
+    sel = synth.random_selection(np.random.default_rng(13), inp.n_ent, 512)
+    a, b = _attn_pair(inp, sel, 32, 14, variant, ring=True)
     assert torch.equal(a, b)
 
 
