@@ -306,7 +306,7 @@ def hybrid_attn_decode_paged(q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, 
     _need(q, "q", min_bytes=B * H * row_bytes(q_fmt, D, rope_dim))
     _need(q_pos, "q_pos", torch.int64, min_numel=B)
     _need(q_norm_w, "q_norm_w", torch.float32, min_numel=D, allow_none=True)
-    _need(idx, "idx", torch.int32, min_numel=B * k)
+    _need(idx, "idx", torch.int32, min_numel=B * k, allow_none=True)
     _need(sinks, "sinks", torch.float32, min_numel=H)
     _need(out, "out", min_bytes=B * H * row_bytes(out_fmt, D, rope_dim))
     _paged_checks(block_table, B, blocks_per_seq, block_rows, kv_pool, pool_rows, rb, q_pos, m, 1 << 62, check)

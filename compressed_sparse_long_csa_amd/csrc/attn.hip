@@ -244,6 +244,9 @@ struct Work {
   int64_t p, N;
   int n_list, win_count, ns, n_steps, k;
   int ring_start, ring_n;          // window ring: first slot, slots (ring_n = 0: rows in order)
+  bool paged;                      // entries through the block table (list mode; HCA lists positions)
+  buf_rsrc tbl_rs;                 // the query's block-table row
+  int sh;                          // log2(rows per block)
   const int32_t* idx;              // this query's selected list (CSA) or nullptr
   buf_rsrc kv_rs, win_rs;
 };
@@ -258,12 +261,17 @@ struct EntryTab {
   uint64_t valid[kTabSteps / 4];
 };
 
-// Selected entry of list position pos, and whether it is a visible entry.
+// Selected entry of list position pos, and whether it is a visible entry
+// (paged: its pool row).  Without a selected list (HCA) position pos is
+// entry pos.
 __device__ __forceinline__ int list_entry(const Work& w, int pos, bool* ok) {
   // the load does not wait for the range test: its address is clamped
-  const int e = w.idx[pos < w.k ? pos : w.k - 1];
+  const int e = w.idx != nullptr ? w.idx[pos < w.k ? pos : w.k - 1] : pos;
   *ok = pos < w.n_list && e >= 0 && e < w.N;
-  return *ok ? e : 0;
+  const int el = *ok ? e : 0;
+  if (!w.paged) return el;
+  const int32_t blk = __builtin_amdgcn_raw_buffer_load_b32(w.tbl_rs, (el >> w.sh) * 4, 0, 0);
+  return static_cast<int>((static_cast<uint32_t>(blk) << w.sh) | (static_cast<uint32_t>(el) & ((1u << w.sh) - 1u)));
 }
 
 // Direct buffer->LDS loads of one wave step into `dst`; returns the step's
@@ -279,7 +287,7 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
     const int pos0 = step * (kWaves * kStepE) + wv * kStepE;
     uint32_t vmask;
     int ereg = 0, base = 0;
-    if (w.idx == nullptr) {
+    if (w.idx == nullptr && !w.paged) {
       const int nv = w.n_list - pos0;
       vmask = nv >= kStepE ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
     } else if (step < kTabSteps) {
@@ -296,7 +304,7 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
       vmask = static_cast<uint32_t>(__ballot(lane < kStepE && ok));
     }
     if (lane < kChunksSplit) {
-      if (w.idx == nullptr) {
+      if (w.idx == nullptr && !w.paged) {
         // (an HCA row past the query's N entries reads as zeros: buffer range check)
 #pragma unroll
         for (int r = 0; r < kStepE; ++r)
@@ -566,7 +574,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 #pragma unroll
   for (int t = 0; t < kTabSteps / 4; ++t) {
     const int pos = (4 * t + (lane >> 4)) * (kWaves * kStepE) + wv * kStepE + (lane & 15);
-    e_ld[t] = idx_q != nullptr ? idx_q[pos < a.k ? pos : a.k - 1] : 0;   // clamped address
+    e_ld[t] = idx_q != nullptr ? idx_q[pos < a.k ? pos : a.k - 1] : pos;   // clamped address; HCA: the position
   }
 
   Work w;
@@ -591,12 +599,16 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                        static_cast<uint32_t>(w.ring_n > 0 ? w.ring_n : w.win_count) * kRowBf16);
+  w.paged = paged;
+  w.sh = paged ? a.blk_shift : 0;
+  w.tbl_rs = make_rsrc(paged ? a.blk_table + static_cast<int64_t>(b) * a.blk_stride : nullptr,
+                       paged ? static_cast<uint32_t>(a.blk_stride * 4) : 0u);
   EntryTab tab;
 #pragma unroll
   for (int t = 0; t < kTabSteps / 4; ++t) {
     const int step = 4 * t + (lane >> 4);
     const int pos = step * (kWaves * kStepE) + wv * kStepE + (lane & 15);
-    const bool ok = w.idx != nullptr && step < w.ns && pos < w.n_list && e_ld[t] >= 0 && e_ld[t] < w.N;
+    const bool ok = (w.idx != nullptr || paged) && step < w.ns && pos < w.n_list && e_ld[t] >= 0 && e_ld[t] < w.N;
     tab.e[t] = ok ? e_ld[t] : 0;
     tab.valid[t] = __ballot(ok);
   }
@@ -604,13 +616,11 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
     // logical entry -> pool row through the query's block table (one more
     // dependent round trip before the first rows go out); a slot without an
     // entry maps entry 0 and stays masked
-    const int sh = a.blk_shift;
-    const buf_rsrc trs = make_rsrc(a.blk_table + static_cast<int64_t>(b) * a.blk_stride,
-                                   static_cast<uint32_t>(a.blk_stride * 4));
+    const int sh = w.sh;
     int32_t blk[kTabSteps / 4];
 #pragma unroll
     for (int t = 0; t < kTabSteps / 4; ++t)
-      blk[t] = __builtin_amdgcn_raw_buffer_load_b32(trs, (tab.e[t] >> sh) * 4, 0, 0);
+      blk[t] = __builtin_amdgcn_raw_buffer_load_b32(w.tbl_rs, (tab.e[t] >> sh) * 4, 0, 0);
 #pragma unroll
     for (int t = 0; t < kTabSteps / 4; ++t)
       tab.e[t] = static_cast<int>((static_cast<uint32_t>(blk[t]) << sh) | (static_cast<uint32_t>(tab.e[t]) & ((1u << sh) - 1u)));

@@ -375,7 +375,6 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
   if (!(q_fmt == CSA_BF16 && kv_fmt == CSA_SPLIT && win_fmt == CSA_BF16 && out_fmt == CSA_BF16))
     return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path is the MFMA path (BF16 q / window / out, SPLIT cache)",
                 what);
-  if (k < 1 || k > 1024) return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path takes 1 <= k <= 1024", what);
   if (block_rows < 1 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
     return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [1, 2^20]", what);
   if (blocks_per_seq < 1 || blocks_per_seq > (int64_t{1} << 26))
@@ -383,7 +382,7 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
   if (pool_rows < 1) return fail(CSA_ERR_INVALID_ARG, "%s: pool_rows must be >= 1", what);
   if (static_cast<uint64_t>(pool_rows) * row_bytes(CSA_SPLIT, D, rope_dim) > 0xffffffffull)
     return fail(CSA_ERR_UNSUPPORTED, "%s: the entry pool must be smaller than 4 GiB", what);
-  if (B > 0 && (!block_table || !idx)) return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (B > 0 && !block_table) return fail(CSA_ERR_INVALID_ARG, "%s: null block_table", what);
   AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt, nullptr, m,
              idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
              scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,

@@ -376,14 +376,17 @@ csa_status hybrid_attn_decode(const void* q, csa_fmt q_fmt, int B, int H, int D,
  *
  *   win_start  [B] int32 or NULL
  *
+ * idx NULL attends every visible entry (HCA; block_rows = 1 is one HCA entry
+ * per 128-token block).  Lists longer than 1024 positions (k > 1024, or HCA
+ * with N_b > 1024) map the positions past the first 1024 one step at a time
+ * inside the loop, which costs a dependent load per step.
  * Supported: the MFMA path (BF16 q / window / out, SPLIT cache, D = 512,
- * rope_dim = 64, H a multiple of 16) with a selected list (idx non-NULL,
- * 1 <= k <= 1024); block_rows a power of two in [1, 2^20]; a pool smaller than
- * 4 GiB.  HCA (idx NULL) and the F32 path: UNSUPPORTED.
+ * rope_dim = 64, H a multiple of 16); block_rows a power of two in [1, 2^20];
+ * a pool smaller than 4 GiB.  The F32 path: UNSUPPORTED.
  * Preconditions as for indexer_score_paged (blocks_per_seq * block_rows >=
  * N_b; used blocks inside the pool).
  * Errors: those of hybrid_attn_decode; INVALID_ARG for bad block_rows /
- * blocks_per_seq / pool_rows or a NULL block_table / idx.
+ * blocks_per_seq / pool_rows or a NULL block_table.
  */
 csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, int D,
                                     const int64_t* q_pos, const float* q_norm_w, float eps,

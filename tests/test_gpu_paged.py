@@ -82,7 +82,7 @@ def _ring(win, win_len, rng):
     return ring, start
 
 
-def _attn_pair(inp, sel, BR, seed, variant, ring=False):
+def _attn_pair(inp, sel, BR, seed, variant, ring=False, hca=False):
     B, H, D = inp.B, inp.H, inp.D
     rb = synth.row_bytes(csa.SPLIT, D, inp.R)
     rng = np.random.default_rng(seed)
@@ -92,18 +92,19 @@ def _attn_pair(inp, sel, BR, seed, variant, ring=False):
     if ring:
         r, st = _ring(inp.win, inp.win_len, rng)
         pwin, pstart = dev(r), dev(st)
-    idx = dev(sel)
+    idx = None if hca else dev(sel)
+    k = 0 if hca else inp.k
     outs = []
     for paged in (False, True):
         out = gpu_bytes(B * H * D * 2)
         if paged:
             csa.hybrid_attn_decode_paged(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(pool),
-                                         csa.SPLIT, pool_rows, dev(table), bps, BR, inp.m, idx, inp.k, pwin,
+                                         csa.SPLIT, pool_rows, dev(table), bps, BR, inp.m, idx, k, pwin,
                                          csa.BF16, inp.n_win, win_len, sinks, inp.scale, out, csa.BF16, variant,
                                          win_start=pstart)
         else:
             csa.hybrid_attn_decode(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(inp.kv),
-                                   csa.SPLIT, dev(inp.kv_off), inp.m, idx, inp.k, win, csa.BF16, inp.n_win,
+                                   csa.SPLIT, dev(inp.kv_off), inp.m, idx, k, win, csa.BF16, inp.n_win,
                                    win_len, sinks, inp.scale, out, csa.BF16, variant)
         outs.append(out)
     torch.cuda.synchronize()
@@ -111,12 +112,23 @@ def _attn_pair(inp, sel, BR, seed, variant, ring=False):
 
 
 @pytest.mark.parametrize("BR,k,variant", [(32, 512, csa.VARIANT_AUTO), (1, 512, csa.VARIANT_LOW_OCC),
-                                          (128, 1024, csa.VARIANT_HIGH_OCC), (32, 64, csa.VARIANT_AUTO)])
+                                          (128, 1024, csa.VARIANT_HIGH_OCC), (32, 64, csa.VARIANT_AUTO),
+                                          (32, 2048, csa.VARIANT_AUTO)])
 def test_attention_paged_matches_contiguous_bits(BR, k, variant):
     lengths = [65536, 9001, 2052, 130, 5, 3, 40000]
     inp = synth.decode_inputs(620 + BR, lengths, m=4, H=64, D=512, R=64, k=k)
     sel = synth.random_selection(np.random.default_rng(9), inp.n_ent, k)
     a, b = _attn_pair(inp, sel, BR, 10, variant)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("BR,variant", [(1, csa.VARIANT_AUTO), (4, csa.VARIANT_LOW_OCC), (16, csa.VARIANT_AUTO)])
+def test_hca_attention_paged_matches_contiguous_bits(BR, variant):
+    """HCA (every visible entry attended; one entry per 128-token block at
+    block_rows = 1), with lists past 1024 positions mapped inside the loop."""
+    lengths = [262144, 40000, 128, 127, 9000, 300000]
+    inp = synth.decode_inputs(660 + BR, lengths, m=128, H=64, D=512, R=64, csa=False)
+    a, b = _attn_pair(inp, None, BR, 15, variant, ring=True, hca=True)
     assert torch.equal(a, b)
 
 
