@@ -585,6 +585,24 @@ def hca_leg(steps, warmup):
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
     per_us, _ = time_kernels([m_[1] for m_ in made], max(20, min(60, steps)))
+    # the attention over a paged copy of the first state (one entry per
+    # block: the pages' one HCA entry per 128-token block, blocks shuffled)
+    # against the same contiguous state, both on that one copy
+    kv0 = states[0][0].view(-1, states[0][0].shape[-1])
+    n_rows = kv0.shape[0]
+    perm = torch.randperm(n_rows, generator=torch.Generator().manual_seed(c["seed"] + 3002))
+    pool = torch.empty_like(kv0)
+    pool[perm.cuda()] = kv0
+    table = torch.empty((B, int(n_ent.max())), dtype=torch.int32)
+    for b in range(B):
+        table[b, : int(n_ent[b])] = perm[int(kv_off_h[b]): int(kv_off_h[b]) + int(n_ent[b])].to(torch.int32)
+    table = table.cuda()
+    one = [[("contiguous", made[0][1][1][1]),
+            ("paged", lambda: csa.hybrid_attn_decode_paged(
+                d["q"], csa.BF16, B, H, D, q_pos, None, EPS, R, BASE, pool, csa.SPLIT, n_rows, table,
+                table.shape[1], 1, m, None, 0, states[0][1], csa.BF16, n_win, win_len, d["sinks"], d["scale"], out,
+                csa.BF16, csa.VARIANT_AUTO, check=False))]]
+    one_us, _ = time_kernels(one, max(20, min(60, steps)))
     split = (D - R) + 2 * R
     attended = n_ent.astype(np.int64) + win_len_h.astype(np.int64)
     a_bytes = int(n_ent.sum()) * split + int(win_len_h.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4
@@ -594,8 +612,9 @@ def hca_leg(steps, warmup):
            "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
            "attn_bytes": a_bytes, "attn_gbps": a_bytes / t / 1e9, "attn_hbm_frac": a_bytes / t / 1e9 / HBM_PEAK_GBPS,
            "attn_tflops": a_flops / t / 1e12, "attn_mfma_frac": a_flops / t / 1e12 / BF16_PEAK_TFLOPS,
-           "state_replicas": n_rep}
-    del states, made, d
+           "state_replicas": n_rep,
+           "attn_us_one_copy": {"contiguous": round(one_us["contiguous"], 2), "paged_block_rows_1": round(one_us["paged"], 2)}}
+    del states, made, d, pool, table
     torch.cuda.empty_cache()
     return res
 
