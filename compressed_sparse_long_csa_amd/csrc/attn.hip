@@ -244,7 +244,6 @@ struct Work {
   int64_t p, N;
   int n_list, win_count, ns, n_steps, k;
   int ring_start, ring_n;          // window ring: first slot, slots (ring_n = 0: rows in order)
-  bool paged;                      // entries through the block table (list mode; HCA lists positions)
   buf_rsrc tbl_rs;                 // the query's block-table row
   int sh;                          // log2(rows per block)
   const int32_t* idx;              // this query's selected list (CSA) or nullptr
@@ -264,12 +263,13 @@ struct EntryTab {
 // Selected entry of list position pos, and whether it is a visible entry
 // (paged: its pool row).  Without a selected list (HCA) position pos is
 // entry pos.
+template <bool PG>   // paged entries (the kernel instance for a block table)
 __device__ __forceinline__ int list_entry(const Work& w, int pos, bool* ok) {
   // the load does not wait for the range test: its address is clamped
   const int e = w.idx != nullptr ? w.idx[pos < w.k ? pos : w.k - 1] : pos;
   *ok = pos < w.n_list && e >= 0 && e < w.N;
   const int el = *ok ? e : 0;
-  if (!w.paged) return el;
+  if (!PG) return el;
   const int32_t blk = __builtin_amdgcn_raw_buffer_load_b32(w.tbl_rs, (el >> w.sh) * 4, 0, 0);
   return static_cast<int>((static_cast<uint32_t>(blk) << w.sh) | (static_cast<uint32_t>(el) & ((1u << w.sh) - 1u)));
 }
@@ -279,6 +279,7 @@ __device__ __forceinline__ int list_entry(const Work& w, int pos, bool* ok) {
 // entry load entry 0, or read as zeros past the end of the query's rows, and
 // stay masked.  A compressed step is 16 load instructions, a window step 8
 // (the loop's wait counts rely on it).
+template <bool PG>
 __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, const EntryTab& tab,
                                                uint8_t* dst) {
   const int lane = threadIdx.x & 63;
@@ -287,7 +288,7 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
     const int pos0 = step * (kWaves * kStepE) + wv * kStepE;
     uint32_t vmask;
     int ereg = 0, base = 0;
-    if (w.idx == nullptr && !w.paged) {
+    if (w.idx == nullptr && !PG) {
       const int nv = w.n_list - pos0;
       vmask = nv >= kStepE ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
     } else if (step < kTabSteps) {
@@ -300,11 +301,11 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
       vmask = static_cast<uint32_t>(vb >> base) & 0xffffu;
     } else {
       bool ok = false;
-      if (lane < kStepE) ereg = list_entry(w, pos0 + lane, &ok);
+      if (lane < kStepE) ereg = list_entry<PG>(w, pos0 + lane, &ok);
       vmask = static_cast<uint32_t>(__ballot(lane < kStepE && ok));
     }
     if (lane < kChunksSplit) {
-      if (w.idx == nullptr && !w.paged) {
+      if (w.idx == nullptr && !PG) {
         // (an HCA row past the query's N entries reads as zeros: buffer range check)
 #pragma unroll
         for (int r = 0; r < kStepE; ++r)
@@ -321,7 +322,7 @@ __device__ __forceinline__ uint32_t issue_step(const Work& w, int step, int wv, 
     return vmask;
   }
   const int j0 = (step - w.ns) * (kWaves * kStepW) + wv * kStepW;
-  if (w.ring_n > 0) {
+  if (PG && w.ring_n > 0) {
     // ring: window row j sits in slot (ring_start + j) mod n_win; a row past
     // the window loads the first row again (finite data, masked: the ring's
     // other slots may hold anything)
@@ -369,7 +370,7 @@ __device__ __forceinline__ float softmax_step(const float (&t)[4], float (&pv)[4
 // 16 compressed entries (or 8 window rows); the MFMA tiles are 16 rows and 32
 // (16) deep, so the second half of a tile multiplies probabilities set to zero
 // by rows of the same step (finite data) -- it adds nothing.
-template <int NB, int NF>
+template <int NB, int NF, bool PG>
 __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, const bf16x8 (&qb)[kD / 32],
                                            float ch, int dbase, float& m_run, float& l_run,
                                            f32x4 (&acc)[NB], const EntryTab& tab, uint32_t vmask_cur) {
@@ -381,7 +382,7 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
     // two steps of rows are in flight while a step computes
     uint32_t vmask_next = 0u;
     if (step + 1 < w.n_steps) {
-      vmask_next = issue_step(w, step + 1, wv, tab, ws.buf[bi ^ 1]);
+      vmask_next = issue_step<PG>(w, step + 1, wv, tab, ws.buf[bi ^ 1]);
       if (step + 1 < w.ns) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepE));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepW));
     } else {
@@ -523,7 +524,9 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, int wv, 
 // 512 / DVS output dims; every wave of it accumulates all of them over its
 // own entries, and the eight partial states are merged at the end in wave
 // order.
-template <int DVS>
+// PG: the instance for paged caches (block table, ring window); the other
+// instance carries none of that addressing.
+template <int DVS, bool PG>
 __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_units,
                                                              int n_pad) {
   constexpr int DWG = kD / DVS;        // output dims of this workgroup
@@ -564,10 +567,10 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
   const double theta = a.rope_theta[tid < kR / 2 ? tid : 0];
   const float sink = a.sinks[ht * 16 + j16];
-  const bool paged = a.blk_table != nullptr;
+  constexpr bool paged = PG;
   const int64_t p_ld = a.q_pos[b], kv0_ld = paged ? 0 : a.kv_off[b];
   const int wl_ld = a.win_mode == 1 ? a.win_len[b] : 0;
-  const int ws_ld = a.win_mode == 1 && a.win_start != nullptr ? a.win_start[b] : 0;
+  const int ws_ld = PG && a.win_mode == 1 && a.win_start != nullptr ? a.win_start[b] : 0;
   const int64_t tp0_ld = a.win_mode == 2 ? a.tok_pos0[b] : 0, toff_ld = a.win_mode == 2 ? a.tok_off[b] : 0;
   const int32_t* idx_q = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
   int e_ld[kTabSteps / 4];
@@ -592,14 +595,13 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   const uint64_t kv_bytes = static_cast<uint64_t>(paged ? a.pool_rows : w.N) * kRowSplit;
   w.kv_rs = make_rsrc(static_cast<const uint8_t*>(a.kv) + (paged ? 0 : kv0 * kRowSplit),
                       kv_bytes < 0xffffffffull ? static_cast<uint32_t>(kv_bytes) : 0xffffffffu);
-  w.ring_n = a.win_mode == 1 && a.win_start != nullptr && w.win_count > 0 ? a.n_win : 0;
+  w.ring_n = PG && a.win_mode == 1 && a.win_start != nullptr && w.win_count > 0 ? a.n_win : 0;
   {
     const int ws = __builtin_amdgcn_readfirstlane(ws_ld);
     w.ring_start = ws < 0 ? 0 : (ws >= a.n_win ? 0 : ws);   // out-of-range starts read from slot 0
   }
   w.win_rs = make_rsrc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                        static_cast<uint32_t>(w.ring_n > 0 ? w.ring_n : w.win_count) * kRowBf16);
-  w.paged = paged;
   w.sh = paged ? a.blk_shift : 0;
   w.tbl_rs = make_rsrc(paged ? a.blk_table + static_cast<int64_t>(b) * a.blk_stride : nullptr,
                        paged ? static_cast<uint32_t>(a.blk_stride * 4) : 0u);
@@ -627,7 +629,7 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
   }
   // the first step's rows go out before the query is prepared
   uint32_t vmask0 = 0u;
-  if (w.n_steps > 0) vmask0 = issue_step(w, 0, wv, tab, ws.buf[0]);
+  if (w.n_steps > 0) vmask0 = issue_step<PG>(w, 0, wv, tab, ws.buf[0]);
 
   if (tid < kR / 2) {
     float sn, cs;
@@ -712,9 +714,9 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(AttnArgs a, int n_u
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (dbase + DWG <= kDF8)
-    entry_loop<NB, NB>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
+    entry_loop<NB, NB, PG>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
   else
-    entry_loop<NB, NFR>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
+    entry_loop<NB, NFR, PG>(w, ws, wv, qb, ch, dbase, m_run, l_run, acc, tab, vmask0);
 
   // -------- merge the waves' states in wave order, then out = acc / (2^8 * l)
   __syncthreads();                                      // every wave is done with its buffers
@@ -790,21 +792,31 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (attr_set_dev != dev) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<2>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mfma_kernel<8>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
-    if (e != hipSuccess) return e;
+    const void* fns[] = {reinterpret_cast<const void*>(&attn_mfma_kernel<2, false>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<4, false>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<8, false>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<2, true>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<4, true>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<8, true>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm));
+      if (e != hipSuccess) return e;
+    }
     attr_set_dev = dev;
   }
-  switch (dvs) {
-    case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
-    case 4: hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
-    default: hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3(n_pad), dim3(kThreads), shm, stream, a, units, n_pad); break;
+  const dim3 g(n_pad), blk(kThreads);
+  if (a.blk_table != nullptr) {
+    switch (dvs) {
+      case 2: hipLaunchKernelGGL((attn_mfma_kernel<2, true>), g, blk, shm, stream, a, units, n_pad); break;
+      case 4: hipLaunchKernelGGL((attn_mfma_kernel<4, true>), g, blk, shm, stream, a, units, n_pad); break;
+      default: hipLaunchKernelGGL((attn_mfma_kernel<8, true>), g, blk, shm, stream, a, units, n_pad); break;
+    }
+  } else {
+    switch (dvs) {
+      case 2: hipLaunchKernelGGL((attn_mfma_kernel<2, false>), g, blk, shm, stream, a, units, n_pad); break;
+      case 4: hipLaunchKernelGGL((attn_mfma_kernel<4, false>), g, blk, shm, stream, a, units, n_pad); break;
+      default: hipLaunchKernelGGL((attn_mfma_kernel<8, false>), g, blk, shm, stream, a, units, n_pad); break;
+    }
   }
   return hipGetLastError();
 }
