@@ -422,21 +422,24 @@ __global__ void __launch_bounds__(256) compress_score_kernel(CompressJobs J, int
 
 // --------------------------------------------------------------- FP8, d = 128, shared keys
 // A prefill batch holds many queries of one sequence, which read the same key
-// rows.  A workgroup takes kShareQ = 4 consecutive queries (one per wave) and
-// a run of up to kShareGroups 64-key groups.  When the four read the same
-// rows (equal key offsets), each group is loaded once -- wave w loads block w
-// with the lane pattern of the streaming kernel -- widened once into LDS, and
-// every wave multiplies it against its own query.  The operands, MFMA tiles,
+// rows.  A workgroup takes QS consecutive queries (one per wave; QS = 8, or 4
+// for 128 heads, whose registers leave no room for the longer step) and a
+// run of up to kShareGroups 64-key groups.  When they read the same rows
+// (equal key offsets), the keys go by in steps of QS blocks of 16: each step
+// is loaded once -- wave w loads block w with the lane pattern of the
+// streaming kernel -- widened once into LDS, and every wave multiplies it
+// against its own query (QS queries share each widening).  The operands, MFMA tiles,
 // their order and the head sum are those of the streaming kernel, so a score
 // has the same bits whichever kernel computed it.  Keys past a query's own N
 // are multiplied but their scores are not stored.  A block whose queries read
 // different rows streams each wave's own groups instead.
-constexpr int kShareQ = 4;
+template <int NHB> constexpr int share_q() { return NHB >= 8 ? 4 : 8; }
 constexpr int kShareGroups = 32;
 constexpr int kShareMinQueries = 1024;   // batches this large take the shared-key kernel
 
+template <int QS>
 struct SharedKeys {
-  bf16x8 k[2][4][4][64];   // [buffer][block][k-step][lane]
+  bf16x8 k[2][QS][4][64];   // [buffer][block][k-step][lane]
 };
 
 // One 16-key block from widened operands: the per-block step of group_fp8.
@@ -462,10 +465,12 @@ __device__ __forceinline__ void block_bf16(const bf16x8 (&kk)[4], const bf16x8 (
 }
 
 template <int NHB>
-__global__ void __launch_bounds__(256) indexer_fp8_shared_kernel(IndexerArgs a, int64_t n_qblk,
-                                                                 int64_t n_kchunk) {
+__global__ void __launch_bounds__(share_q<NHB>() * 64) indexer_fp8_shared_kernel(IndexerArgs a, int64_t n_qblk,
+                                                                                 int64_t n_kchunk) {
   constexpr int H = NHB * 16;
-  __shared__ SharedKeys sk;
+  constexpr int kShareQ = share_q<NHB>();
+  constexpr uint32_t kShareStepKeys = kShareQ * 16;   // keys per step: one 16-key block per wave
+  __shared__ SharedKeys<kShareQ> sk;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, j16 = lane & 15;
@@ -520,46 +525,48 @@ __global__ void __launch_bounds__(256) indexer_fp8_shared_kernel(IndexerArgs a, 
     for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     int pend = -1;
     if (same) {
-      // wave wv loads block wv of every group: rows t*64 + wv*16 + j16, bytes [32g, 32g+32)
+      // wave wv loads block wv of every step: rows k0 + s*kShareStepKeys + wv*16 + j16, bytes [32g, 32g+32)
       const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + koff0 * 128,
                                     static_cast<uint32_t>(N_max * 128));
-      const uint32_t voff0 = (t0 * kGroupKeys + static_cast<uint32_t>(wv) * 16u + j16) * 128u + g * 32u;
-      // group t -> buffer (t - t0) % 2; its loads went out two groups earlier
-      auto load = [&](uint4 (&kr)[2], uint32_t t) __attribute__((always_inline)) {
-        const uint32_t o = t < t1 ? voff0 + (t - t0) * (kGroupKeys * 128u) : 0x80000000u;   // past t1: no traffic
+      const uint32_t k0 = t0 * kGroupKeys;                 // first key of the run
+      const uint32_t n_st = ((t1 - t0) * kGroupKeys + kShareStepKeys - 1) / kShareStepKeys;
+      const uint32_t voff0 = (k0 + static_cast<uint32_t>(wv) * 16u + j16) * 128u + g * 32u;
+      // step s -> buffer s % 2; its loads went out two steps earlier
+      auto load = [&](uint4 (&kr)[2], uint32_t st) __attribute__((always_inline)) {
+        const uint32_t o = st < n_st ? voff0 + st * (kShareStepKeys * 128u) : 0x80000000u;   // past the run: no traffic
         kr[0] = buf_load_x4(rs, o, 0);
         kr[1] = buf_load_x4(rs, o + 16u, 0);
       };
-      auto step = [&](uint4 (&kr)[2], uint32_t t, int buf) __attribute__((always_inline)) {
+      auto step = [&](uint4 (&kr)[2], uint32_t st, int buf) __attribute__((always_inline)) {
         bf16x8* dst = &sk.k[buf][wv][0][lane];
         dst[0] = fp8x8_to_bf16(kr[0].x, kr[0].y);
         dst[64] = fp8x8_to_bf16(kr[0].z, kr[0].w);
         dst[128] = fp8x8_to_bf16(kr[1].x, kr[1].y);
         dst[192] = fp8x8_to_bf16(kr[1].z, kr[1].w);
-        // the buffer holds the whole group once every wave's LDS writes are
-        // done (and every wave has read the group two back from it); the
+        // the buffer holds the whole step once every wave's LDS writes are
+        // done (and every wave has read the step two back from it); the
         // barrier waits for LDS only, so the key loads stay in flight
         asm volatile("" : : : "memory");
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" : : : "memory");
-        load(kr, t + 2);                                 // two groups ahead
-        asm volatile("" : : : "memory");                 // (issued before the group's LDS reads)
+        load(kr, st + 2);                                // two steps ahead
+        asm volatile("" : : : "memory");                 // (issued before the step's LDS reads)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < kShareQ; ++kb) {
           const bf16x8 kk[4] = {sk.k[buf][kb][0][lane], sk.k[buf][kb][1][lane], sk.k[buf][kb][2][lane],
                                 sk.k[buf][kb][3][lane]};
-          block_bf16<NHB>(kk, qb, wr, cp, pend, static_cast<int>((t * kGroupKeys + kb * 16u) * 4u), out_rs,
-                          out_off);
+          block_bf16<NHB>(kk, qb, wr, cp, pend, static_cast<int>((k0 + st * kShareStepKeys + kb * 16u) * 4u),
+                          out_rs, out_off);
         }
       };
       uint4 ka[2], kb2[2];
-      load(ka, t0);
+      load(ka, 0);
       asm volatile("" : : : "memory");                   // in this order: the loop's waits count on it
-      load(kb2, t0 + 1);
-      for (uint32_t t = t0; t < t1; t += 2) {
-        step(ka, t, 0);
-        if (t + 1 < t1) step(kb2, t + 1, 1);             // uniform over the workgroup
+      load(kb2, 1);
+      for (uint32_t st = 0; st < n_st; st += 2) {
+        step(ka, st, 0);
+        if (st + 1 < n_st) step(kb2, st + 1, 1);         // uniform over the workgroup
       }
     } else {
       // the wave's own rows, group by group (no barriers: the branch is
@@ -862,16 +869,21 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     }                                                                                                    \
     break;
   if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries && !paged) {
-    const int64_t n_qblk = (a.nq + kShareQ - 1) / kShareQ;
+    // QS queries (waves) per workgroup; resident workgroups per CU from the
+    // kernel's register count (two waves per SIMD at 64 heads and more)
+    const int qs = nhb >= 8 ? share_q<8>() : share_q<1>();
+    const int64_t n_qblk = (a.nq + qs - 1) / qs;
     const int64_t n_kchunk = ((a.ld + kGroupKeys - 1) / kGroupKeys + kShareGroups - 1) / kShareGroups;
     const int64_t units = n_qblk * n_kchunk;
-    const int64_t cap_o = static_cast<int64_t>(device_cu_count()) * (nhb <= 2 ? 4 : 2);   // resident workgroups
+    const int64_t waves_cu = nhb <= 2 ? 16 : 8;
+    const int64_t cap_o = static_cast<int64_t>(device_cu_count()) * (waves_cu / qs);   // resident workgroups
     const unsigned grid_s = static_cast<unsigned>(units < cap_o ? units : cap_o);
+    const dim3 blk(static_cast<unsigned>(qs * 64));
     switch (nhb) {
-      case 1: hipLaunchKernelGGL(indexer_fp8_shared_kernel<1>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
-      case 2: hipLaunchKernelGGL(indexer_fp8_shared_kernel<2>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
-      case 4: hipLaunchKernelGGL(indexer_fp8_shared_kernel<4>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
-      case 8: hipLaunchKernelGGL(indexer_fp8_shared_kernel<8>, dim3(grid_s), dim3(256), 0, stream, a, n_qblk, n_kchunk); break;
+      case 1: hipLaunchKernelGGL(indexer_fp8_shared_kernel<1>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
+      case 2: hipLaunchKernelGGL(indexer_fp8_shared_kernel<2>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
+      case 4: hipLaunchKernelGGL(indexer_fp8_shared_kernel<4>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
+      case 8: hipLaunchKernelGGL(indexer_fp8_shared_kernel<8>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

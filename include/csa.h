@@ -194,9 +194,9 @@ csa_status csa_compress_batch(const csa_compress_job* jobs /*[host]*/, int n_job
  *   scores  [nq, ld] float32
  * Supported: F32 any n_heads <= 64, d_idx <= 256; FP8 / MXFP4 with n_heads a
  * multiple of 16 (<= 128) and d_idx == 128.  Else UNSUPPORTED.  FP8 batches
- * of 1024 queries or more (prefill chunks) run a kernel in which four
- * queries with the same key_off share each load of their keys; a score has
- * the same bits from either kernel.
+ * of 1024 queries or more (prefill chunks) run a kernel in which eight
+ * queries (four at 128 heads) with the same key_off share each load and
+ * widening of their keys; a score has the same bits from either kernel.
  * Errors: INVALID_ARG for ld < 1 or ld > 2^24 (16.7M entries, 64M tokens at
  * m = 4), m < 1, nq < 0, null pointers, a format other than the three above.
  */
