@@ -175,3 +175,33 @@ def test_compress_score_argument_errors(lib):
     assert call([key_job()], ld=0) == INVALID
     assert lib.csa_compress_score(None, 0, p, p, 0, 64, 128, keys, csa.FP8, p, p, 4, p,
                                   ctypes.c_int64(1024), None) == OK   # nothing to do
+
+
+def test_paged_entry_points_argument_errors(lib):
+    """indexer_score_paged / hybrid_attn_decode_paged: block geometry, pool
+    size and format checks run on the host before any launch."""
+    p, tbl = _fake(), _fake(3)
+
+    def idx(fmt=csa.FP8, pool_rows=1000, bps=10, br=32, d=128):
+        return lib.indexer_score_paged(p, p, 2, 64, d, p, fmt, ctypes.c_int64(pool_rows), tbl,
+                                       ctypes.c_int64(bps), br, p, 4, p, ctypes.c_int64(1024), None)
+    assert idx(br=24) == INVALID                   # not a power of two
+    assert idx(br=8) == INVALID                    # below one 16-key MFMA block
+    assert idx(bps=0) == INVALID
+    assert idx(pool_rows=0) == INVALID
+    assert idx(pool_rows=1 << 26) == UNSUPPORTED   # 8 GiB of 128-byte keys: past 32-bit offsets
+    assert idx(fmt=csa.F32) == UNSUPPORTED
+    assert idx(d=96) == UNSUPPORTED
+    assert "indexer_score_paged" in _last_error(lib)
+
+    def att(q_fmt=csa.BF16, kv_fmt=csa.SPLIT, br=32, bps=10, pool_rows=1000, table=tbl):
+        return lib.hybrid_attn_decode_paged(p, q_fmt, 2, 64, 512, p, None, ctypes.c_float(1e-6), 64,
+                                            ctypes.c_float(1e4), p, kv_fmt, ctypes.c_int64(pool_rows), table,
+                                            ctypes.c_int64(bps), br, 4, p, 512, p, csa.BF16, 128, None, p, p,
+                                            ctypes.c_float(0.04), p, csa.BF16, 0, None)
+    assert att(br=3) == INVALID
+    assert att(bps=0) == INVALID
+    assert att(pool_rows=1 << 23) == UNSUPPORTED   # 4.8 GB of 576-byte entries
+    assert att(q_fmt=csa.F32, kv_fmt=csa.F32) == UNSUPPORTED
+    assert att(table=None) == INVALID
+    assert "hybrid_attn_decode_paged" in _last_error(lib)
