@@ -3,7 +3,7 @@ row), indexer_score, topk_select, hybrid_attn_decode, or the same step with
 csa_compress_score in place of the first two -- captured in one HIP graph and
 replayed: every replay, with eager work and synchronisation between replays,
 gives the bits of the eager step.  Also the CSA prefill indexer (shared-key
-kernel) and top-k captured together."""
+kernel) and top-k captured together, and the decode step over paged caches."""
 import numpy as np
 import pytest
 import torch
@@ -130,4 +130,35 @@ def test_prefill_indexer_and_topk_in_a_graph():
     def bufs():
         return (torch.full((chunk, n_tot), -7.0, dtype=torch.float32, device=DEV),
                 torch.empty((chunk, k), dtype=torch.int32, device=DEV))
+    _replay_matches(run, bufs)
+
+
+def test_paged_decode_step_in_a_graph():
+    """indexer_score_paged -> topk_select -> hybrid_attn_decode_paged over
+    shuffled 32-entry blocks and ring windows, captured and replayed."""
+    from test_gpu_paged import _paginate, _ring
+    inp = synth.decode_inputs(91, [65536, 9001, 2052, 130, 40000], m=4, H=64, D=512, R=64, k=512)
+    B, ld, k, BR = inp.B, int(inp.n_ent.max()), inp.k, 32
+    rng = np.random.default_rng(92)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    kpool, ktab, kbps, krows = _paginate(inp.keys.reshape(-1, 128), inp.n_ent, inp.kv_off, BR, rng)
+    vpool, vtab, vbps, vrows = _paginate(inp.kv.reshape(-1, 576), inp.n_ent, inp.kv_off, BR, rng)
+    ring, start = _ring(inp.win, inp.win_len, rng)
+    d = dict(q_idx=dv(inp.q_idx), w=dv(inp.w), q_pos=dv(inp.q_pos), nv=dv(inp.n_ent), q=dv(inp.q),
+             kpool=dv(kpool), ktab=dv(ktab), vpool=dv(vpool), vtab=dv(vtab), win=dv(ring), start=dv(start),
+             win_len=dv(inp.win_len), sinks=dv(inp.sinks))
+
+    def run(scores, idx, out, check):
+        csa.indexer_score_paged(d["q_idx"], d["w"], B, 64, 128, d["kpool"], csa.FP8, krows, d["ktab"], kbps, BR,
+                                d["q_pos"], 4, scores, ld, check=check)
+        csa.topk_select(scores, ld, B, d["nv"], k, idx, None, check=check)
+        csa.hybrid_attn_decode_paged(d["q"], csa.BF16, B, 64, 512, d["q_pos"], None, EPS, 64, ROPE_BASE, d["vpool"],
+                                     csa.SPLIT, vrows, d["vtab"], vbps, BR, 4, idx, k, d["win"], csa.BF16,
+                                     inp.n_win, d["win_len"], d["sinks"], inp.scale, out, csa.BF16,
+                                     csa.VARIANT_AUTO, check=check, win_start=d["start"])
+
+    def bufs():
+        return (torch.full((B, ld), -7.0, dtype=torch.float32, device=DEV),
+                torch.empty((B, k), dtype=torch.int32, device=DEV),
+                torch.empty((B, 64, 512), dtype=torch.bfloat16, device=DEV))
     _replay_matches(run, bufs)
