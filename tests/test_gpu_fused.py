@@ -151,3 +151,33 @@ def test_fused_rejects_a_key_job_of_the_wrong_shape():
     with pytest.raises(csa.CsaError):
         csa.csa_compress_score([bad], st["q_idx"], st["w"], 2, inp.H_I, inp.d_I, keys, csa.FP8, st["kv_off"],
                                st["q_pos"], M, scores, st["ld"], check=False)
+
+
+def test_fused_scores_independent_of_batch_order():
+    """The one-launch step gives every query the same score bits whatever the
+    order of the batch (its segments permuted with it), and writes the same
+    key rows (QbitAI piece on batch invariance)."""
+    lengths = [65536, 9000, 2052, 132, 8, 40000, 4, 3]
+    new = np.array([True, False, True, True, True, False, True, False])
+    st = _case(lengths, new, 64, csa.FP8, 707)
+    keys0, _, s0 = _run(st, True)
+    perm = np.random.default_rng(708).permutation(st["B"])
+    inp = st["inp"]
+    seg_len = np.where(new, M, 0).astype(np.int64)
+    # the same tokens, segments re-ordered with the queries
+    tok_first = np.concatenate([[0], np.cumsum(seg_len)])[:-1]
+    order = np.concatenate([np.arange(tok_first[b], tok_first[b] + seg_len[b]) for b in perm]).astype(np.int64)
+    sp = dict(st)
+    sp["seg_off"] = dev(np.concatenate([[0], np.cumsum(seg_len[perm])]).astype(np.int64))
+    sp["pos0"] = dev(st["pos0"].cpu().numpy()[perm])
+    sp["rows"] = dev(st["rows"].cpu().numpy()[perm])
+    idx_t = torch.as_tensor(order, device=DEV) if order.size else None
+    for name in ("key_tok", "key_gate", "kv_tok", "kv_gate"):
+        sp[name] = st[name][idx_t].contiguous() if idx_t is not None else st[name]
+    sp["q_idx"] = dev(inp.q_idx[perm])
+    sp["w"] = dev(inp.w[perm])
+    sp["kv_off"] = dev(inp.kv_off[perm])
+    sp["q_pos"] = dev(inp.q_pos[perm])
+    keys1, _, s1 = _run(sp, True)
+    assert np.array_equal(keys1, keys0)
+    assert np.array_equal(s1.view(np.uint32), s0[perm].view(np.uint32))
