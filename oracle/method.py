@@ -56,6 +56,8 @@ READINGS = {
     "A13 sink": "z_h is on the scaled-logit scale; exp(z_h) joins the denominator only",
     "A14 overlap": "window and compressed entries are both used, no de-duplication",
     "A15 window": "min(n_win, p+1) tokens ending at p inclusive",
+    "A25 empty set": "a query with no compressed entry and no window row attends nothing: "
+                     "its output is the empty weighted sum, 0, for every sink value",
 }
 
 ROPE_BASE = 10000.0
@@ -180,6 +182,11 @@ def sink_attention(qhat, ents, z, scale, return_weight=False):
     qhat = np.asarray(qhat, np.float64)
     ents = np.asarray(ents, np.float64)
     z = np.asarray(z, np.float64)
+    if ents.shape[0] == 0:
+        # nothing attended: the numerator is an empty sum, so the output is 0
+        # whatever the sink (for z = -inf the denominator is empty too)
+        o = np.zeros((qhat.shape[0], ents.shape[1] if ents.ndim == 2 else qhat.shape[1]))
+        return (o, np.zeros(qhat.shape[0])) if return_weight else o
     logits = scale * (qhat @ ents.T)                              # [H, n]
     M = np.maximum(z, logits.max(axis=1) if ents.shape[0] else -np.inf)
     e = np.exp(logits - M[:, None])

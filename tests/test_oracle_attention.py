@@ -62,6 +62,25 @@ def test_sink_large_z_sends_weight_to_zero_with_logistic_law():
     assert np.all(np.abs(o) < 1e-80) and np.all(W < 1e-80)
 
 
+def test_minus_infinity_sink_and_empty_set():
+    """z = -inf is plain softmax attention (torch SDPA without the extra key);
+    an empty attended set gives the zero vector for every z, -inf included."""
+    rng = np.random.default_rng(4)
+    H, D, n = 4, 32, 9
+    qhat = rng.standard_normal((H, D))
+    ents = rng.standard_normal((n, D))
+    got = M.sink_attention(qhat, ents, np.full(H, -np.inf), 0.3)
+    q = torch.from_numpy(qhat).reshape(H, 1, D)
+    kv = torch.from_numpy(ents).expand(H, n, D)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kv, kv, scale=0.3).reshape(H, D).numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    z = np.array([-np.inf, -1.0, 0.0, 60.0])
+    o, W = M.sink_attention(qhat, np.zeros((0, D)), z, 0.3, return_weight=True)
+    assert o.shape == (H, D) and np.all(o == 0.0) and np.all(W == 0.0)
+    o = M.decode_one(rng.standard_normal((H, D)), 2, np.zeros((0, D)), np.zeros((0, D)), z, 0.3, 4)
+    assert np.all(o == 0.0)
+
+
 def test_single_entry_and_equal_logits_closed_forms():
     rng = np.random.default_rng(3)
     H, D = 5, 8
