@@ -15,15 +15,16 @@ import torch
 
 F32, BF16, FP8, MXFP4, SPLIT = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_HIGH_OCC, VARIANT_LOW_OCC = 0, 1, 2
-_STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_HIP"}
+_STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_HIP",
+           4: "CSA_ERR_WORKSPACE"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libcsa.so")
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
            "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
-           "indexer_score_paged", "topk_select", "hybrid_attn_decode", "hybrid_attn_decode_paged",
-           "hybrid_attn_prefill")
+           "indexer_score_paged", "topk_select", "csa_topk_workspace_bytes", "hybrid_attn_decode",
+           "hybrid_attn_decode_paged", "hybrid_attn_prefill")
 
 _lib = None
 
@@ -65,7 +66,9 @@ def load_library():
     lib.indexer_score.restype = I
     lib.indexer_score.argtypes = [P, P, I, I, I, P, I, P, P, I, P, I64, P]
     lib.topk_select.restype = I
-    lib.topk_select.argtypes = [P, I64, I, P, I, P, P, P]
+    lib.topk_select.argtypes = [P, I64, I, P, I, P, P, P, U, P]
+    lib.csa_topk_workspace_bytes.restype = U
+    lib.csa_topk_workspace_bytes.argtypes = [I, I64, I]
     lib.hybrid_attn_decode.restype = I
     lib.hybrid_attn_decode.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, P, I, P, I, P, I, I, P,
                                        P, F, P, I, I, P]
@@ -254,14 +257,27 @@ def _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, 
             raise ValueError("a query's visible keys run past the end of `keys`")
 
 
-def topk_select(scores, ld, nq, n_valid, k, idx, top_scores=None, stream=None, check=True):
+def topk_workspace_bytes(nq, ld, k):
+    """Device bytes topk_select needs as workspace for these sizes (0: none)."""
+    return int(load_library().csa_topk_workspace_bytes(nq, ld, k))
+
+
+def topk_select(scores, ld, nq, n_valid, k, idx, top_scores=None, stream=None, check=True, workspace=None):
+    """workspace: a uint8 device tensor of at least topk_workspace_bytes(nq, ld, k)
+    bytes; when None and one is needed, a fresh one is taken from torch's
+    allocator for this call (calls that may overlap must not share one)."""
     lib = load_library()
     _need(scores, "scores", torch.float32, min_numel=nq * ld)
     _need(n_valid, "n_valid", torch.int64, min_numel=nq, allow_none=True)
     _need(idx, "idx", torch.int32, min_numel=nq * k)
     _need(top_scores, "top_scores", torch.float32, min_numel=nq * k, allow_none=True)
+    ws_need = int(lib.csa_topk_workspace_bytes(nq, ld, k))
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=scores.device)
+    _need(workspace, "workspace", allow_none=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.topk_select(_ptr(scores), ld, nq, _ptr(n_valid), k, _ptr(idx), _ptr(top_scores),
-                           _stream(stream)))
+                           _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def _attn_checks(q, q_fmt, nq, H, D, q_pos, q_norm_w, kv, kv_fmt, kv_off, m, idx, k, sinks, out,

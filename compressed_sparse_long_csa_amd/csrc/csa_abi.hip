@@ -59,6 +59,7 @@ const char* csa_status_string(csa_status s) {
     case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG";
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
     case CSA_ERR_HIP: return "CSA_ERR_HIP";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE";
     default: return "CSA_ERR_UNKNOWN";
   }
 }
@@ -288,23 +289,35 @@ csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const vo
   return launched(e, what);
 }
 
+size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k) {
+  if (nq <= 0 || ld < 1 || k < 1 || k > 4096 || ld > (int64_t{1} << 28)) return 0;
+  return plan_topk(ld, nq, k).ws_bytes;
+}
+
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
-                       int32_t* idx, float* top_scores, hipStream_t stream) {
+                       int32_t* idx, float* top_scores, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
   if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "topk_select: nq < 0");
   if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "topk_select: k must be in [1, 4096]");
   if (ld < 1 || ld > (int64_t{1} << 28))
     return fail(CSA_ERR_INVALID_ARG, "topk_select: ld must be in [1, 2^28]");
+  if (nq > kTopkMaxRows)
+    return fail(CSA_ERR_INVALID_ARG, "topk_select: nq must be <= %d", kTopkMaxRows);
   if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
   if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "topk_select: null pointer");
+  const TopkPlan pl = plan_topk(ld, nq, k);
+  if (static_cast<int64_t>(nq) * pl.P > kTopkMaxRows)
+    return fail(CSA_ERR_INVALID_ARG, "topk_select: nq * %d slices exceeds %d workgroups", pl.P, kTopkMaxRows);
+  if (pl.ws_bytes > 0) {
+    if (!workspace || ws_bytes < pl.ws_bytes)
+      return fail(CSA_ERR_WORKSPACE, "topk_select: rows of %lld scores need a %zu-byte workspace, got %zu%s",
+                  static_cast<long long>(ld), pl.ws_bytes, workspace ? ws_bytes : size_t{0},
+                  workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(CSA_ERR_WORKSPACE, "topk_select: the workspace must be 16-byte aligned");
+  }
   TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};
-  bool capturing = false;
-  const hipError_t e = launch_topk(a, stream, &capturing);
-  if (capturing)
-    return fail(CSA_ERR_UNSUPPORTED,
-                "topk_select: rows longer than 33792 need a %zu-byte device workspace, which "
-                "cannot be allocated during stream capture: make one call of this size first",
-                plan_topk(ld, nq, k).ws_bytes);
-  return launched(e, "topk_select");
+  return launched(launch_topk(a, workspace, stream), "topk_select");
 }
 
 static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream) {

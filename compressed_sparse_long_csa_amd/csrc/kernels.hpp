@@ -58,9 +58,12 @@ struct TopkArgs {
 // Long rows (ld > 33792) take two passes through a device workspace: P slices
 // of Cs scores, ws_bytes of candidates (P = 0: one pass, no workspace).
 struct TopkPlan { int P; uint32_t Cs; size_t ws_bytes; };
+// Rows (or rows x slices) of one launch: one 1024-thread workgroup each, so
+// the grid stays below 2^32 threads.
+constexpr int kTopkMaxRows = 1 << 22;
 TopkPlan plan_topk(int64_t ld, int nq, int k);
-// *capturing is set when the workspace would have to grow during stream capture.
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream, bool* capturing);
+// ws: at least plan_topk(...).ws_bytes of device memory (unused when P = 0).
+hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream);
 
 // Attention over [selected or all compressed entries] ++ [window rows].
 // The window of query b is `win_count` consecutive rows starting at row

@@ -30,8 +30,6 @@
 // reduction costs one barrier.  The result is the exact set, ascending,
 // whatever the batch or launch.  Loads and stores go through buffer
 // descriptors, so slots past a row's end need neither branches nor clamps.
-#include <mutex>
-
 #include "kernels.hpp"
 
 namespace csa {
@@ -530,34 +528,6 @@ uint32_t stage_cap(uint64_t n) {
 }
 size_t stage_bytes(uint32_t cap) { return cap ? (static_cast<size_t>(cap) + kStageSlack) * sizeof(float) : 0; }
 
-// Candidate workspace of the long-row path, one per device, grown on demand
-// and never freed (a captured graph may still use an old one).
-std::mutex g_ws_mu;
-struct Workspace { void* ptr = nullptr; size_t bytes = 0; };
-Workspace g_ws[64];
-
-hipError_t workspace(size_t bytes, hipStream_t stream, void** out, bool* capturing) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace& w = g_ws[dev];
-  if (w.bytes < bytes) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &st);
-    if (e != hipSuccess) return e;
-    if (st != hipStreamCaptureStatusNone) { *capturing = true; return hipErrorStreamCaptureUnsupported; }
-    void* p = nullptr;
-    e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) return e;
-    w.ptr = p;
-    w.bytes = bytes;
-  }
-  *out = w.ptr;
-  return hipSuccess;
-}
-
 }  // namespace
 
 TopkPlan plan_topk(int64_t ld, int nq, int k) {
@@ -573,8 +543,7 @@ TopkPlan plan_topk(int64_t ld, int nq, int k) {
   return pl;
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream, bool* capturing) {
-  *capturing = false;
+hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
   if (a.nq == 0) return hipSuccess;
   static thread_local int configured_dev = -1;
   int dev = 0;
@@ -595,9 +564,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream, bool* capturing) {
     hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), stage_bytes(cap), stream, a, cap);
     return hipGetLastError();
   }
-  void* ws = nullptr;
-  e = workspace(pl.ws_bytes, stream, &ws, capturing);
-  if (e != hipSuccess) return e;
   const size_t per = static_cast<size_t>(a.nq) * pl.P * a.k;
   int32_t* cidx = static_cast<int32_t*>(ws);
   float* cscore = reinterpret_cast<float*>(cidx + per);

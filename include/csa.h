@@ -19,11 +19,11 @@
  *     kernels on `stream` and returns; nothing is synchronised.  On any status
  *     other than CSA_OK nothing was enqueued, except CSA_ERR_HIP, which reports
  *     a failed launch.  csa_last_error() returns a thread-local message.
- *   - The caller owns every buffer.  The library keeps no pointer after
- *     returning and never writes `const` inputs; it allocates nothing except
- *     topk_select's per-device workspace for rows longer than 33792 scores
- *     (see there).  Calls on different streams touching disjoint outputs may
- *     run concurrently.
+ *   - The caller owns every buffer, scratch memory included (topk_select's
+ *     workspace, sized by csa_topk_workspace_bytes).  The library allocates
+ *     no device memory, keeps no pointer after returning and never writes
+ *     `const` inputs.  Calls on different streams touching disjoint outputs
+ *     and disjoint workspaces may run concurrently.
  *   - Row formats (csa_fmt), for a row of D values:
  *       CSA_F32    4*D bytes, float32
  *       CSA_BF16   2*D bytes, bfloat16
@@ -50,13 +50,14 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
   CSA_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, a mismatch */
   CSA_ERR_UNSUPPORTED = 2, /* a valid combination the library has no kernel for */
-  CSA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+  CSA_ERR_HIP = 3,         /* the HIP runtime refused a launch */
+  CSA_ERR_WORKSPACE = 4    /* a required workspace is missing, too small or misaligned */
 } csa_status;
 
 typedef enum csa_fmt {
@@ -68,11 +69,11 @@ typedef enum csa_fmt {
 } csa_fmt;
 
 typedef enum csa_variant {
-  CSA_VARIANT_AUTO = 0,     /* the fewest workgroups per (query, 16 heads) -- 2, 4
-                               or 8 -- that still give every CU one */
+  CSA_VARIANT_AUTO = 0,     /* the fewest workgroups per (query, 16 heads) -- 2
+                               or 4 -- that still give every CU one */
   CSA_VARIANT_HIGH_OCC = 1, /* two workgroups per (query, 16 heads), 256 output
                                dims each: for a batch that fills the GPU */
-  CSA_VARIANT_LOW_OCC = 2   /* eight, 64 output dims each: for a small batch.
+  CSA_VARIANT_LOW_OCC = 2   /* four, 128 output dims each: for a small batch.
                                All variants give the same bits (the fp32 path
                                has one kernel and ignores the variant). */
 } csa_variant;
@@ -295,18 +296,27 @@ csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_
  * not be NaN.  n_valid is clamped to [0, ld] on the device.
  *
  *   scores  [nq, ld] float32;  idx [nq, k] int32;  top_scores [nq, k] or NULL
- * Rows longer than 33792 scores (ld > 33792) are selected in two passes
- * (slices of the row, then a merge of the slices' sets) through a device
- * workspace of nq * P * k * 8 bytes (P <= 64 slices) that the library keeps
- * per device, grows on demand and never frees.  Calls with such rows that
- * overlap on one device (different streams) share it and race.
+ * Rows longer than 33792 scores (ld > 33792) are selected in two passes: P
+ * slices of about 16K scores each give their own exact top-k (P = min(
+ * ceil(ld / 16384), max(2, 16384 / k))), written into a candidate row, and
+ * the row's top-k is selected from the candidates.  The candidates live in
+ * `workspace`, caller-owned device memory of at least
+ * csa_topk_workspace_bytes(nq, ld, k) bytes (nq * P * k * 8), 16-byte
+ * aligned; its contents on entry do not matter and are left undefined.
+ * When that size is 0 (ld <= 33792) workspace may be NULL.  Two calls that
+ * may run at the same time need two workspaces.  nq * P must not exceed
+ * 2^22 (one 1024-thread workgroup per row or slice).
  * Errors: INVALID_ARG for k < 1, k > 4096, ld < 1, ld > 2^28, nq < 0,
- * null pointers; UNSUPPORTED when the workspace would have to grow while
- * `stream` is being captured into a graph (make one call of that size
- * before capturing); HIP when it cannot be allocated.
+ * nq * P > 2^22, null pointers; WORKSPACE when a workspace is needed and is
+ * NULL, smaller than required or misaligned.
  */
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
-                       int32_t* idx, float* top_scores, hipStream_t stream);
+                       int32_t* idx, float* top_scores, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Bytes of workspace topk_select needs for nq rows of ld scores and this k
+ * (0: none); 0 as well for arguments topk_select rejects. */
+size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k);
 
 /*
  * hybrid_attn_decode -- sink multi-query attention of one decode token per
@@ -330,10 +340,13 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
  *   l_j  = scale * qhat . e_j                (the stored entry is key and value)
  *   out[b,h] = sum_j e^{l_j} e_j / (sum_j e^{l_j} + e^{sinks[h]})
  * The reduction order over E is fixed per token, the same in every variant
- * and batch.  F32 path: E in list order from the sink.  MFMA path: eight
- * interleaved slices -- slice w takes list positions [128 s + 16 w, +16) of
- * the compressed part and window rows [64 t + 8 w, +8) -- each reduced in
- * order (the sink enters slice 0), then merged in slice order.
+ * and batch.  F32 path: E in list order.  MFMA path: four interleaved
+ * slices -- slice w takes list positions [64 s + 16 w, +16) of the
+ * compressed part and window rows [64 t + 16 w, +16) -- each reduced in
+ * order, then merged in slice order.  In both the sink joins the denominator after
+ * the entries (so sinks[h] = -inf is standard softmax and a large sinks[h]
+ * scales the output down without underflowing the weights); a query with
+ * nothing to attend gets a zero output.
  *
  *   q, out   [B, H] rows of D values (q_fmt / out_fmt: F32 or BF16)
  *   kv       rows of D values in kv_fmt (SPLIT, or F32 on the fp32 path)

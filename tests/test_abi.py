@@ -38,7 +38,8 @@ def test_every_declared_function_is_exported(lib):
 def test_version_status_strings_and_row_bytes(lib):
     assert lib.csa_abi_version() >= 1
     lib.csa_status_string.restype = ctypes.c_char_p
-    for code, name in ((0, b"CSA_OK"), (1, b"CSA_ERR_INVALID_ARG"), (2, b"CSA_ERR_UNSUPPORTED")):
+    for code, name in ((0, b"CSA_OK"), (1, b"CSA_ERR_INVALID_ARG"), (2, b"CSA_ERR_UNSUPPORTED"),
+                       (3, b"CSA_ERR_HIP"), (4, b"CSA_ERR_WORKSPACE")):
         assert lib.csa_status_string(code) == name
     lib.csa_row_bytes.restype = ctypes.c_size_t
     for fmt in (csa.F32, csa.BF16, csa.FP8, csa.MXFP4, csa.SPLIT):
@@ -62,12 +63,40 @@ def _fake(n=1):
 def test_topk_argument_errors(lib):
     p = _fake()
     for ld, nq, k, want in ((100, 1, 0, INVALID), (100, 1, 4097, INVALID), (0, 1, 8, INVALID),
-                            ((1 << 28) + 1, 1, 8, INVALID), (100, -1, 8, INVALID)):
-        st = lib.topk_select(p, ctypes.c_int64(ld), nq, None, k, p, None, None)
+                            ((1 << 28) + 1, 1, 8, INVALID), (100, -1, 8, INVALID), (100, (1 << 22) + 1, 8, INVALID)):
+        st = lib.topk_select(p, ctypes.c_int64(ld), nq, None, k, p, None, None, 0, None)
         assert st == want, (ld, nq, k, st)
         assert "topk_select" in _last_error(lib)
-    assert lib.topk_select(None, ctypes.c_int64(100), 1, None, 8, None, None, None) == INVALID
-    assert lib.topk_select(None, ctypes.c_int64(100), 0, None, 8, None, None, None) == OK
+    assert lib.topk_select(None, ctypes.c_int64(100), 1, None, 8, None, None, None, 0, None) == INVALID
+    assert lib.topk_select(None, ctypes.c_int64(100), 0, None, 8, None, None, None, 0, None) == OK
+    # rows x slices past 2^22 workgroups: rejected before anything is launched
+    assert lib.topk_select(p, ctypes.c_int64(1 << 20), 1 << 20, None, 512, p, None, p, 1 << 62, None) == INVALID
+
+
+WORKSPACE = 4
+
+
+def test_topk_workspace_contract(lib):
+    """Rows up to 33792 scores need no workspace; longer rows need nq * P * k * 8
+    bytes of caller memory (P slices of about 16K scores), and a missing, short
+    or misaligned workspace is refused with CSA_ERR_WORKSPACE before any launch."""
+    wsb = lib.csa_topk_workspace_bytes
+    assert wsb(16, 16384, 512) == 0 and wsb(4, 33792, 1024) == 0
+    assert wsb(16, 262144, 512) == 16 * 16 * 512 * 8             # P = 16 slices of 16384
+    assert wsb(64, 262144, 1024) == 64 * 16 * 1024 * 8            # P = min(16, 16384 / 1024)
+    assert wsb(3, 1048576, 512) == 3 * 32 * 512 * 8               # P = 16384 / 512 = 32
+    assert wsb(2, 40000, 4096) == 2 * 3 * 4096 * 8                # P = ceil(40000 / 16384)
+    assert wsb(0, 262144, 512) == 0 and wsb(4, 262144, 0) == 0    # rejected sizes
+    assert csa.topk_workspace_bytes(16, 262144, 512) == wsb(16, 262144, 512)
+    p = _fake()
+    need = wsb(16, 262144, 512)
+    assert lib.topk_select(p, ctypes.c_int64(262144), 16, None, 512, p, None, None, need, None) == WORKSPACE
+    assert "workspace" in _last_error(lib)
+    assert lib.topk_select(p, ctypes.c_int64(262144), 16, None, 512, p, None, p, need - 1, None) == WORKSPACE
+    assert lib.topk_select(p, ctypes.c_int64(262144), 16, None, 512, p, None, ctypes.c_void_p(0x1004), need,
+                           None) == WORKSPACE
+    lib.csa_status_string.restype = ctypes.c_char_p
+    assert lib.csa_status_string(WORKSPACE) == b"CSA_ERR_WORKSPACE"
 
 
 def test_compress_argument_errors(lib):

@@ -302,19 +302,21 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
 
 
 def test_topk_long_rows_in_a_graph():
-    """The long-row path (slices, then a candidate merge through the library's
+    """The long-row path (slices, then a candidate merge through the caller's
     workspace) captured in a HIP graph: every replay, with eager work in
     between, gives the eager result."""
     nq, ld, k = 3, 200000, 1024
     s, nv = synth.random_scores(77, nq, ld, [200000, 150000, 34000], 0)
     S, NV = dev(s), dev(nv)
+    ws = torch.empty(csa.topk_workspace_bytes(nq, ld, k), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > 0
     eager = torch.empty((nq, k), dtype=torch.int32, device=DEV)
-    csa.topk_select(S, ld, nq, NV, k, eager)           # sizes the workspace outside capture
+    csa.topk_select(S, ld, nq, NV, k, eager)
     torch.cuda.synchronize()
     out = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        csa.topk_select(S, ld, nq, NV, k, out, check=False)
+        csa.topk_select(S, ld, nq, NV, k, out, check=False, workspace=ws)
     for _ in range(3):
         out.fill_(-7)
         g.replay()
@@ -327,6 +329,54 @@ def test_topk_long_rows_in_a_graph():
     for i in range(nq):
         want = OM.top_k(s[i, : nv[i]].astype(np.float64), k)
         assert np.array_equal(eager.cpu().numpy()[i, : len(want)], want)
+
+
+def test_topk_long_rows_on_two_streams():
+    """Two long-row selections running concurrently on two streams, each with
+    its own workspace, give the bits each gives alone (the caller owns the
+    scratch, so concurrent calls do not share it)."""
+    k = 512
+    sa, nva = synth.random_scores(78, 8, 262144, [262144] * 6 + [100000, 40000], 0)
+    sb, nvb = synth.random_scores(79, 5, 1048576, [1048576, 700000, 300000, 40000, 1048575], 3)
+    A, NA, B_, NB = dev(sa), dev(nva), dev(sb), dev(nvb)
+    ref_a = torch.empty((8, k), dtype=torch.int32, device=DEV)
+    ref_b = torch.empty((5, k), dtype=torch.int32, device=DEV)
+    csa.topk_select(A, 262144, 8, NA, k, ref_a)
+    csa.topk_select(B_, 1048576, 5, NB, k, ref_b)
+    torch.cuda.synchronize()
+    wa = torch.empty(csa.topk_workspace_bytes(8, 262144, k), dtype=torch.uint8, device=DEV)
+    wb = torch.empty(csa.topk_workspace_bytes(5, 1048576, k), dtype=torch.uint8, device=DEV)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(4):
+        oa = torch.full((8, k), -7, dtype=torch.int32, device=DEV)
+        ob = torch.full((5, k), -7, dtype=torch.int32, device=DEV)
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s1):
+            csa.topk_select(A, 262144, 8, NA, k, oa, workspace=wa, stream=s1)
+        with torch.cuda.stream(s2):
+            csa.topk_select(B_, 1048576, 5, NB, k, ob, workspace=wb, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b), f"repetition {rep}"
+        outs.append(oa)
+    for i in range(5):
+        want = OM.top_k(sb[i, : nvb[i]].astype(np.float64), k)
+        assert np.array_equal(ref_b.cpu().numpy()[i, : len(want)], want)
+
+
+def test_topk_workspace_errors_on_the_device_path():
+    """A short workspace is refused before anything runs: the outputs keep
+    their contents."""
+    nq, ld, k = 2, 100000, 512
+    s, nv = synth.random_scores(80, nq, ld, None, 0)
+    out = torch.full((nq, k), -7, dtype=torch.int32, device=DEV)
+    need = csa.topk_workspace_bytes(nq, ld, k)
+    short = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(csa.CsaError, match="WORKSPACE"):
+        csa.topk_select(dev(s), ld, nq, dev(nv), k, out, workspace=short)
+    torch.cuda.synchronize()
+    assert torch.all(out == -7)
 
 
 @pytest.mark.parametrize("ld", [20000, 40000])
