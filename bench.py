@@ -344,10 +344,7 @@ def spot_check(W):
                         W["m"], idx=sel, R=W["R"])
     got = OF.decode_rows(W["out"][b].view(torch.uint8).cpu().numpy(), csa.BF16, W["D"]).reshape(ref.shape)
     rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-    ax = np.abs(ref)
-    _, e = np.frexp(np.where(ax > 0, ax, 1.0))
-    slack = np.where(ax > 0, np.ldexp(1.0, e - 9), 0.0)
-    return float((np.maximum(np.abs(got - ref) - slack, 0) / rms).max())
+    return float((np.abs(got - ref) / rms).max())
 
 
 def cpu_baseline(W, budget_s=12.0):

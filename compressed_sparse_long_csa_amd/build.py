@@ -21,9 +21,12 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-# per-file additions: the indexer keeps MFMA results in VGPRs (its head sum
-# reads every result element, and AGPR results would need a copy each)
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-file additions: the indexer and the attention keep MFMA results in
+# VGPRs (the indexer's head sum reads every result element; the attention's
+# accumulators are rescaled by VALU, and AGPR-held results would be copied
+# through VGPRs at every loop iteration)
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

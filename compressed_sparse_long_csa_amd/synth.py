@@ -50,8 +50,10 @@ def _fp8_bytes(x32):
     return t.view(torch.uint8).numpy().reshape(x32.shape)
 
 
-def random_rows(rng, n, D, fmt, R=0, chunk=1 << 16):
-    """n rows of N(0,1) values stored in `fmt`; uint8 [n, row_bytes]."""
+def random_rows(rng, n, D, fmt, R=0, chunk=1 << 16, mx_scales=(124, 128)):
+    """n rows of N(0,1) values stored in `fmt`; uint8 [n, row_bytes].  MXFP4
+    rows hold uniform random E2M1 codes and E8M0 scale bytes drawn uniformly
+    from [mx_scales[0], mx_scales[1])."""
     rb = row_bytes(fmt, D, R)
     out = np.empty((n, rb), dtype=np.uint8)
     for a in range(0, n, chunk):
@@ -59,7 +61,7 @@ def random_rows(rng, n, D, fmt, R=0, chunk=1 << 16):
         if fmt == MXFP4:
             codes = rng.integers(0, 16, size=(b - a, D), dtype=np.uint8)
             out[a:b, : D // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
-            out[a:b, D // 2:] = rng.integers(124, 128, size=(b - a, D // 32), dtype=np.uint8)
+            out[a:b, D // 2:] = rng.integers(mx_scales[0], mx_scales[1], size=(b - a, D // 32), dtype=np.uint8)
             continue
         x = rng.standard_normal((b - a, D), dtype=np.float32)
         if fmt == F32:
@@ -114,10 +116,11 @@ class DecodeInputs:
 
 
 def decode_inputs(seed, lengths, *, m, H, D, R, n_win=128, kv_fmt=SPLIT, q_fmt=BF16,
-                  win_fmt=BF16, csa=True, k=512, idx_fmt=FP8, H_I=64, d_I=128, rng=None):
+                  win_fmt=BF16, csa=True, k=512, idx_fmt=FP8, H_I=64, d_I=128, rng=None,
+                  mx_scales=(124, 128)):
     """Seeded decode batch.  Draw order: lengths (given) -> cache entries ->
     window rows -> queries -> index keys -> index queries -> head weights ->
-    sinks."""
+    sinks.  mx_scales: range of the E8M0 scale bytes of MXFP4 index rows."""
     rng = rng or rng_for(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
     B = lengths.shape[0]
@@ -130,8 +133,8 @@ def decode_inputs(seed, lengths, *, m, H, D, R, n_win=128, kv_fmt=SPLIT, q_fmt=B
     q = random_rows(rng, B * H, D, q_fmt, R).reshape(B, H, row_bytes(q_fmt, D, R))
     keys = q_idx = w = None
     if csa:
-        keys = random_rows(rng, int(n_ent.sum()), d_I, idx_fmt)
-        q_idx = random_rows(rng, B * H_I, d_I, idx_fmt).reshape(B, H_I, row_bytes(idx_fmt, d_I))
+        keys = random_rows(rng, int(n_ent.sum()), d_I, idx_fmt, mx_scales=mx_scales)
+        q_idx = random_rows(rng, B * H_I, d_I, idx_fmt, mx_scales=mx_scales).reshape(B, H_I, row_bytes(idx_fmt, d_I))
         w = rng.uniform(0.0, 1.0, size=(B, H_I)).astype(np.float32)
     sinks = rng.standard_normal(H).astype(np.float32)
     return DecodeInputs(B=B, H=H, D=D, R=R, m=m, n_win=n_win, lengths=lengths,
