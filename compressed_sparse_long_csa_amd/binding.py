@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
            "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
-           "indexer_score_paged", "topk_select", "csa_topk_workspace_bytes", "hybrid_attn_decode",
+           "indexer_score_paged", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
+           "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
            "hybrid_attn_decode_paged", "hybrid_attn_prefill")
 
 _lib = None
@@ -69,6 +70,10 @@ def load_library():
     lib.topk_select.argtypes = [P, I64, I, P, I, P, P, P, U, P]
     lib.csa_topk_workspace_bytes.restype = U
     lib.csa_topk_workspace_bytes.argtypes = [I, I64, I]
+    lib.topk_select_noalloc.restype = I
+    lib.topk_select_noalloc.argtypes = [P, I64, I, P, I, P, P, P]
+    lib.csa_topk_noalloc_max_bytes.restype = U
+    lib.csa_topk_noalloc_max_bytes.argtypes = []
     lib.hybrid_attn_decode.restype = I
     lib.hybrid_attn_decode.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, P, I, P, I, P, I, I, P,
                                        P, F, P, I, I, P]
@@ -278,6 +283,24 @@ def topk_select(scores, ld, nq, n_valid, k, idx, top_scores=None, stream=None, c
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.topk_select(_ptr(scores), ld, nq, _ptr(n_valid), k, _ptr(idx), _ptr(top_scores),
                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def topk_noalloc_max_bytes():
+    """Size of topk_select_noalloc's static candidate array (per GPU)."""
+    return int(load_library().csa_topk_noalloc_max_bytes())
+
+
+def topk_select_noalloc(scores, ld, nq, n_valid, k, idx, top_scores=None, stream=None):
+    """topk_select without a workspace: the library's static per-GPU array holds
+    the candidates, so nothing is allocated.  Calls that may overlap on one GPU
+    race on that array."""
+    lib = load_library()
+    _need(scores, "scores", torch.float32, min_numel=nq * ld)
+    _need(n_valid, "n_valid", torch.int64, min_numel=nq, allow_none=True)
+    _need(idx, "idx", torch.int32, min_numel=nq * k)
+    _need(top_scores, "top_scores", torch.float32, min_numel=nq * k, allow_none=True)
+    _check(lib.topk_select_noalloc(_ptr(scores), ld, nq, _ptr(n_valid), k, _ptr(idx), _ptr(top_scores),
+                                   _stream(stream)))
 
 
 def _attn_checks(q, q_fmt, nq, H, D, q_pos, q_norm_w, kv, kv_fmt, kv_off, m, idx, k, sinks, out,

@@ -294,20 +294,30 @@ size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k) {
   return plan_topk(ld, nq, k).ws_bytes;
 }
 
+namespace {
+// Checks shared by both top-k entry points; *pl receives the launch plan.
+csa_status topk_check(const char* name, const float* scores, int64_t ld, int nq, int k, const int32_t* idx,
+                      TopkPlan* pl) {
+  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "%s: nq < 0", name);
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "%s: k must be in [1, 4096]", name);
+  if (ld < 1 || ld > (int64_t{1} << 28)) return fail(CSA_ERR_INVALID_ARG, "%s: ld must be in [1, 2^28]", name);
+  if (nq > kTopkMaxRows) return fail(CSA_ERR_INVALID_ARG, "%s: nq must be <= %d", name, kTopkMaxRows);
+  if (nq == 0) return CSA_OK;
+  if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", name);
+  *pl = plan_topk(ld, nq, k);
+  if (static_cast<int64_t>(nq) * pl->P > kTopkMaxRows)
+    return fail(CSA_ERR_INVALID_ARG, "%s: nq * %d slices exceeds %d workgroups", name, pl->P, kTopkMaxRows);
+  return CSA_OK;
+}
+}  // namespace
+
 csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
                        int32_t* idx, float* top_scores, void* workspace, size_t ws_bytes,
                        hipStream_t stream) {
-  if (nq < 0) return fail(CSA_ERR_INVALID_ARG, "topk_select: nq < 0");
-  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "topk_select: k must be in [1, 4096]");
-  if (ld < 1 || ld > (int64_t{1} << 28))
-    return fail(CSA_ERR_INVALID_ARG, "topk_select: ld must be in [1, 2^28]");
-  if (nq > kTopkMaxRows)
-    return fail(CSA_ERR_INVALID_ARG, "topk_select: nq must be <= %d", kTopkMaxRows);
+  TopkPlan pl{};
+  const csa_status st = topk_check("topk_select", scores, ld, nq, k, idx, &pl);
+  if (st != CSA_OK) return st;
   if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
-  if (!scores || !idx) return fail(CSA_ERR_INVALID_ARG, "topk_select: null pointer");
-  const TopkPlan pl = plan_topk(ld, nq, k);
-  if (static_cast<int64_t>(nq) * pl.P > kTopkMaxRows)
-    return fail(CSA_ERR_INVALID_ARG, "topk_select: nq * %d slices exceeds %d workgroups", pl.P, kTopkMaxRows);
   if (pl.ws_bytes > 0) {
     if (!workspace || ws_bytes < pl.ws_bytes)
       return fail(CSA_ERR_WORKSPACE, "topk_select: rows of %lld scores need a %zu-byte workspace, got %zu%s",
@@ -318,6 +328,29 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
   }
   TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};
   return launched(launch_topk(a, workspace, stream), "topk_select");
+}
+
+size_t csa_topk_noalloc_max_bytes(void) { return kTopkScratchBytes; }
+
+csa_status topk_select_noalloc(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
+                               int32_t* idx, float* top_scores, hipStream_t stream) {
+  TopkPlan pl{};
+  const csa_status st = topk_check("topk_select_noalloc", scores, ld, nq, k, idx, &pl);
+  if (st != CSA_OK) return st;
+  if (nq == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (pl.ws_bytes > kTopkScratchBytes)
+    return fail(CSA_ERR_WORKSPACE,
+                "topk_select_noalloc: %d rows of %lld scores at k=%d need %zu bytes of candidates; the static "
+                "scratch holds %zu (use topk_select with a workspace)",
+                nq, static_cast<long long>(ld), k, pl.ws_bytes, kTopkScratchBytes);
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    const hipError_t e = topk_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(CSA_ERR_HIP, "topk_select_noalloc: scratch address lookup failed: %s", hipGetErrorString(e));
+  }
+  TopkArgs a{scores, ld, nq, n_valid, k, idx, top_scores};
+  return launched(launch_topk(a, ws, stream), "topk_select_noalloc");
 }
 
 static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream) {

@@ -64,6 +64,10 @@ constexpr int kTopkMaxRows = 1 << 22;
 TopkPlan plan_topk(int64_t ld, int nq, int k);
 // ws: at least plan_topk(...).ws_bytes of device memory (unused when P = 0).
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream);
+// Size of the library's static top-k candidate array (one per device) and its
+// device address on the current device, looked up on the first call per device.
+constexpr size_t kTopkScratchBytes = size_t{16} << 20;
+hipError_t topk_scratch(void** ptr);
 
 // Attention over [selected or all compressed entries] ++ [window rows].
 // The window of query b is `win_count` consecutive rows starting at row

@@ -30,7 +30,15 @@
 // reduction costs one barrier.  The result is the exact set, ascending,
 // whatever the batch or launch.  Loads and stores go through buffer
 // descriptors, so slots past a row's end need neither branches nor clamps.
+#include <atomic>
+
 #include "kernels.hpp"
+
+// Candidate workspace of topk_select_noalloc: one static array per GPU the
+// library runs on, held until the process ends.  Host code must not use this
+// name as a device address; it takes the address hipGetSymbolAddress reports
+// for the current device (topk_scratch below).
+static __device__ __align__(256) uint8_t scratch[csa::kTopkScratchBytes];
 
 namespace csa {
 
@@ -541,6 +549,25 @@ TopkPlan plan_topk(int64_t ld, int nq, int k) {
   pl.Cs = static_cast<uint32_t>(((ld + pl.P - 1) / pl.P + 63) / 64 * 64);
   pl.ws_bytes = static_cast<size_t>(nq) * pl.P * k * (sizeof(int32_t) + sizeof(float));
   return pl;
+}
+
+hipError_t topk_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the device is current here; two threads racing on the first call
+    // store the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {

@@ -319,6 +319,30 @@ csa_status topk_select(const float* scores, int64_t ld, int nq, const int64_t* n
 size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k);
 
 /*
+ * topk_select_noalloc -- topk_select for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same selection, same arguments minus the workspace,
+ * same results bit for bit.
+ *
+ * The candidate rows of the two-pass path live in a static device array of
+ * the library, csa_topk_noalloc_max_bytes() bytes (16 MiB) per GPU, held from
+ * the first call on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).  Its contents on
+ * entry do not matter and nothing needs clearing.  Every call on one GPU
+ * shares the array: two calls that may overlap on one GPU (other streams,
+ * other threads) race and give undefined results; serialise them or use
+ * topk_select with disjoint workspaces.
+ * Errors: those of topk_select, and WORKSPACE when
+ * csa_topk_workspace_bytes(nq, ld, k) exceeds csa_topk_noalloc_max_bytes()
+ * (nothing is enqueued); HIP when the array's address cannot be obtained.
+ */
+csa_status topk_select_noalloc(const float* scores, int64_t ld, int nq, const int64_t* n_valid, int k,
+                               int32_t* idx, float* top_scores, hipStream_t stream);
+
+/* Size of topk_select_noalloc's static candidate array in bytes. */
+size_t csa_topk_noalloc_max_bytes(void);
+
+/*
  * hybrid_attn_decode -- sink multi-query attention of one decode token per
  * sequence over its compressed entries (top-k selected for CSA, all for HCA)
  * followed by its sliding window.

@@ -99,6 +99,22 @@ def test_topk_workspace_contract(lib):
     assert lib.csa_status_string(WORKSPACE) == b"CSA_ERR_WORKSPACE"
 
 
+def test_topk_noalloc_limits(lib):
+    """The no-allocation top-k holds 16 MiB of candidates per GPU; larger
+    selections and bad arguments are refused on the host, before any device
+    call."""
+    assert lib.csa_topk_noalloc_max_bytes() == 16 << 20
+    p = _fake()
+    nq, ld, k = 256, 1 << 20, 4096
+    assert lib.csa_topk_workspace_bytes(nq, ld, k) == nq * 4 * k * 8 > 16 << 20
+    assert lib.topk_select_noalloc(p, ctypes.c_int64(ld), nq, None, k, p, None, None) == WORKSPACE
+    assert "static scratch" in _last_error(lib)
+    assert lib.topk_select_noalloc(p, ctypes.c_int64(ld), 4, None, 0, p, None, None) == INVALID
+    assert lib.topk_select_noalloc(None, ctypes.c_int64(ld), 4, None, 512, p, None, None) == INVALID
+    assert lib.topk_select_noalloc(p, ctypes.c_int64(ld), -1, None, 512, p, None, None) == INVALID
+    assert lib.topk_select_noalloc(p, ctypes.c_int64(ld), 0, None, 512, p, None, None) == 0
+
+
 def test_compress_argument_errors(lib):
     p = _fake()
     base = dict(x=p, x_fmt=csa.F32, gate=p, gate_cols=1, n_tok=8, D=512, m=4, nseg=1, off=p, pos0=p,
