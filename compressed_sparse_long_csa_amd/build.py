@@ -18,6 +18,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS buffers are written and read through different types (packed
+    # words, vectors, byte pointers): no type-based alias assumptions
+    "-fno-strict-aliasing",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
@@ -26,7 +29,9 @@ FLAGS = [
 # accumulators are rescaled by VALU, and AGPR-held results would be copied
 # through VGPRs at every loop iteration)
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         # the ILP scheduler batches each step's operand reads ahead of its
+         # MFMAs (one wave per SIMD has no other wave to hide LDS latency)
+         "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src):
