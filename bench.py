@@ -23,10 +23,15 @@ sequences of 65,536 tokens (16,384 compressed entries each, top-k 512, FP8
 indexer 64 x 128, 64 query heads, head dim 512).
 
 Prints one JSON line.  `roofline` is measured for the dominant launch
-(csa_compress_score, whose indexer part moves most of the step's bytes) with
-events around its launches on its stream; `kernels` gives every kernel's duration, algorithmic
-bytes and FLOPs against the HBM and BF16 MFMA peaks; `cpu_baseline` times the
-float64 oracle on a bounded sample on the host.  `context_scan` repeats the
+(csa_compress_score, whose indexer part moves most of the step's bytes): the
+indexer's input bytes (every visible key, the index query and head weights)
+over the launch's mean period when launched back to back between two events
+on its stream (duration plus dispatch gap, so never shorter than the traced
+duration); `kernels` gives every kernel's period the same way, its bytes and
+FLOPs against the HBM and BF16 MFMA peaks; `hbm_frac_step` is the step's byte
+model over the step time; `fp32_b1_ctx2048` times the all-float32 step of one
+2,048-token sequence; `cpu_baseline` times the float64 oracle on a bounded
+sample on the host, with every BLAS thread and with one.  `context_scan` repeats the
 step at 256K and 1M tokens per sequence; `hca_decode` the HCA decode step
 (32 x 262,144 tokens, every compressed entry attended); `ragged` a CSA layer
 (MXFP4 indexer, top-1,024) and an HCA layer over 64 sequences of 1K to 1M
@@ -55,6 +60,7 @@ from compressed_sparse_long_csa_amd import synth  # noqa: E402
 METRIC = "CSA/HCA decode query-tokens/s and achieved HBM GB/s at 64K-1M context"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 EPS, BASE = 1e-6, 10000.0
 
 
@@ -210,6 +216,10 @@ def algorithmic_bytes(W):
         + B * k * 4 + B * H * D * 2 * 2 + H * 4,
     }
     per_kernel["csa_compress_score"] = per_kernel["csa_compress_batch"] + per_kernel["indexer_score"]
+    # the indexer's inputs alone (every visible key, the index query and head
+    # weights of each query): the step byte model's share of the launch, with
+    # the score writes (scratch) and the compress jobs left out
+    per_kernel["indexer_inputs"] = int((N * d_I).sum()) + B * c["H_I"] * (d_I + 4)
     step_bytes = (int((N * d_I).sum()) + B * c["H_I"] * (d_I + 4) + int((sel * split).sum())
                   + int(inp.win_len.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4)
     return step_bytes, per_kernel
@@ -284,16 +294,40 @@ def _event_pairs(fs, steps):
     return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def time_kernels(kernels_r, steps):
+def _batch_period(fs, steps):
+    """Mean time per launch of `steps` launches queued back to back (f taken in
+    turn from fs) between two events, behind a spin kernel: each launch's
+    duration plus the dispatch gap to the next."""
+    torch.cuda._sleep(int(2e7))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fs[i % len(fs)]()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / steps
+
+
+def kernel_periods(kernels_r, steps):
+    """Every kernel's mean back-to-back launch period (us), launches rotating
+    over the replicas."""
+    names = [n for n, _ in kernels_r[0]]
+    return {n: _batch_period([kr[j][1] for kr in kernels_r], steps) for j, n in enumerate(names)}
+
+
+def time_kernels(kernels_r, steps, batch=None):
     """Average device duration (us) of every kernel, launches rotating over the
     replicas: events around each launch on the stream the kernel runs on
     (torch's current stream), less the time between two events with nothing in
-    between."""
+    between.  `batch` (a dict) receives each kernel's back-to-back launch
+    period as well."""
     empty = _event_pairs([lambda: None], steps)
     names = [n for n, _ in kernels_r[0]]
     out = {}
     for j, n in enumerate(names):
         out[n] = _event_pairs([kr[j][1] for kr in kernels_r], steps) - empty
+        if batch is not None:
+            batch[n] = _batch_period([kr[j][1] for kr in kernels_r], steps)
     return out, empty
 
 
@@ -320,7 +354,7 @@ def copy_gbps(mb=512, reps=20):
     fs = [lambda x=x: torch.mul(x, 1.0, out=y) for x in xs]
     fs[0]()
     torch.cuda.synchronize()
-    us = _event_pairs(fs, reps) - _event_pairs([lambda: None], reps)
+    us = _batch_period(fs, reps)
     return 2 * n * 4 / (us * 1e-6) / 1e9
 
 
@@ -347,16 +381,22 @@ def spot_check(W):
     return float((np.abs(got - ref) / rms).max())
 
 
-def cpu_baseline(W, budget_s=12.0):
-    """The float64 oracle (indexer -> top-k -> sink MQA) on the same inputs,
-    one decode query at a time, until the time budget is used."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sample(W, budget_s):
+    """The float64 oracle (indexer -> top-k -> sink MQA) on the step's inputs,
+    one decode query at a time, until the time budget is used: (queries, s)."""
     from oracle import formats as OF
     from oracle import method as OM
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     inp = W["inp"]
     c = W["c"]
     kv = inp.kv
@@ -378,10 +418,29 @@ def cpu_baseline(W, budget_s=12.0):
         OM.decode_one(q, int(inp.q_pos[b]), ents, win, inp.sinks.astype(np.float64), inp.scale,
                       W["m"], idx=sel, R=W["R"])
         done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode queries (indexer over 16384 FP8 keys, top-512, sink MQA "
-                      f"over 512+128 entries) of the same batch in {dt:.1f} s"}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(W, budget_s=12.0):
+    """The oracle timed on the host: with every BLAS thread the process has
+    (the reported value), and limited to one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        threads = 1
+    done, dt = _oracle_sample(W, budget_s)
+    res = {"value": done / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} decode queries (indexer over 16384 FP8 keys, top-512, sink MQA over "
+                     f"512+128 entries) of the same batch in {dt:.1f} s",
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, t1 = _oracle_sample(W, budget_s / 2)
+        res["one_thread"] = {"value": d1 / t1, "unit": "query-tokens/s", "cores": 1,
+                             "sample": f"{d1} decode queries in {t1:.1f} s"}
+    return res
 
 
 def traffic_record(kernel):
@@ -417,7 +476,7 @@ def context_scan(contexts, steps, warmup):
             st()
         torch.cuda.synchronize()
         ms = time_graph([m[0] for m in made], steps, warmup)
-        per_us, _ = time_kernels([m[1] for m in made], max(20, min(60, steps)))
+        per_us = kernel_periods([m[1] for m in made], max(20, min(60, steps)))
         idx_gbps = kbytes["csa_compress_score"] / (per_us["csa_compress_score"] * 1e-6) / 1e9
         rows.append({"context": L, "ms_per_step": ms, "query_tokens_per_s": W["B"] / (ms * 1e-3),
                      "step_hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
@@ -522,7 +581,7 @@ def paged_leg(reps, steps, warmup):
         st()
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
-    us, _ = time_kernels([m_[1] for m_ in made], max(20, min(100, steps)))
+    us = kernel_periods([m_[1] for m_ in made], max(20, min(100, steps)))
     out = {"block_rows": PAGED_BLOCK_ROWS, "window": "ring", "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
            "kernels_us": {n: round(v, 2) for n, v in us.items()}}
     del pr, made
@@ -581,7 +640,7 @@ def hca_leg(steps, warmup):
         st()
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
-    per_us, _ = time_kernels([m_[1] for m_ in made], max(20, min(60, steps)))
+    per_us = kernel_periods([m_[1] for m_ in made], max(20, min(60, steps)))
     # the attention over a paged copy of the first state (one entry per
     # block: the pages' one HCA entry per 128-token block, blocks shuffled)
     # against the same contiguous state, both on that one copy
@@ -599,7 +658,7 @@ def hca_leg(steps, warmup):
                 d["q"], csa.BF16, B, H, D, q_pos, None, EPS, R, BASE, pool, csa.SPLIT, n_rows, table,
                 table.shape[1], 1, m, None, 0, states[0][1], csa.BF16, n_win, win_len, d["sinks"], d["scale"], out,
                 csa.BF16, csa.VARIANT_AUTO, check=False))]]
-    one_us, _ = time_kernels(one, max(20, min(60, steps)))
+    one_us = kernel_periods(one, max(20, min(60, steps)))
     split = (D - R) + 2 * R
     attended = n_ent.astype(np.int64) + win_len_h.astype(np.int64)
     a_bytes = int(n_ent.sum()) * split + int(win_len_h.sum()) * 2 * D + B * H * D * 2 * 2 + H * 4
@@ -685,7 +744,7 @@ def ragged_leg(steps, warmup):
     step()
     torch.cuda.synchronize()
     ms = time_graph([step], steps, warmup)
-    per_us, _ = time_kernels([kern], max(20, min(60, steps)))
+    per_us = kernel_periods([kern], max(20, min(60, steps)))
     n_ent = dc["n_ent"].astype(np.int64)
     idx_bytes = int(n_ent.sum()) * (68 + 4) + B * H_I * (68 + 4)
     res = {"workload": RAGGED, "lengths_min_median_max": [int(lengths.min()), int(np.median(lengths)),
@@ -700,6 +759,46 @@ def ragged_leg(steps, warmup):
 
 
 PREFILL = "csa_prefill_ctx131072_chunk2048"
+
+
+def fp32_leg(steps, warmup):
+    """The all-float32 CSA decode step of one 2,048-token sequence (D = 128,
+    8 heads, indexer 4 x 64, top-64, window 128): indexer, top-k and attention,
+    captured in a HIP graph.  A latency workload: its time, no roofline."""
+    name = "csa_decode_fp32_b1_ctx2048"
+    c = synth.WORKLOADS[name]
+    inp = synth.workload_decode_inputs(name, seed=c["seed"])
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    q, q_pos, kv, kv_off = dev(inp.q), dev(inp.q_pos), dev(inp.kv), dev(inp.kv_off)
+    win, win_len, sinks = dev(inp.win), dev(inp.win_len), dev(inp.sinks)
+    keys, q_idx, w = dev(inp.keys), dev(inp.q_idx), dev(inp.w)
+    B, H, D, R, k = inp.B, inp.H, inp.D, inp.R, inp.k
+    ld = int(inp.n_ent.max())
+    n_valid = dev(np.asarray(inp.n_ent, np.int64))
+    scores = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+
+    def k_indexer():
+        csa.indexer_score(q_idx, w, B, inp.H_I, inp.d_I, keys, csa.F32, kv_off, q_pos, inp.m, scores, ld,
+                          check=False)
+
+    def k_topk():
+        csa.topk_select(scores, ld, B, n_valid, k, idx, None, check=False)
+
+    def k_attn():
+        csa.hybrid_attn_decode(q, csa.F32, B, H, D, q_pos, None, EPS, R, BASE, kv, csa.F32, kv_off, inp.m, idx, k,
+                               win, csa.F32, inp.n_win, win_len, sinks, inp.scale, out, csa.F32,
+                               csa.VARIANT_AUTO, check=False)
+    kernels = [("indexer_score", k_indexer), ("topk_select", k_topk), ("hybrid_attn_decode", k_attn)]
+
+    def step():
+        for _, f in kernels:
+            f()
+    ms = time_graph([step], steps, warmup)
+    us = kernel_periods([kernels], max(20, min(100, steps)))
+    return {"workload": name, "ms_per_step": ms, "query_tokens_per_s": B / (ms * 1e-3),
+            "kernels_us": {n: round(v, 2) for n, v in us.items()}, "graph": True}
 
 
 def prefill_leg(reps=10):
@@ -760,8 +859,7 @@ def prefill_leg(reps=10):
     for _, f in kernels:
         f()
     torch.cuda.synchronize()
-    empty = _event_pairs([lambda: None], reps)
-    us = {n: _event_pairs([f], reps) - empty for n, f in kernels}
+    us = {n: _batch_period([f], reps) for n, f in kernels}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -778,7 +876,9 @@ def prefill_leg(reps=10):
     res = {"workload": PREFILL, "ms_per_chunk": ms, "tokens_per_s": chunk / (ms * 1e-3),
            "kernels_us": {n: round(v, 1) for n, v in us.items()},
            "indexer_tflops": tflops(f_idx, us["indexer_score"]),
-           "indexer_mfma_frac": tflops(f_idx, us["indexer_score"]) / BF16_PEAK_TFLOPS,
+           # an FP8 contraction (run on BF16 MFMA over exactly widened codes)
+           "indexer_frac_of_fp8_peak": tflops(f_idx, us["indexer_score"]) / FP8_PEAK_TFLOPS,
+           "indexer_frac_of_bf16_peak": tflops(f_idx, us["indexer_score"]) / BF16_PEAK_TFLOPS,
            "attn_tflops": tflops(f_attn, us["hybrid_attn_prefill"]),
            "attn_mfma_frac": tflops(f_attn, us["hybrid_attn_prefill"]) / BF16_PEAK_TFLOPS,
            "topk_gbps": topk_bytes / (us["topk_select"] * 1e-6) / 1e9}
@@ -833,11 +933,13 @@ def main():
     made = [make_step(Wr, check=False) for Wr in reps]
     ms_warm = time_graph([made[0][0]], args.steps, args.warmup)
     ms = time_graph([m[0] for m in made], args.steps, args.warmup)
-    per_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)))
+    batch_us = {}
+    event_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)), batch_us)
+    per_us = batch_us
     # the same step as four launches (compress, then the indexer), for comparison
     made4 = [make_step(Wr, check=False, fused=False) for Wr in reps]
     ms4 = time_graph([m[0] for m in made4], args.steps, args.warmup)
-    per_us4, _ = time_kernels([m[1] for m in made4], max(20, min(100, args.steps)))
+    per_us4 = kernel_periods([m[1] for m in made4], max(20, min(100, args.steps)))
     made[0][0]()                             # replica 0 last, for the spot check
     torch.cuda.synchronize()
     step_bytes, kbytes = algorithmic_bytes(W)
@@ -857,7 +959,9 @@ def main():
                                 "mfma_frac": flops[n] / t / 1e12 / BF16_PEAK_TFLOPS})
         return kern
     kern = table(per_us)
-    ach = kern[dom]["gbps"]
+    for n in kern:
+        kern[n]["us_events_less_floor"] = event_us[n]
+    ach = kbytes["indexer_inputs"] / (per_us[dom] * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": B / (ms * 1e-3),
@@ -879,7 +983,12 @@ def main():
         "step_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_record(dom),
-                     "kernel": dom, "bytes_per_launch": kbytes[dom], "us_per_launch": per_us[dom]},
+                     "kernel": dom, "bytes_per_launch": kbytes["indexer_inputs"],
+                     "bytes_per_launch_with_jobs_and_scores": kbytes[dom], "us_per_launch": per_us[dom],
+                     "us_per_launch_events_less_floor": event_us[dom],
+                     "timing": "mean period of back-to-back launches between two events (duration "
+                               "plus dispatch gap)"},
+        "hbm_frac_step": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernels": kern,
         "four_launches": {"ms_per_step": ms4, "query_tokens_per_s": B / (ms4 * 1e-3),
                           "kernels": table(per_us4)},
@@ -887,6 +996,7 @@ def main():
         "copy_probe_gbps": copy_gbps(),
         "check_max_err_over_rms": err,
     }
+    line["fp32_b1_ctx2048"] = fp32_leg(args.steps, args.warmup)
     if not args.no_paged:
         line["paged"] = paged_leg(reps, args.steps, args.warmup)
     if not args.no_context_scan:

@@ -19,6 +19,16 @@
       record keeps the sha256 of the kernel's source files (concatenated in
       the order given): a reader can tell whether the counters were taken on
       the current kernel.
+
+  python -m compressed_sparse_long_csa_amd.profiling counters --csv CSV \\
+      --trace-db RESULTS_DB [--kernel SUBSTR ...]
+      MFMA use per kernel from one `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+      SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8
+      SQ_INSTS_VALU_MFMA_MOPS_F6F4 ...` run: busy SIMD-cycles and MOPS per
+      dispatch (a MOP is 512 FLOPs), against the kernel's average duration in
+      a kernel-trace run of the same workload.  busy = busy cycles / (1024
+      SIMDs x duration x 2.4 GHz); TFLOP/s per operand type, and the fraction
+      of that type's dense peak (BF16 2.5, FP8 5.0, FP6/FP4 10.1 PFLOP/s).
 """
 import argparse
 import collections
@@ -70,6 +80,37 @@ def counter_per_dispatch(path, substr, counter):
     return statistics.mean(vals.values()), len(vals)
 
 
+SIMDS, CLOCK_GHZ = 1024, 2.4
+MOPS_PEAK_TFLOPS = {"SQ_INSTS_VALU_MFMA_MOPS_BF16": ("bf16", 2500.0), "SQ_INSTS_VALU_MFMA_MOPS_F8": ("fp8", 5000.0),
+                    "SQ_INSTS_VALU_MFMA_MOPS_F6F4": ("fp6/fp4", 10100.0)}
+
+
+def counters_table(csv_path, db, substrs=None):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    dur = {r["kernel"]: r["avg_us"] for r in kernel_stats(db)}
+    out = []
+    for name, cs in per.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in cs or (substrs and not any(x in name for x in substrs)):
+            continue
+        busy = statistics.mean(cs["SQ_VALU_MFMA_BUSY_CYCLES"])
+        if busy == 0 or name not in dur:
+            continue
+        us = dur[name]
+        row = dict(kernel=name, dispatches=len(cs["SQ_VALU_MFMA_BUSY_CYCLES"]), busy_cycles=busy, avg_us=us,
+                   busy_frac=busy / (SIMDS * us * 1e-6 * CLOCK_GHZ * 1e9), types={})
+        for c, (ty, peak) in MOPS_PEAK_TFLOPS.items():
+            if c in cs:
+                fl = statistics.mean(cs[c]) * 512.0
+                if fl > 0:
+                    tf = fl / (us * 1e-6) / 1e12
+                    row["types"][ty] = dict(gflop=fl / 1e9, tflops=tf, frac_of_peak=tf / peak)
+        out.append(row)
+    return sorted(out, key=lambda r: -r["avg_us"])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -82,7 +123,18 @@ def main(argv=None):
     t.add_argument("--source", action="append", required=True)
     t.add_argument("--copy-kernel", default="elementwise")
     t.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy launch")
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--trace-db", required=True)
+    c.add_argument("--kernel", action="append")
     args = ap.parse_args(argv)
+    if args.cmd == "counters":
+        print(f"{'kernel':70s} {'disp':>5s} {'avg_us':>8s} {'mfma_busy':>9s}  per type: GFLOP/dispatch, TFLOP/s, of peak")
+        for r in counters_table(args.csv, args.trace_db, args.kernel):
+            ty = "; ".join(f"{t} {v['gflop']:.3f} GFLOP {v['tflops']:.1f} TF/s {100 * v['frac_of_peak']:.1f}%"
+                           for t, v in r["types"].items())
+            print(f"{r['kernel'][:70]:70s} {r['dispatches']:5d} {r['avg_us']:8.2f} {100 * r['busy_frac']:8.1f}%  {ty}")
+        return
     if args.cmd == "stats":
         parts = ([("launches next to a launch of the same kernel", True),
                   ("all other launches", False)] if args.split_runs else [(None, None)])

@@ -301,6 +301,55 @@ def test_topk_exact(ld, k, tie_levels, n_valid):
         assert np.all(np.isneginf(gs[i, c:]))
 
 
+def _sampled_positions(ld):
+    """Row positions the selector samples for its threshold estimate: thread t
+    of 1024 samples position 1024 (t % V) + t, V the registers per thread."""
+    V = next(v for v in (4, 8, 16, 24, 33) if ld <= 1024 * v)
+    t = np.arange(1024)
+    p = 1024 * (t % V) + t
+    return p[p < ld]
+
+
+@pytest.mark.parametrize("case", ["top_at_samples", "top_off_samples", "ascending", "descending", "relu_zeros",
+                                  "boundaries"])
+def test_topk_value_layouts(case):
+    """Layouts that defeat the sampled threshold estimate (too few or too many
+    candidates) take the general selection; every layout gives the exact set."""
+    rng = np.random.default_rng(11)
+    rows = []
+    if case == "boundaries":
+        for ld in (513, 4096, 4097, 8192, 8193, 16384, 16385, 24576, 24577, 33792):
+            rows.append((rng.standard_normal(ld).astype(np.float32), 512))
+    else:
+        for ld in (3000, 16384, 24000, 33792):
+            x = rng.standard_normal(ld).astype(np.float32)
+            ps = _sampled_positions(ld)
+            if case == "top_at_samples":
+                x[ps] += 20.0
+            elif case == "top_off_samples":
+                off = np.setdiff1d(np.arange(ld), ps)
+                x[off[rng.choice(len(off), min(3000, len(off) // 2), replace=False)]] += 20.0
+            elif case == "ascending":
+                x = np.sort(x)
+            elif case == "descending":
+                x = np.sort(x)[::-1].copy()
+            elif case == "relu_zeros":
+                x = np.maximum(x, 0.0).astype(np.float32)
+            rows.append((x, 512))
+            rows.append((x, 1024))
+    for x, k in rows:
+        ld = len(x)
+        s = x[None, :]
+        idx = torch.empty((1, k), dtype=torch.int32, device=DEV)
+        tops = torch.empty((1, k), dtype=torch.float32, device=DEV)
+        csa.topk_select(dev(s), ld, 1, None, k, idx, tops)
+        got = idx.cpu().numpy()[0]
+        want = OM.top_k(x.astype(np.float64), k)
+        assert np.array_equal(got[: len(want)], want), f"{case} ld={ld} k={k}"
+        assert np.all(got[len(want):] == -1)
+        assert np.array_equal(tops.cpu().numpy()[0, : len(want)], x[want])
+
+
 def test_topk_long_rows_in_a_graph():
     """The long-row path (slices, then a candidate merge through the caller's
     workspace) captured in a HIP graph: every replay, with eager work in
