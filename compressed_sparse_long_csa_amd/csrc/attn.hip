@@ -346,8 +346,9 @@ __device__ __forceinline__ int list_entry(const Work& w, int pos, bool* ok) {
 // (bit r = row r holds a real entry).  Rows without an entry load entry 0, or
 // read as zeros past the end of the query's rows, and stay masked.
 // The rows of a wave's first kTabSteps compressed steps (the entry, or the
-// pool row when paged; -1 where the slot is empty or invalid) sit in the
-// wave's LDS table, written by the prologue; later steps map theirs here.
+// pool row when paged) sit in the wave's LDS table, written by the prologue;
+// a slot without an entry holds ~row of entry 0 (finite data, masked: a free
+// pool row may hold anything).  Later steps map theirs here.
 template <bool PG>
 __device__ __forceinline__ uint32_t issue_load(const Work& w, int L, int wv, const int* tab, uint32_t lds) {
   const int lane = threadIdx.x & 63;
@@ -363,7 +364,7 @@ __device__ __forceinline__ uint32_t issue_load(const Work& w, int L, int wv, con
       row = pos0 + r;                                   // (a row past N reads as zeros)
     } else if (L < kTabSteps) {
       const int e = tab[L * kStepE + r];
-      row = e < 0 ? 0 : e;
+      row = e < 0 ? ~e : e;
       vmask = static_cast<uint32_t>(__ballot(lane < kStepE && e >= 0));
     } else {
       bool ok = false;
@@ -771,26 +772,27 @@ attn_mfma_kernel(AttnArgs a, int n_units, int n_pad) {
   // rows go out)
   {
     int e[kTabSteps / 4];
+    bool valid[kTabSteps / 4];
 #pragma unroll
     for (int t = 0; t < kTabSteps / 4; ++t) {
       const int step = 4 * t + (lane >> 4);
       const int pos = step * (kWaves * kStepE) + wv * kStepE + (lane & 15);
       const bool ok = (w.idx != nullptr || paged) && step < w.ns && pos < w.n_list && e_ld[t] >= 0 && e_ld[t] < w.N;
-      e[t] = ok ? e_ld[t] : -1;
+      e[t] = ok ? e_ld[t] : 0;                          // no entry: entry 0's row, masked
+      valid[t] = ok;
     }
     if (paged) {
       const int sh = w.sh;
       int32_t blk[kTabSteps / 4];
 #pragma unroll
       for (int t = 0; t < kTabSteps / 4; ++t)
-        blk[t] = __builtin_amdgcn_raw_buffer_load_b32(w.tbl_rs, ((e[t] < 0 ? 0 : e[t]) >> sh) * 4, 0, 0);
+        blk[t] = __builtin_amdgcn_raw_buffer_load_b32(w.tbl_rs, (e[t] >> sh) * 4, 0, 0);
 #pragma unroll
       for (int t = 0; t < kTabSteps / 4; ++t)
-        if (e[t] >= 0)
-          e[t] = static_cast<int>((static_cast<uint32_t>(blk[t]) << sh) | (static_cast<uint32_t>(e[t]) & ((1u << sh) - 1u)));
+        e[t] = static_cast<int>((static_cast<uint32_t>(blk[t]) << sh) | (static_cast<uint32_t>(e[t]) & ((1u << sh) - 1u)));
     }
 #pragma unroll
-    for (int t = 0; t < kTabSteps / 4; ++t) ws.tab[64 * t + lane] = e[t];
+    for (int t = 0; t < kTabSteps / 4; ++t) ws.tab[64 * t + lane] = valid[t] ? e[t] : ~e[t];
   }
   // the first two loads go out before the query is prepared (slots 2 and 3
   // hold the query staging until the operands are taken)
