@@ -392,6 +392,14 @@ def _cpu_model():
     return "unknown"
 
 
+def _physical_cores():
+    try:
+        import psutil
+        return psutil.cpu_count(logical=False)
+    except Exception:  # pragma: no cover
+        return None
+
+
 def _oracle_sample(W, budget_s):
     """The float64 oracle (indexer -> top-k -> sink MQA) on the step's inputs,
     one decode query at a time, until the time budget is used: (queries, s)."""
@@ -434,7 +442,7 @@ def cpu_baseline(W, budget_s=12.0):
     res = {"value": done / dt, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{done} decode queries (indexer over 16384 FP8 keys, top-512, sink MQA over "
                      f"512+128 entries) of the same batch in {dt:.1f} s",
-           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "host_physical_cores": _physical_cores()}
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
             d1, t1 = _oracle_sample(W, budget_s / 2)

@@ -25,7 +25,7 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_by
            "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
            "indexer_score_paged", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
-           "hybrid_attn_decode_paged", "hybrid_attn_prefill")
+           "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged")
 
 _lib = None
 
@@ -80,6 +80,9 @@ def load_library():
     lib.hybrid_attn_prefill.restype = I
     lib.hybrid_attn_prefill.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, P, I, P, I, P, I, P,
                                         P, I, P, F, P, I, I, P]
+    lib.hybrid_attn_prefill_paged.restype = I
+    lib.hybrid_attn_prefill_paged.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, I64, P, I64, I64, I, P, I, P, I,
+                                              P, I, P, P, I, P, F, P, I, I, P]
     _lib = lib
     return lib
 
@@ -215,19 +218,26 @@ def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, sc
                              _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
-def _paged_checks(table, nq, blocks_per_seq, block_rows, pool, pool_rows, rb, q_pos, m, ld, check):
+def _paged_checks(table, nq, blocks_per_seq, block_rows, pool, pool_rows, rb, q_pos, m, ld, check,
+                  table_rows=None, q_block_row=None):
     """Host-side checks of a block table: its shape, and with check=True that
-    every block a query uses is inside the pool."""
-    _need(table, "block_table", torch.int32, min_numel=nq * blocks_per_seq)
+    every block a query uses is inside the pool.  Query i reads table row
+    q_block_row[i] (None: row i) of table_rows rows (None: nq)."""
+    table_rows = nq if table_rows is None else table_rows
+    _need(table, "block_table", torch.int32, min_numel=table_rows * blocks_per_seq)
     _need(pool, "pool", min_bytes=pool_rows * rb)
+    _need(q_block_row, "q_block_row", torch.int32, min_numel=nq, allow_none=True)
     if check and nq > 0:
         N = torch.clamp((_host(q_pos)[:nq] + 1) // m, max=ld)
         if int(N.max()) > blocks_per_seq * block_rows:
             raise ValueError("a query sees more rows than its block-table row holds")
-        t = _host(table)[: nq * blocks_per_seq].view(nq, blocks_per_seq)
+        t = _host(table)[: table_rows * blocks_per_seq].view(table_rows, blocks_per_seq)
+        rows = torch.arange(nq) if q_block_row is None else _host(q_block_row)[:nq].long()
+        if int(rows.min()) < 0 or int(rows.max()) >= table_rows:
+            raise ValueError("a q_block_row entry is outside the block table")
         nb = (N + block_rows - 1) // block_rows
         for i in range(nq):
-            used = t[i, : int(nb[i])]
+            used = t[int(rows[i]), : int(nb[i])]
             if used.numel() and (int(used.min()) < 0 or (int(used.max()) + 1) * block_rows > pool_rows):
                 raise ValueError(f"query {i} uses a block outside the pool")
 
@@ -380,3 +390,33 @@ def hybrid_attn_prefill(q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope
                                    _ptr(idx), k, _ptr(tok), tok_fmt, _ptr(tok_off), _ptr(tok_pos0),
                                    n_win, _ptr(sinks), scale, _ptr(out), out_fmt, variant,
                                    _stream(stream)))
+
+
+def hybrid_attn_prefill_paged(q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt,
+                              pool_rows, block_table, table_rows, blocks_per_seq, block_rows, q_block_row, m, idx,
+                              k, tok, tok_fmt, tok_off, tok_pos0, n_win, sinks, scale, out, out_fmt,
+                              variant=VARIANT_AUTO, stream=None, check=True):
+    lib = load_library()
+    rb = row_bytes(kv_fmt, D, rope_dim)
+    _need(q, "q", min_bytes=nq * H * row_bytes(q_fmt, D, rope_dim))
+    _need(q_pos, "q_pos", torch.int64, min_numel=nq)
+    _need(q_norm_w, "q_norm_w", torch.float32, min_numel=D, allow_none=True)
+    _need(idx, "idx", torch.int32, min_numel=nq * k, allow_none=True)
+    _need(sinks, "sinks", torch.float32, min_numel=H)
+    _need(out, "out", min_bytes=nq * H * row_bytes(out_fmt, D, rope_dim))
+    _paged_checks(block_table, nq, blocks_per_seq, block_rows, kv_pool, pool_rows, rb, q_pos, m, 1 << 62, check,
+                  table_rows=table_rows, q_block_row=q_block_row)
+    if n_win > 0:
+        _need(tok, "tok")
+        _need(tok_off, "tok_off", torch.int64, min_numel=nq)
+        _need(tok_pos0, "tok_pos0", torch.int64, min_numel=nq)
+        if check and nq > 0:
+            p = _host(q_pos)[:nq]
+            last = _host(tok_off)[:nq] + (p - _host(tok_pos0)[:nq])
+            if int(last.max()) + 1 > (tok.numel() * tok.element_size()) // row_bytes(tok_fmt, D, rope_dim):
+                raise ValueError("a query's window runs past the end of `tok`")
+    _check(lib.hybrid_attn_prefill_paged(_ptr(q), q_fmt, nq, H, D, _ptr(q_pos), _ptr(q_norm_w), eps, rope_dim,
+                                         rope_base, _ptr(kv_pool), kv_fmt, pool_rows, _ptr(block_table),
+                                         table_rows, blocks_per_seq, block_rows, _ptr(q_block_row), m, _ptr(idx),
+                                         k, _ptr(tok), tok_fmt, _ptr(tok_off), _ptr(tok_pos0), n_win,
+                                         _ptr(sinks), scale, _ptr(out), out_fmt, variant, _stream(stream)))

@@ -733,6 +733,7 @@ attn_mfma_kernel(AttnArgs a, int n_units, int n_pad) {
   const int ws_ld = PG && a.win_mode == 1 && a.win_start != nullptr ? a.win_start[b] : 0;
   const int64_t tp0_ld = a.win_mode == 2 ? a.tok_pos0[b] : 0, toff_ld = a.win_mode == 2 ? a.tok_off[b] : 0;
   const int32_t* idx_q = a.idx != nullptr ? a.idx + static_cast<int64_t>(b) * a.k : nullptr;
+  const int32_t trow_ld = PG && a.blk_row != nullptr ? a.blk_row[b] : b;
   int e_ld[kTabSteps / 4];
 #pragma unroll
   for (int t = 0; t < kTabSteps / 4; ++t) {
@@ -764,8 +765,13 @@ attn_mfma_kernel(AttnArgs a, int n_units, int n_pad) {
   w.win_d = make_desc(w.win_count > 0 ? static_cast<const uint8_t*>(a.win) + win_row0 * kRowBf16 : nullptr,
                       static_cast<uint32_t>(w.ring_n > 0 ? w.ring_n : w.win_count) * kRowBf16);
   w.sh = paged ? a.blk_shift : 0;
-  w.tbl_rs = make_rsrc(paged ? a.blk_table + static_cast<int64_t>(b) * a.blk_stride : nullptr,
-                       paged ? static_cast<uint32_t>(a.blk_stride * 4) : 0u);
+  {
+    // the query's block-table row (clamped: an out-of-range row reads row 0 or the last)
+    int64_t tr = __builtin_amdgcn_readfirstlane(trow_ld);
+    tr = tr < 0 ? 0 : (tr >= a.blk_rows ? a.blk_rows - 1 : tr);
+    w.tbl_rs = make_rsrc(paged ? a.blk_table + tr * a.blk_stride : nullptr,
+                         paged ? static_cast<uint32_t>(a.blk_stride * 4) : 0u);
+  }
   // the wave's rows of its first kTabSteps steps (lane l: step 4 t + l / 16,
   // row l % 16) to its LDS table; paged: logical entry -> pool row through
   // the query's block table (one more dependent round trip before the first

@@ -432,7 +432,7 @@ csa_status hybrid_attn_decode_paged(const void* q, csa_fmt q_fmt, int B, int H, 
   AttnArgs a{q, q_fmt, B, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt, nullptr, m,
              idx, k, win, win_fmt, n_win, n_win > 0 ? 1 : 0, win_len, nullptr, nullptr, sinks,
              scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,
-             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows, win_start};
+             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows, win_start, nullptr, B};
   return attn_common(what, a, stream);
 }
 
@@ -450,6 +450,40 @@ csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int 
              idx, k, tok, tok_fmt, n_win, n_win > 0 ? 2 : 0, nullptr, tok_off, tok_pos0, sinks,
              scale, out, out_fmt, static_cast<int>(variant), {}};
   return attn_common("hybrid_attn_prefill", a, stream);
+}
+
+csa_status hybrid_attn_prefill_paged(const void* q, csa_fmt q_fmt, int nq, int H, int D,
+                                     const int64_t* q_pos, const float* q_norm_w, float eps,
+                                     int rope_dim, float rope_base, const void* kv_pool, csa_fmt kv_fmt,
+                                     int64_t pool_rows, const int32_t* block_table, int64_t table_rows,
+                                     int64_t blocks_per_seq, int block_rows, const int32_t* q_block_row,
+                                     int m, const int32_t* idx, int k, const void* tok, csa_fmt tok_fmt,
+                                     const int64_t* tok_off, const int64_t* tok_pos0, int n_win,
+                                     const float* sinks, float scale, void* out, csa_fmt out_fmt,
+                                     csa_variant variant, hipStream_t stream) {
+  const char* what = "hybrid_attn_prefill_paged";
+  if (nq > 0 && n_win > 0 && (!tok_off || !tok_pos0))
+    return fail(CSA_ERR_INVALID_ARG, "%s: null tok_off / tok_pos0", what);
+  if (!(q_fmt == CSA_BF16 && kv_fmt == CSA_SPLIT && tok_fmt == CSA_BF16 && out_fmt == CSA_BF16))
+    return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path is the MFMA path (BF16 q / window / out, SPLIT cache)",
+                what);
+  if (block_rows < 1 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
+    return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [1, 2^20]", what);
+  if (blocks_per_seq < 1 || blocks_per_seq > (int64_t{1} << 26))
+    return fail(CSA_ERR_INVALID_ARG, "%s: blocks_per_seq must be in [1, 2^26]", what);
+  if (table_rows < 1 || table_rows > (int64_t{1} << 31))
+    return fail(CSA_ERR_INVALID_ARG, "%s: table_rows must be in [1, 2^31]", what);
+  if (pool_rows < 1) return fail(CSA_ERR_INVALID_ARG, "%s: pool_rows must be >= 1", what);
+  if (static_cast<uint64_t>(pool_rows) * row_bytes(CSA_SPLIT, D, rope_dim) > 0xffffffffull)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: the entry pool must be smaller than 4 GiB", what);
+  if (nq > 0 && !block_table) return fail(CSA_ERR_INVALID_ARG, "%s: null block_table", what);
+  if (nq > 0 && !q_block_row && table_rows < nq)
+    return fail(CSA_ERR_INVALID_ARG, "%s: without q_block_row, query i reads table row i (table_rows < nq)", what);
+  AttnArgs a{q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim, rope_base, kv_pool, kv_fmt, nullptr, m,
+             idx, k, tok, tok_fmt, n_win, n_win > 0 ? 2 : 0, nullptr, tok_off, tok_pos0, sinks,
+             scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,
+             __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows, nullptr, q_block_row, table_rows};
+  return attn_common(what, a, stream);
 }
 
 }  // extern "C"

@@ -84,13 +84,17 @@ struct AttnArgs {
   const int64_t* tok_off; const int64_t* tok_pos0;      // prefill
   const float* sinks; float scale; void* out; csa_fmt out_fmt; int variant;
   double rope_theta[kMaxRopePairs];
-  // paged cache (blk_table != nullptr, selected-entry decode only; kv_off
-  // unused): entry e of query b is pool row
-  // blk_table[b * blk_stride + (e >> blk_shift)] * 2^blk_shift + (e mod 2^blk_shift)
+  // paged cache (blk_table != nullptr; kv_off unused): entry e of query b is
+  // pool row blk_table[r * blk_stride + (e >> blk_shift)] * 2^blk_shift +
+  // (e mod 2^blk_shift), r = blk_row[b] (or b)
   const int32_t* blk_table; int64_t blk_stride; int blk_shift; int64_t pool_rows;
   // decode window kept as a ring (win_start != nullptr, MFMA path): window
   // row t of query b is row b * n_win + (win_start[b] + t) mod n_win of win
   const int32_t* win_start;
+  // the block-table row of each query (paged prefill: the queries of one
+  // sequence share a row); nullptr: query b uses row b.  Rows are clamped to
+  // [0, blk_rows).
+  const int32_t* blk_row; int64_t blk_rows;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 

@@ -462,6 +462,47 @@ csa_status hybrid_attn_prefill(const void* q, csa_fmt q_fmt, int nq, int H, int 
                                float scale, void* out, csa_fmt out_fmt, csa_variant variant,
                                hipStream_t stream);
 
+/*
+ * hybrid_attn_prefill_paged -- hybrid_attn_prefill over a paged entry cache.
+ *
+ * Source: the passages of hybrid_attn_prefill; 硅星人 article, classic-cache
+ * paragraph (the compressed entries of a request live in fixed blocks of the
+ * shared pool, reached through the request's block table).
+ *
+ * Query i reads block-table row r = q_block_row[i] (q_block_row NULL: r = i);
+ * its entry e (e < floor((q_pos[i]+1)/m)) is row
+ *   block_table[r * blocks_per_seq + (e / block_rows)] * block_rows + e % block_rows
+ * of kv_pool (pool_rows SPLIT rows).  The queries of one sequence in a chunk
+ * share one table row, so a chunk needs one row per sequence, not per query.
+ * The window is read from per-token rows exactly as in hybrid_attn_prefill
+ * (tok, tok_off, tok_pos0).  Everything else -- the top-k rows idx (logical
+ * entry numbers), the sinks, the reduction order -- is that of
+ * hybrid_attn_prefill, and so are the output bits: a query gives the same
+ * bits whether its entries are paged or contiguous.
+ *
+ *   block_table  [table_rows, blocks_per_seq] int32
+ *   q_block_row  [nq] int32 or NULL; a row outside [0, table_rows) is clamped
+ *                into it (memory safety only: the result is then that row's)
+ *
+ * Supported: the MFMA path only (BF16 q / tok / out, SPLIT cache, D = 512,
+ * rope_dim = 64, H a multiple of 16); block_rows a power of two in [1, 2^20];
+ * blocks_per_seq in [1, 2^26]; table_rows in [1, 2^31]; a pool smaller than
+ * 4 GiB.  Preconditions as for hybrid_attn_decode_paged (the table row covers
+ * every visible entry; used blocks inside the pool).
+ * Errors: those of hybrid_attn_prefill; UNSUPPORTED for other formats;
+ * INVALID_ARG for bad block_rows / blocks_per_seq / table_rows / pool_rows, a
+ * NULL block_table, or q_block_row NULL with table_rows < nq.
+ */
+csa_status hybrid_attn_prefill_paged(const void* q, csa_fmt q_fmt, int nq, int H, int D,
+                                     const int64_t* q_pos, const float* q_norm_w, float eps,
+                                     int rope_dim, float rope_base, const void* kv_pool, csa_fmt kv_fmt,
+                                     int64_t pool_rows, const int32_t* block_table, int64_t table_rows,
+                                     int64_t blocks_per_seq, int block_rows, const int32_t* q_block_row,
+                                     int m, const int32_t* idx, int k, const void* tok, csa_fmt tok_fmt,
+                                     const int64_t* tok_off, const int64_t* tok_pos0, int n_win,
+                                     const float* sinks, float scale, void* out, csa_fmt out_fmt,
+                                     csa_variant variant, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -223,7 +223,7 @@ def test_compress_score_argument_errors(lib):
 
 
 def test_paged_entry_points_argument_errors(lib):
-    """indexer_score_paged / hybrid_attn_decode_paged: block geometry, pool
+    """indexer_score_paged / hybrid_attn_{decode,prefill}_paged: block geometry, pool
     size and format checks run on the host before any launch."""
     p, tbl = _fake(), _fake(3)
 
@@ -250,3 +250,20 @@ def test_paged_entry_points_argument_errors(lib):
     assert att(q_fmt=csa.F32, kv_fmt=csa.F32) == UNSUPPORTED
     assert att(table=None) == INVALID
     assert "hybrid_attn_decode_paged" in _last_error(lib)
+
+    def pre(nq=2, q_fmt=csa.BF16, br=32, bps=10, pool_rows=1000, table=tbl, table_rows=4, qrow=p):
+        return lib.hybrid_attn_prefill_paged(p, q_fmt, nq, 64, 512, p, None, ctypes.c_float(1e-6), 64,
+                                             ctypes.c_float(1e4), p, csa.SPLIT, ctypes.c_int64(pool_rows), table,
+                                             ctypes.c_int64(table_rows), ctypes.c_int64(bps), br, qrow, 4, p, 512,
+                                             p, csa.BF16, p, p, 128, p, ctypes.c_float(0.04), p, csa.BF16, 0, None)
+    assert pre(br=48) == INVALID
+    assert pre(bps=0) == INVALID
+    assert pre(table_rows=0) == INVALID
+    assert pre(table_rows=1 << 32) == INVALID
+    assert pre(pool_rows=0) == INVALID
+    assert pre(pool_rows=1 << 23) == UNSUPPORTED
+    assert pre(q_fmt=csa.F32) == UNSUPPORTED
+    assert pre(table=None) == INVALID
+    assert pre(nq=5, table_rows=4, qrow=None) == INVALID   # query 4 would read table row 4
+    assert "hybrid_attn_prefill_paged" in _last_error(lib)
+    assert pre(nq=0) == OK
