@@ -9,6 +9,7 @@ from .binding import (BF16, F32, FP8, MXFP4, SPLIT, VARIANT_AUTO, VARIANT_HIGH_O
                       VARIANT_LOW_OCC, CsaError, csa_compress, csa_compress_batch, csa_compress_score,
                       hybrid_attn_decode, hybrid_attn_decode_paged,
                       hybrid_attn_prefill, hybrid_attn_prefill_paged, indexer_score, indexer_score_paged,
+                      indexer_score_paged_rows,
                       load_library, row_bytes,
                       topk_noalloc_max_bytes, topk_select, topk_select_noalloc,
                       topk_workspace_bytes)

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
            "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
-           "indexer_score_paged", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
+           "indexer_score_paged", "indexer_score_paged_rows", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
            "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged")
 
@@ -61,6 +61,8 @@ def load_library():
                                        I64, P]
     lib.indexer_score_paged.restype = I
     lib.indexer_score_paged.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I, P, I, P, I64, P]
+    lib.indexer_score_paged_rows.restype = I
+    lib.indexer_score_paged_rows.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I64, I, P, P, I, P, I64, P]
     lib.hybrid_attn_decode_paged.restype = I
     lib.hybrid_attn_decode_paged.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, I64, P, I64, I, I, P, I, P, I, I,
                                              P, P, P, F, P, I, I, P]
@@ -254,6 +256,21 @@ def indexer_score_paged(q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, 
     _check(lib.indexer_score_paged(_ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool), fmt, pool_rows,
                                    _ptr(block_table), blocks_per_seq, block_rows, _ptr(q_pos), m, _ptr(scores),
                                    ld, _stream(stream)))
+
+
+def indexer_score_paged_rows(q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table, table_rows,
+                             blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, stream=None, check=True):
+    lib = load_library()
+    rb = row_bytes(fmt, d_idx)
+    _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
+    _need(w, "w", torch.float32, min_numel=nq * n_heads)
+    _need(q_pos, "q_pos", torch.int64, min_numel=nq)
+    _need(scores, "scores", torch.float32, min_numel=nq * ld)
+    _paged_checks(block_table, nq, blocks_per_seq, block_rows, key_pool, pool_rows, rb, q_pos, m, ld, check,
+                  table_rows=table_rows, q_block_row=q_block_row)
+    _check(lib.indexer_score_paged_rows(_ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool), fmt, pool_rows,
+                                        _ptr(block_table), table_rows, blocks_per_seq, block_rows,
+                                        _ptr(q_block_row), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
 def _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check):

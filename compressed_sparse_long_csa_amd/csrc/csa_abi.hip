@@ -225,11 +225,11 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
   return launched(launch_indexer(a, stream), "indexer_score");
 }
 
-csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
-                               const void* key_pool, csa_fmt fmt, int64_t pool_rows,
-                               const int32_t* block_table, int64_t blocks_per_seq, int block_rows,
-                               const int64_t* q_pos, int m, float* scores, int64_t ld, hipStream_t stream) {
-  const char* what = "indexer_score_paged";
+static csa_status indexer_paged(const char* what, const void* q_idx, const float* w, int nq, int n_heads,
+                                int d_idx, const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                                const int32_t* block_table, int64_t table_rows, int64_t blocks_per_seq,
+                                int block_rows, const int32_t* q_block_row, const int64_t* q_pos, int m,
+                                float* scores, int64_t ld, hipStream_t stream) {
   if (fmt == CSA_F32) return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path takes FP8 or MXFP4 keys", what);
   IndexerArgs a{};
   bool empty = false;
@@ -242,16 +242,40 @@ csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_
     return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [16, 2^20]", what);
   if (blocks_per_seq < 1 || blocks_per_seq > (int64_t{1} << 26))
     return fail(CSA_ERR_INVALID_ARG, "%s: blocks_per_seq must be in [1, 2^26]", what);
+  if (table_rows < 1 || table_rows > (int64_t{1} << 31))
+    return fail(CSA_ERR_INVALID_ARG, "%s: table_rows must be in [1, 2^31]", what);
   if (pool_rows < 1) return fail(CSA_ERR_INVALID_ARG, "%s: pool_rows must be >= 1", what);
   if (static_cast<uint64_t>(pool_rows) * row_bytes(fmt, d_idx, 0) > 0xffffffffull)
     return fail(CSA_ERR_UNSUPPORTED, "%s: the key pool must be smaller than 4 GiB", what);
+  if (!q_block_row && table_rows < nq)
+    return fail(CSA_ERR_INVALID_ARG, "%s: without q_block_row, query i reads table row i (table_rows < nq)", what);
   if (empty) { g_err[0] = '\0'; return CSA_OK; }
   a.key_off = nullptr;
   a.blk_table = block_table;
   a.blk_stride = blocks_per_seq;
   a.blk_shift = __builtin_ctz(static_cast<unsigned>(block_rows));
   a.pool_rows = pool_rows;
+  a.blk_row = q_block_row;
+  a.blk_rows = table_rows;
   return launched(launch_indexer(a, stream), what);
+}
+
+csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                               const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                               const int32_t* block_table, int64_t blocks_per_seq, int block_rows,
+                               const int64_t* q_pos, int m, float* scores, int64_t ld, hipStream_t stream) {
+  return indexer_paged("indexer_score_paged", q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table,
+                       nq > 0 ? nq : 1, blocks_per_seq, block_rows, nullptr, q_pos, m, scores, ld, stream);
+}
+
+csa_status indexer_score_paged_rows(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                                    const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                                    const int32_t* block_table, int64_t table_rows, int64_t blocks_per_seq,
+                                    int block_rows, const int32_t* q_block_row, const int64_t* q_pos, int m,
+                                    float* scores, int64_t ld, hipStream_t stream) {
+  return indexer_paged("indexer_score_paged_rows", q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows,
+                       block_table, table_rows, blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld,
+                       stream);
 }
 
 csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,

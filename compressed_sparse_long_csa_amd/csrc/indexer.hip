@@ -123,12 +123,23 @@ struct PagedTab {
   int bpg_shift;                                         // log2(blocks per 64-key group)
 };
 
+// Block-table row of query i: i, or blk_row[i] clamped into the table (an
+// out-of-range row reads row 0 or the last one; the caller checks rows).
+__device__ __forceinline__ int64_t table_row(const IndexerArgs& a, int i) {
+  if (a.blk_row == nullptr) return i;
+  const int64_t r = __builtin_amdgcn_readfirstlane(a.blk_row[i]);
+  return r < 0 ? 0 : (r >= a.blk_rows ? a.blk_rows - 1 : r);
+}
+
+__device__ __forceinline__ buf_rsrc table_rsrc(const IndexerArgs& a, int64_t row) {
+  return make_rsrc(a.blk_table + row * a.blk_stride, static_cast<uint32_t>(a.blk_stride * 4));
+}
+
 __device__ __forceinline__ void paged_tab_load(const IndexerArgs& a, int i, uint32_t first, uint32_t step,
                                                int R, int lane, PagedTab& pt) {
   const int sh = a.blk_shift;
   pt.bpg_shift = sh >= 6 ? 0 : 6 - sh;
-  const buf_rsrc trs = make_rsrc(a.blk_table + static_cast<int64_t>(i) * a.blk_stride,
-                                 static_cast<uint32_t>(a.blk_stride * 4));
+  const buf_rsrc trs = table_rsrc(a, table_row(a, i));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const uint32_t e = static_cast<uint32_t>(s * 64 + lane);
@@ -464,7 +475,12 @@ __device__ __forceinline__ void block_bf16(const bf16x8 (&kk)[4], const bf16x8 (
   pend = nxt;
 }
 
-template <int NHB>
+// kPaged: keys through the block table; the queries of a workgroup share
+// their keys when they share a table row.  Wave wv's 16-key block of step s
+// lies in one table block (block_rows >= 16, blocks start at multiples of
+// 16), so each step needs one table entry per wave: lane s of the wave loads
+// the entry of step s when the unit starts, and step s reads it with readlane.
+template <int NHB, bool kPaged>
 __global__ void __launch_bounds__(share_q<NHB>() * 64) indexer_fp8_shared_kernel(IndexerArgs a, int64_t n_qblk,
                                                                                  int64_t n_kchunk) {
   constexpr int H = NHB * 16;
@@ -496,7 +512,8 @@ __global__ void __launch_bounds__(share_q<NHB>() * 64) indexer_fp8_shared_kernel
 #pragma unroll
     for (int q = 0; q < kShareQ; ++q) {
       const int iq = i0 + (q < nqb ? q : 0);
-      const int64_t ko = uniform64(scalar_load(a.key_off, iq));
+      // paged: the table row stands in for the key offset (same row, same keys)
+      const int64_t ko = kPaged ? table_row(a, iq) : uniform64(scalar_load(a.key_off, iq));
       int64_t n = (uniform64(scalar_load(a.q_pos, iq)) + 1) / a.m;
       n = n > a.ld ? a.ld : n;
       if (q == 0) koff0 = ko;
@@ -524,16 +541,38 @@ __global__ void __launch_bounds__(share_q<NHB>() * 64) indexer_fp8_shared_kernel
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) cp[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     int pend = -1;
+    const uint64_t pool_bytes = static_cast<uint64_t>(a.pool_rows) * 128u;
+    const uint32_t pool_lim = pool_bytes < 0xffffffffull ? static_cast<uint32_t>(pool_bytes) : 0xffffffffu;
     if (same) {
       // wave wv loads block wv of every step: rows k0 + s*kShareStepKeys + wv*16 + j16, bytes [32g, 32g+32)
-      const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + koff0 * 128,
-                                    static_cast<uint32_t>(N_max * 128));
+      const buf_rsrc rs = kPaged ? make_rsrc(a.keys, pool_lim)
+                                 : make_rsrc(static_cast<const uint8_t*>(a.keys) + koff0 * 128,
+                                             static_cast<uint32_t>(N_max * 128));
       const uint32_t k0 = t0 * kGroupKeys;                 // first key of the run
       const uint32_t n_st = ((t1 - t0) * kGroupKeys + kShareStepKeys - 1) / kShareStepKeys;
       const uint32_t voff0 = (k0 + static_cast<uint32_t>(wv) * 16u + j16) * 128u + g * 32u;
+      // paged: lane s holds the table entry of the wave's block in step s
+      // (n_st <= 32); a block past the query's visible rows reads block 0
+      // (masked: its scores are never stored)
+      int32_t tab_e = 0;
+      if (kPaged) {
+        const uint32_t key = k0 + static_cast<uint32_t>(lane) * kShareStepKeys + static_cast<uint32_t>(wv) * 16u;
+        const uint32_t lb = key >> a.blk_shift;
+        const bool ok = static_cast<uint32_t>(lane) < n_st && key < static_cast<uint64_t>(N_max);
+        tab_e = __builtin_amdgcn_raw_buffer_load_b32(table_rsrc(a, koff0), ok ? static_cast<int>(lb * 4u)
+                                                                               : static_cast<int>(0x80000000u), 0, 0);
+      }
       // step s -> buffer s % 2; its loads went out two steps earlier
       auto load = [&](uint4 (&kr)[2], uint32_t st) __attribute__((always_inline)) {
-        const uint32_t o = st < n_st ? voff0 + st * (kShareStepKeys * 128u) : 0x80000000u;   // past the run: no traffic
+        uint32_t o;
+        if (kPaged) {
+          const uint32_t key = k0 + st * kShareStepKeys + static_cast<uint32_t>(wv) * 16u;
+          const uint32_t blk = static_cast<uint32_t>(__builtin_amdgcn_readlane(tab_e, static_cast<int>(st & 63u)));
+          const uint32_t row = (blk << a.blk_shift) | (key & ((1u << a.blk_shift) - 1u));
+          o = st < n_st ? (row + static_cast<uint32_t>(j16)) * 128u + static_cast<uint32_t>(g) * 32u : 0x80000000u;
+        } else {
+          o = st < n_st ? voff0 + st * (kShareStepKeys * 128u) : 0x80000000u;   // past the run: no traffic
+        }
         kr[0] = buf_load_x4(rs, o, 0);
         kr[1] = buf_load_x4(rs, o + 16u, 0);
       };
@@ -571,13 +610,17 @@ __global__ void __launch_bounds__(share_q<NHB>() * 64) indexer_fp8_shared_kernel
     } else {
       // the wave's own rows, group by group (no barriers: the branch is
       // uniform over the workgroup and this path has none)
-      const buf_rsrc rs = make_rsrc(static_cast<const uint8_t*>(a.keys) + koff_i * 128,
-                                    static_cast<uint32_t>(N_i * 128));
+      const buf_rsrc rs = kPaged ? make_rsrc(a.keys, pool_lim)
+                                 : make_rsrc(static_cast<const uint8_t*>(a.keys) + koff_i * 128,
+                                             static_cast<uint32_t>(N_i * 128));
       const uint32_t voff0 = (t0 * kGroupKeys + j16) * 128u + g * 32u;
       const int ng = static_cast<int>(t1 - t0);
+      PagedTab pt{};
+      if (kPaged) paged_tab_load(a, i, t0, 1u, ng, lane, pt);
       uint4 ka[4][2];
       for (int t = 0; t < ng; ++t) {
-        load_group_fp8(rs, voff0, kGroupKeys * 128u, t, ng, ka);
+        if (kPaged) load_group_fp8_paged(rs, pt, a.blk_shift, t0, 1u, t, ng, j16, g, ka);
+        else load_group_fp8(rs, voff0, kGroupKeys * 128u, t, ng, ka);
         group_fp8<NHB>(ka, qb, wr, cp, pend, static_cast<int>((t0 + static_cast<uint32_t>(t)) * kGroupKeys * 4u),
                        out_rs, out_off);
       }
@@ -868,7 +911,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
       else hipLaunchKernelGGL((K<NB, false, false>), dim3(grid), dim3(256), 0, stream, a, n_items, n_chunk, r); \
     }                                                                                                    \
     break;
-  if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries && !paged) {
+  if (a.fmt == CSA_FP8 && a.nq >= kShareMinQueries) {
     // QS queries (waves) per workgroup; resident workgroups per CU from the
     // kernel's register count (two waves per SIMD at 64 heads and more)
     const int qs = nhb >= 8 ? share_q<8>() : share_q<1>();
@@ -879,13 +922,19 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     const int64_t cap_o = static_cast<int64_t>(device_cu_count()) * (waves_cu / qs);   // resident workgroups
     const unsigned grid_s = static_cast<unsigned>(units < cap_o ? units : cap_o);
     const dim3 blk(static_cast<unsigned>(qs * 64));
+#define CSA_SHARED_CASE(NB)                                                                              \
+  case NB:                                                                                               \
+    if (paged) hipLaunchKernelGGL((indexer_fp8_shared_kernel<NB, true>), dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); \
+    else hipLaunchKernelGGL((indexer_fp8_shared_kernel<NB, false>), dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); \
+    break;
     switch (nhb) {
-      case 1: hipLaunchKernelGGL(indexer_fp8_shared_kernel<1>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
-      case 2: hipLaunchKernelGGL(indexer_fp8_shared_kernel<2>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
-      case 4: hipLaunchKernelGGL(indexer_fp8_shared_kernel<4>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
-      case 8: hipLaunchKernelGGL(indexer_fp8_shared_kernel<8>, dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); break;
+      CSA_SHARED_CASE(1)
+      CSA_SHARED_CASE(2)
+      CSA_SHARED_CASE(4)
+      CSA_SHARED_CASE(8)
       default: return hipErrorInvalidValue;
     }
+#undef CSA_SHARED_CASE
     return hipGetLastError();
   }
   if (a.fmt == CSA_FP8) {

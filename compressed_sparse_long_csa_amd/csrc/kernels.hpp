@@ -43,6 +43,8 @@ struct IndexerArgs {
   // paged keys (blk_table != nullptr; key_off unused): row s of query i is pool
   // row blk_table[i * blk_stride + (s >> blk_shift)] * 2^blk_shift + (s mod 2^blk_shift)
   const int32_t* blk_table; int64_t blk_stride; int blk_shift; int64_t pool_rows;
+  // query i reads table row blk_row[i] (clamped into [0, blk_rows)) in place of i
+  const int32_t* blk_row; int64_t blk_rows;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 // jobs (n <= kMaxCompressJobs, none empty) and the indexer in one launch when

@@ -269,7 +269,8 @@ csa_status csa_compress_score(const csa_compress_job* jobs /*[host]*/, int n_job
  * scores, no fault).
  * Supported: FP8 / MXFP4 keys with indexer_score's head and dim rules,
  * block_rows a power of two in [16, 2^20], a pool smaller than 4 GiB
- * (UNSUPPORTED otherwise).  Every batch size runs the streaming kernel.
+ * (UNSUPPORTED otherwise).  Batches take the kernels of indexer_score (the
+ * shared-key kernel for FP8 batches of 1024 queries or more).
  * Errors: those of indexer_score (block_table takes key_off's place in the
  * null-pointer check); INVALID_ARG for bad block_rows / blocks_per_seq /
  * pool_rows.
@@ -279,6 +280,32 @@ csa_status indexer_score_paged(const void* q_idx, const float* w, int nq, int n_
                                const int32_t* block_table, int64_t blocks_per_seq, int block_rows,
                                const int64_t* q_pos, int m, float* scores, int64_t ld,
                                hipStream_t stream);
+
+/*
+ * indexer_score_paged_rows -- indexer_score_paged with a table row per query.
+ *
+ * Source: as indexer_score_paged (硅星人 article, classic-cache paragraph).
+ *
+ * Query i reads block-table row r = q_block_row[i] (q_block_row NULL: r = i)
+ * of a table of table_rows rows: its logical row s is row
+ *   block_table[r * blocks_per_seq + (s / block_rows)] * block_rows + s % block_rows
+ * of key_pool.  The queries of one sequence in a prefill chunk share one
+ * table row.  In the shared-key kernel (FP8, 1024 queries or more), queries
+ * of one workgroup that name the same row read each key once for all of
+ * them.  A q_block_row entry outside [0, table_rows) is clamped into it
+ * (memory safety only: the result is then that row's).  The scores are the
+ * bits indexer_score gives for the same keys laid out contiguously.
+ *
+ *   block_table  [table_rows, blocks_per_seq] int32;  q_block_row  [nq] int32 or NULL
+ * Preconditions, support and errors: those of indexer_score_paged; also
+ * INVALID_ARG for table_rows outside [1, 2^31], or q_block_row NULL with
+ * table_rows < nq.
+ */
+csa_status indexer_score_paged_rows(const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                                    const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                                    const int32_t* block_table, int64_t table_rows, int64_t blocks_per_seq,
+                                    int block_rows, const int32_t* q_block_row, const int64_t* q_pos, int m,
+                                    float* scores, int64_t ld, hipStream_t stream);
 
 /*
  * topk_select -- the top-k selector.

@@ -239,6 +239,17 @@ def test_paged_entry_points_argument_errors(lib):
     assert idx(d=96) == UNSUPPORTED
     assert "indexer_score_paged" in _last_error(lib)
 
+    def idr(nq=2, table_rows=4, qrow=p, br=32):
+        return lib.indexer_score_paged_rows(p, p, nq, 64, 128, p, csa.FP8, ctypes.c_int64(1000), tbl,
+                                            ctypes.c_int64(table_rows), ctypes.c_int64(10), br, qrow, p, 4, p,
+                                            ctypes.c_int64(1024), None)
+    assert idr(table_rows=0) == INVALID
+    assert idr(table_rows=1 << 32) == INVALID
+    assert idr(br=24) == INVALID
+    assert idr(nq=5, table_rows=4, qrow=None) == INVALID   # query 4 would read table row 4
+    assert "indexer_score_paged_rows" in _last_error(lib)
+    assert idr(nq=0) == OK
+
     def att(q_fmt=csa.BF16, kv_fmt=csa.SPLIT, br=32, bps=10, pool_rows=1000, table=tbl):
         return lib.hybrid_attn_decode_paged(p, q_fmt, 2, 64, 512, p, None, ctypes.c_float(1e-6), 64,
                                             ctypes.c_float(1e4), p, kv_fmt, ctypes.c_int64(pool_rows), table,

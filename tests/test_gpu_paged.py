@@ -1,4 +1,4 @@
-"""Paged caches: indexer_score_paged and hybrid_attn_decode_paged read a
+"""Paged caches: indexer_score_paged(_rows) and hybrid_attn_decode_paged read a
 query's keys / entries through a block table (硅星人 article, classic-cache
 paragraph: fixed 128-token blocks of 32 CSA entries).  The same rows, paged
 in shuffled blocks of a pool, must give the bits of the contiguous calls --
@@ -68,6 +68,58 @@ def test_indexer_paged_long_rows_interleaved_shares():
     inp = synth.decode_inputs(611, lengths, m=4, H=16, D=512, R=64, idx_fmt=csa.FP8, H_I=64)
     a, b = _indexer_pair(inp, 32, 8)
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("H_I,BR,fmt", [(64, 32, csa.FP8), (32, 16, csa.FP8), (128, 64, csa.FP8),
+                                        (64, 32, csa.MXFP4)])
+def test_indexer_paged_rows_matches_contiguous_bits(H_I, BR, fmt):
+    """A prefill chunk of two sequences (1,102 queries: FP8 takes the
+    shared-key kernel, one four-query block straddling the two sequences)
+    reads each sequence's keys through one shared block-table row
+    (q_block_row) of a table with spare rows; the scores carry the bits of
+    indexer_score over the same keys stored contiguously.  So do the same
+    queries with one table row each (q_block_row NULL), and a small batch of
+    picked queries (the streaming kernel) naming the shared rows."""
+    gen = synth.device_generator(81 + H_I + BR)
+    rng = np.random.default_rng(82 + H_I + BR)
+    m, d_I = 4, 128
+    n_a, n_b = 40000, 5000
+    keys = synth.device_rows(gen, n_a + n_b, d_I, fmt)
+    nq_a, nq_b = 701, 401
+    q_pos = np.concatenate([rng.integers(0, n_a * m, nq_a), rng.integers(0, n_b * m, nq_b)]).astype(np.int64)
+    q_pos[:8] = [n_a * m - 1, 3, 64 * m - 1, 64 * m, 2048 * m + 5, n_a * m - 2, 0, 17]
+    key_off = np.concatenate([np.zeros(nq_a), np.full(nq_b, n_a)]).astype(np.int64)
+    nq = nq_a + nq_b
+    q_idx = synth.device_rows(gen, nq * H_I, d_I, fmt).reshape(nq, H_I, -1)
+    w = torch.rand((nq, H_I), generator=gen, device=DEV, dtype=torch.float32)
+    ld = n_a
+    ref = torch.full((nq, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score(q_idx, w, nq, H_I, d_I, keys, fmt, dev(key_off), dev(q_pos), m, ref, ld)
+    rb = synth.row_bytes(fmt, d_I)
+    pool, tab2, bps, pool_rows = _paginate(keys.cpu().numpy().reshape(-1, rb), [n_a, n_b], [0, n_a], BR, rng)
+    table = rng.integers(0, pool_rows // BR, size=(4, bps)).astype(np.int32)   # rows 0 and 2: spare
+    table[1], table[3] = tab2[0], tab2[1]
+    q_row = np.array([1] * nq_a + [3] * nq_b, np.int32)
+    pool_d, q_pos_d = dev(pool), dev(q_pos)
+    got = torch.full((nq, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score_paged_rows(q_idx, w, nq, H_I, d_I, pool_d, fmt, pool_rows, dev(table), 4, bps, BR,
+                                 dev(q_row), q_pos_d, m, got, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), got.view(torch.int32)), "shared table rows: bits differ"
+    if H_I == 64 and fmt == csa.FP8:
+        per_q = torch.full((nq, ld), -7.0, dtype=torch.float32, device=DEV)
+        csa.indexer_score_paged_rows(q_idx, w, nq, H_I, d_I, pool_d, fmt, pool_rows, dev(table[q_row]), nq, bps,
+                                     BR, None, q_pos_d, m, per_q, ld)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int32), per_q.view(torch.int32)), "a table row per query: bits differ"
+    picks = np.array([0, 1, 2, 4, 7, 350, 699, 700, 701, 702, 1100, 1101])
+    pk = torch.as_tensor(picks, device=DEV)
+    small = torch.full((len(picks), ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score_paged_rows(q_idx[pk].contiguous(), w[pk].contiguous(), len(picks), H_I, d_I, pool_d, fmt,
+                                 pool_rows, dev(table), 4, bps, BR, dev(q_row[picks]), dev(q_pos[picks]), m, small,
+                                 ld)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[pk].view(torch.int32), small.view(torch.int32)), "picked queries: bits differ"
 
 
 def _ring(win, win_len, rng):
