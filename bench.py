@@ -890,7 +890,41 @@ def prefill_leg(reps=10):
            "attn_tflops": tflops(f_attn, us["hybrid_attn_prefill"]),
            "attn_mfma_frac": tflops(f_attn, us["hybrid_attn_prefill"]) / BF16_PEAK_TFLOPS,
            "topk_gbps": topk_bytes / (us["topk_select"] * 1e-6) / 1e9}
-    del kv, keys, tok, scores, q, q_idx
+    # the same chunk over paged caches: entries and index keys in shuffled
+    # 32-entry blocks (one 128-token block each) of two pools, one block-table
+    # row that every query of the chunk names
+    br = 32
+    n_blk = (n_tot + br - 1) // br
+    total = n_blk + 8
+    perm = torch.randperm(total, generator=gen, device=cuda)[:n_blk]
+    def paged(rows):
+        rb = rows.shape[-1]
+        pool = torch.zeros((total * br, rb), dtype=torch.uint8, device=cuda)
+        padded = torch.zeros((n_blk * br, rb), dtype=torch.uint8, device=cuda)
+        padded[:n_tot] = rows.view(n_tot, rb)
+        pool.view(total, br, rb)[perm] = padded.view(n_blk, br, rb)
+        return pool
+    kv_pool, key_pool = paged(kv.view(n_tot, -1)), paged(keys.view(n_tot, -1))
+    table = perm.to(torch.int32).reshape(1, n_blk).contiguous()
+    q_row = torch.zeros(chunk, dtype=torch.int32, device=cuda)
+    pk = [("indexer_score_paged_rows", lambda: csa.indexer_score_paged_rows(
+              q_idx, w, chunk, H_I, d_I, key_pool, csa.FP8, total * br, table, 1, n_blk, br, q_row, q_pos, m,
+              scores, n_tot, check=False)),
+          ("hybrid_attn_prefill_paged", lambda: csa.hybrid_attn_prefill_paged(
+              q, csa.BF16, chunk, H, D, q_pos, None, EPS, R, BASE, kv_pool, csa.SPLIT, total * br, table, 1, n_blk,
+              br, q_row, m, idx, k, tok, csa.BF16, zeros, tp0, n_win, sinks, 1.0 / np.sqrt(D), out, csa.BF16,
+              check=False))]
+    kernels[1][1]()
+    kernels[3][1]()
+    ref_scores, ref_out = scores.clone(), out.clone()
+    for _, f in pk:
+        f()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref_scores.view(torch.int32), scores.view(torch.int32)) and torch.equal(ref_out, out))
+    del ref_scores, ref_out
+    res["paged"] = {"block_rows": br, "kernels_us": {n: round(_batch_period([f], reps), 1) for n, f in pk},
+                    "bits_equal_contiguous": same}
+    del kv, keys, tok, scores, q, q_idx, kv_pool, key_pool
     torch.cuda.empty_cache()
     return res
 
