@@ -25,7 +25,8 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_by
            "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
            "indexer_score_paged", "indexer_score_paged_rows", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
-           "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged")
+           "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged",
+           "csa_debug_poison_lds")
 
 _lib = None
 
@@ -85,6 +86,8 @@ def load_library():
     lib.hybrid_attn_prefill_paged.restype = I
     lib.hybrid_attn_prefill_paged.argtypes = [P, I, I, I, I, P, P, F, I, F, P, I, I64, P, I64, I64, I, P, I, P, I,
                                               P, I, P, P, I, P, F, P, I, I, P]
+    lib.csa_debug_poison_lds.restype = I
+    lib.csa_debug_poison_lds.argtypes = [ctypes.c_uint32, P]
     _lib = lib
     return lib
 
@@ -437,3 +440,8 @@ def hybrid_attn_prefill_paged(q, q_fmt, nq, H, D, q_pos, q_norm_w, eps, rope_dim
                                          table_rows, blocks_per_seq, block_rows, _ptr(q_block_row), m, _ptr(idx),
                                          k, _ptr(tok), tok_fmt, _ptr(tok_off), _ptr(tok_pos0), n_win,
                                          _ptr(sinks), scale, _ptr(out), out_fmt, variant, _stream(stream)))
+
+
+def debug_poison_lds(pattern, stream=None):
+    """Fill every CU's LDS with the 32-bit pattern (a test diagnostic)."""
+    _check(load_library().csa_debug_poison_lds(pattern & 0xffffffff, _stream(stream)))

@@ -1029,6 +1029,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (f32) {
     const int units = a.nq * a.H;
     const dim3 grid((units + 3) / 4);
+    log_launch("attention: fp32 path, %d queries x %d heads, D %d, grid %u x 256 threads", a.nq, a.H, a.D, grid.x);
     switch (a.D / 64) {
       case 2: hipLaunchKernelGGL(attn_f32_kernel<2>, grid, dim3(256), 0, stream, a); break;
       case 4: hipLaunchKernelGGL(attn_f32_kernel<4>, grid, dim3(256), 0, stream, a); break;
@@ -1039,10 +1040,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int base_units = a.nq * (a.H / 16);
-  const int dvs = pick_dvs(a.variant, base_units, device_cu_count());
+  const int variant = env_variant(a.variant);
+  const int dvs = pick_dvs(variant, base_units, device_cu_count());
   const int units = base_units * dvs;
   const int n_pad = (units + 7) / 8 * 8;
   const size_t shm = sizeof(AttnSmem);
+  log_launch("attention: MFMA path%s, %d queries x %d heads, variant %s (%s), %d output-dim slices, "
+             "grid %d x 256 threads (%d padding), LDS %zu B",
+             a.blk_table != nullptr ? " (paged)" : "", a.nq, a.H,
+             dvs == 2 ? "HIGH_OCC" : "LOW_OCC",
+             a.variant != CSA_VARIANT_AUTO ? "requested" : (variant != CSA_VARIANT_AUTO ? "CSA_VARIANT" : "auto"),
+             dvs, n_pad,
+             n_pad - units, shm);
   // the workgroup needs more than the default 64 KB of dynamic LDS
   static thread_local int attr_set_dev = -1;
   int dev = 0;

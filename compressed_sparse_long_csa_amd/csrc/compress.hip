@@ -86,6 +86,8 @@ hipError_t launch_compress_jobs(const CompressArgs* jobs, int n, hipStream_t str
   if (J.n == 0) return hipSuccess;
   const int64_t total = J.blk0[J.n];
   const int64_t grid = total < 65536 ? total : 65536;
+  log_launch("compress: %d jobs, %lld blocks, grid %lld x %d threads", J.n, static_cast<long long>(total),
+             static_cast<long long>(grid), kThreads);
   if (any)
     hipLaunchKernelGGL(compress_jobs_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
                        shm_bytes(maxD), stream, J);

@@ -3,6 +3,8 @@
 #include <stddef.h>
 #include <stdio.h>
 #include <stdarg.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "kernels.hpp"
 
@@ -16,6 +18,7 @@ csa_status fail(csa_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+  if (env_log_level() >= 1) fprintf(stderr, "[csa] error %d: %s\n", static_cast<int>(s), g_err);
   return s;
 }
 
@@ -33,6 +36,35 @@ static_assert(sizeof(csa_compress_job) == 128 && offsetof(csa_compress_job, out_
 static_assert(CSA_COMPRESS_MAX_JOBS == kMaxCompressJobs, "job limit");
 }  // namespace
 
+int env_log_level() {
+  static const int level = [] {
+    const char* v = getenv("CSA_LOG");
+    return v != nullptr && *v != '\0' ? atoi(v) : 0;
+  }();
+  return level;
+}
+
+int env_variant(int requested) {
+  static const int forced = [] {
+    const char* v = getenv("CSA_VARIANT");
+    if (v == nullptr) return static_cast<int>(CSA_VARIANT_AUTO);
+    if (strcmp(v, "high") == 0) return static_cast<int>(CSA_VARIANT_HIGH_OCC);
+    if (strcmp(v, "low") == 0) return static_cast<int>(CSA_VARIANT_LOW_OCC);
+    return static_cast<int>(CSA_VARIANT_AUTO);
+  }();
+  return requested == CSA_VARIANT_AUTO ? forced : requested;
+}
+
+void log_launch(const char* fmt, ...) {
+  if (env_log_level() < 1) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[csa] %s\n", buf);
+}
+
 int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -44,6 +76,17 @@ int device_cu_count() {
   }
   return cached[dev];
 }
+
+namespace {
+constexpr uint32_t kLdsBytesPerCu = 160 * 1024;   // gfx950
+
+__global__ void __launch_bounds__(1024) poison_lds_kernel(uint32_t pattern) {
+  extern __shared__ uint32_t lds_words[];
+  for (uint32_t i = threadIdx.x; i < kLdsBytesPerCu / 4; i += blockDim.x) lds_words[i] = pattern;
+  asm volatile("" : : : "memory");                       // the stores are the kernel's only effect
+  __syncthreads();
+}
+}  // namespace
 
 }  // namespace csa
 
@@ -508,6 +551,23 @@ csa_status hybrid_attn_prefill_paged(const void* q, csa_fmt q_fmt, int nq, int H
              scale, out, out_fmt, static_cast<int>(variant), {}, block_table, blocks_per_seq,
              __builtin_ctz(static_cast<unsigned>(block_rows)), pool_rows, nullptr, q_block_row, table_rows};
   return attn_common(what, a, stream);
+}
+
+csa_status csa_debug_poison_lds(uint32_t pattern, hipStream_t stream) {
+  static thread_local int attr_dev = -1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CSA_ERR_HIP, "csa_debug_poison_lds: no device");
+  if (attr_dev != dev) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&poison_lds_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(kLdsBytesPerCu));
+    if (e != hipSuccess) return launched(e, "csa_debug_poison_lds");
+    attr_dev = dev;
+  }
+  // four workgroups per CU, each holding the whole LDS, so every CU runs some
+  hipLaunchKernelGGL(poison_lds_kernel, dim3(static_cast<unsigned>(device_cu_count()) * 4), dim3(1024),
+                     kLdsBytesPerCu, stream, pattern);
+  return launched(hipGetLastError(), "csa_debug_poison_lds");
 }
 
 }  // extern "C"

@@ -862,6 +862,8 @@ hipError_t launch_compress_score(const CompressArgs* jobs, int n, int key_job, c
   }
   const dim3 grid(static_cast<unsigned>(n_cwg) + p.grid), block(256);
   const size_t shm = cmp::shm_bytes(maxD);
+  log_launch("compress+score: one launch, %d jobs in %d workgroups + FP8 indexer of %d queries in %u workgroups "
+             "(%lld groups per wave)", J.n, n_cwg, a.nq, p.grid, static_cast<long long>(p.R));
   const int r = static_cast<int>(p.R);
   const bool three = !il && p.R == 3;                 // every group of a three-group share in flight
 #define CSA_CS_LAUNCH(NB, IL, ANY, BUF)                                                                    \
@@ -890,6 +892,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
   if (a.fmt == CSA_F32) {
     const int64_t n_chunk = (a.ld + 255) / 256;
     const size_t shm = (static_cast<size_t>(a.H) * a.d + a.H) * sizeof(float);
+    log_launch("indexer: fp32 kernel, %d queries x %d heads, grid %lld x 256 threads", a.nq, a.H,
+               static_cast<long long>(a.nq * n_chunk));
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(static_cast<unsigned>(a.nq * n_chunk)), dim3(256),
                        shm, stream, a, n_chunk);
     return hipGetLastError();
@@ -922,6 +926,9 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
     const int64_t cap_o = static_cast<int64_t>(device_cu_count()) * (waves_cu / qs);   // resident workgroups
     const unsigned grid_s = static_cast<unsigned>(units < cap_o ? units : cap_o);
     const dim3 blk(static_cast<unsigned>(qs * 64));
+    log_launch("indexer: FP8 shared-key kernel%s, %d queries x %d heads, %lld query blocks x %lld key chunks, "
+               "grid %u x %u threads", paged ? " (paged)" : "", a.nq, a.H, static_cast<long long>(n_qblk),
+               static_cast<long long>(n_kchunk), grid_s, blk.x);
 #define CSA_SHARED_CASE(NB)                                                                              \
   case NB:                                                                                               \
     if (paged) hipLaunchKernelGGL((indexer_fp8_shared_kernel<NB, true>), dim3(grid_s), blk, 0, stream, a, n_qblk, n_kchunk); \
@@ -937,6 +944,10 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream) {
 #undef CSA_SHARED_CASE
     return hipGetLastError();
   }
+  log_launch("indexer: %s streaming kernel%s, %d queries x %d heads, ld %lld, %lld items of %d waves x %lld "
+             "groups (%s shares), grid %u x 256 threads", a.fmt == CSA_FP8 ? "FP8" : "MXFP4", paged ? " (paged)" : "",
+             a.nq, a.H, static_cast<long long>(a.ld), static_cast<long long>(n_items), 4, static_cast<long long>(p.R),
+             il ? "interleaved" : "contiguous", grid);
   if (a.fmt == CSA_FP8) {
     switch (nhb) {
       CSA_IDX_CASE(indexer_fp8_kernel, 1)

@@ -102,4 +102,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
 int device_cu_count();
 
+// Diagnostics from the environment, read once per process.  CSA_LOG >= 1:
+// every error message, and each launch's kernel choice and grid, go to
+// stderr.  CSA_VARIANT = high | low: calls that pass CSA_VARIANT_AUTO take
+// that variant instead (explicit variants are kept).
+int env_log_level();
+int env_variant(int requested);
+void log_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 }  // namespace csa

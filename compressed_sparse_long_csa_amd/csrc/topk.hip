@@ -588,6 +588,8 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
   const TopkPlan pl = plan_topk(a.ld, a.nq, a.k);
   if (pl.P == 0) {
     const uint32_t cap = stage_cap(static_cast<uint64_t>(a.ld));
+    log_launch("top-k: one pass, %d rows of %lld scores, k %d, grid %d x %d threads, LDS %zu B", a.nq,
+               static_cast<long long>(a.ld), a.k, a.nq, kThreads, stage_bytes(cap));
     hipLaunchKernelGGL(topk_kernel, dim3(a.nq), dim3(kThreads), stage_bytes(cap), stream, a, cap);
     return hipGetLastError();
   }
@@ -595,6 +597,9 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
   int32_t* cidx = static_cast<int32_t*>(ws);
   float* cscore = reinterpret_cast<float*>(cidx + per);
   const uint32_t cap_s = stage_cap(pl.Cs);
+  log_launch("top-k: two passes, %d rows of %lld scores, k %d, %d slices of %u, grid %lld then %d x %d threads, "
+             "workspace %zu B", a.nq, static_cast<long long>(a.ld), a.k, pl.P, pl.Cs,
+             static_cast<long long>(a.nq) * pl.P, a.nq, kThreads, pl.ws_bytes);
   hipLaunchKernelGGL(topk_slice_kernel, dim3(static_cast<unsigned>(a.nq) * pl.P), dim3(kThreads),
                      stage_bytes(cap_s), stream, a, pl.P, pl.Cs, cap_s, cidx, cscore);
   e = hipGetLastError();

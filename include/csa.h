@@ -530,6 +530,19 @@ csa_status hybrid_attn_prefill_paged(const void* q, csa_fmt q_fmt, int nq, int H
                                      const float* sinks, float scale, void* out, csa_fmt out_fmt,
                                      csa_variant variant, hipStream_t stream);
 
+/*
+ * csa_debug_poison_lds -- fill the LDS of every compute unit with a pattern.
+ *
+ * A diagnostic for tests of the kernels' LDS hygiene, not a step of the
+ * path: launched on `stream` before a kernel, it leaves every CU's 160 KB of
+ * LDS holding the 32-bit `pattern`, so a kernel that read LDS it had not
+ * written first would give results that depend on the pattern.  The
+ * hardware does not promise that a later kernel finds these bytes; equal
+ * results under several patterns are evidence, not proof.
+ * Errors: HIP for a failed launch.
+ */
+csa_status csa_debug_poison_lds(uint32_t pattern, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

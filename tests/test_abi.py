@@ -4,6 +4,8 @@ device work (no compute call runs here)."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -278,3 +280,16 @@ def test_paged_entry_points_argument_errors(lib):
     assert pre(nq=5, table_rows=4, qrow=None) == INVALID   # query 4 would read table row 4
     assert "hybrid_attn_prefill_paged" in _last_error(lib)
     assert pre(nq=0) == OK
+
+
+def test_log_names_errors_on_stderr():
+    """CSA_LOG=1 copies every error message to stderr (read once per process)."""
+    code = ("import sys, ctypes; sys.path.insert(0, sys.argv[1]); import compressed_sparse_long_csa_amd as c; "
+            "lib = c.load_library(); "
+            "print(lib.topk_select(None, ctypes.c_int64(100), 1, None, 8, None, None, None, 0, None))")
+    for level, shown in (("1", True), ("0", False)):
+        r = subprocess.run([sys.executable, "-c", code, ROOT], env=dict(os.environ, CSA_LOG=level),
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        assert r.stdout.strip().splitlines()[-1] == str(INVALID)
+        assert ("[csa] error 1: topk_select" in r.stderr) == shown, r.stderr[-2000:]

@@ -7,7 +7,9 @@ of n_win slots.  After the stream the pool, read in logical order, holds the
 bytes of one bulk csa_compress of every complete block; the ring holds the
 bulk window rows of the last n_win tokens; and the last token's attention
 over the paged cache and the ring equals the contiguous call bit for bit and
-the oracle within the low-precision bar."""
+the oracle within the low-precision bar.  A stream saved to the host
+mid-way, restored into fresh buffers and continued ends with the same bytes
+and the same attention bits."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +104,63 @@ def test_state_cache_stream(m, T, BR):
     ref = OM.decode_one(qh, p, ents, win, sinks.astype(np.float64), scale, m, idx=None, eps=EPS, R=R,
                         base=ROPE_BASE)
     assert_lowp_close(decode_out(out_c, csa.BF16, 1, H, D)[0], ref, what=f"state-cache stream m={m}")
+
+
+def _run_stream(x, gate, m, D, R, n_win, pool, ring, phys, t0, t1):
+    for t in range(t0, t1):
+        if (t + 1) % m == 0:
+            j = t // m
+            _compress(x[t + 1 - m: t + 1], gate[t + 1 - m: t + 1], m, m, t + 1 - m, phys(j), pool, csa.SPLIT, D, R)
+        _compress(x[t: t + 1], gate[t: t + 1], 1, 1, t, t % n_win, ring, csa.BF16, D, R)
+
+
+@pytest.mark.parametrize("m,T,BR,cut", [(4, 4 * 61 + 2, 16, 4 * 30 + 1), (128, 128 * 2 + 9, 1, 200)])
+def test_cache_save_restore_continue(m, T, BR, cut):
+    """Resume: the caches are the caller's memory, so saving them is a copy.
+    A stream stopped after token `cut`, its paged pool and window ring copied
+    to the host, restored into fresh buffers that held other bytes, and
+    continued, ends with the bytes of the uninterrupted stream, and the last
+    token's paged attention has the same bits."""
+    D, R, H, n_win = 512, 64, 16, 128
+    rng = np.random.default_rng(1000 + m)
+    x = torch.as_tensor(rng.standard_normal((T, D), dtype=np.float32), device=DEV).to(torch.bfloat16)
+    gate = torch.as_tensor(rng.standard_normal((T, 1), dtype=np.float32), device=DEV)
+    rb, wb = synth.row_bytes(csa.SPLIT, D, R), synth.row_bytes(csa.BF16, D, R)
+    n_blk = (T // m + BR - 1) // BR
+    total = n_blk + 2
+    table = rng.permutation(total)[:n_blk].astype(np.int32)
+    phys = lambda j: int(table[j // BR]) * BR + j % BR  # noqa: E731
+    fresh = lambda n, w: torch.as_tensor(rng.integers(0, 256, size=(n, w), dtype=np.uint8), device=DEV)  # noqa: E731
+    pool_a, ring_a = fresh(total * BR, rb), fresh(n_win, wb)
+    pool_b, ring_b = fresh(total * BR, rb), fresh(n_win, wb)
+    pool_b.copy_(pool_a)
+    ring_b.copy_(ring_a)
+    # run A: uninterrupted
+    _run_stream(x, gate, m, D, R, n_win, pool_a, ring_a, phys, 0, T)
+    # run B: stop at `cut`, save to the host, restore into new buffers, continue
+    _run_stream(x, gate, m, D, R, n_win, pool_b, ring_b, phys, 0, cut)
+    torch.cuda.synchronize()
+    saved_pool, saved_ring = pool_b.cpu(), ring_b.cpu()
+    pool_c, ring_c = fresh(total * BR, rb), fresh(n_win, wb)
+    pool_c.copy_(saved_pool.to(DEV))
+    ring_c.copy_(saved_ring.to(DEV))
+    del pool_b, ring_b
+    _run_stream(x, gate, m, D, R, n_win, pool_c, ring_c, phys, cut, T)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_a, pool_c), "the resumed pool differs"
+    assert torch.equal(ring_a, ring_c), "the resumed window ring differs"
+    p = T - 1
+    q_b = torch.as_tensor(rng.standard_normal((1, H, D), dtype=np.float32), device=DEV).to(torch.bfloat16)
+    sinks = dev(rng.standard_normal(H).astype(np.float32))
+    wl = min(n_win, p + 1)
+    start = dev(np.array([(p + 1 - wl) % n_win], np.int32))
+    outs = []
+    for pool, ring in ((pool_a, ring_a), (pool_c, ring_c)):
+        out = gpu_bytes(H * D * 2)
+        csa.hybrid_attn_decode_paged(q_b, csa.BF16, 1, H, D, _i64([p]), None, EPS, R, ROPE_BASE, pool, csa.SPLIT,
+                                     total * BR, dev(table), n_blk, BR, m, None, 0, ring, csa.BF16, n_win,
+                                     dev(np.array([wl], np.int32)), sinks, 1.0 / np.sqrt(D), out, csa.BF16,
+                                     win_start=start)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "attention after the resume differs"
