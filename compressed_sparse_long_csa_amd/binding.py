@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
-           "csa_compress", "csa_compress_batch", "csa_compress_score", "indexer_score",
+           "csa_compress", "csa_compress_batch", "csa_compress_score", "csa_compress_score_paged", "indexer_score",
            "indexer_score_paged", "indexer_score_paged_rows", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
            "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged",
@@ -60,6 +60,9 @@ def load_library():
     lib.csa_compress_score.restype = I
     lib.csa_compress_score.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, P, P, I, P,
                                        I64, P]
+    lib.csa_compress_score_paged.restype = I
+    lib.csa_compress_score_paged.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, I64, P, I64, I64, I,
+                                             P, P, I, P, I64, P]
     lib.indexer_score_paged.restype = I
     lib.indexer_score_paged.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I, P, I, P, I64, P]
     lib.indexer_score_paged_rows.restype = I
@@ -213,6 +216,23 @@ def csa_compress_score(jobs, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q
     _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check)
     _check(lib.csa_compress_score(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(keys), fmt,
                                   _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
+
+
+def csa_compress_score_paged(jobs, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table, table_rows,
+                             blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, stream=None, check=True):
+    """csa_compress_batch(jobs) then indexer_score_paged_rows(...), in one launch where it can."""
+    lib = load_library()
+    arr = _job_array(jobs, check)
+    rb = row_bytes(fmt, d_idx)
+    _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
+    _need(w, "w", torch.float32, min_numel=nq * n_heads)
+    _need(q_pos, "q_pos", torch.int64, min_numel=nq)
+    _need(scores, "scores", torch.float32, min_numel=nq * ld)
+    _paged_checks(block_table, nq, blocks_per_seq, block_rows, key_pool, pool_rows, rb, q_pos, m, ld, check,
+                  table_rows=table_rows, q_block_row=q_block_row)
+    _check(lib.csa_compress_score_paged(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool),
+                                        fmt, pool_rows, _ptr(block_table), table_rows, blocks_per_seq, block_rows,
+                                        _ptr(q_block_row), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
 
 
 def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld,

@@ -268,18 +268,16 @@ csa_status indexer_score(const void* q_idx, const float* w, int nq, int n_heads,
   return launched(launch_indexer(a, stream), "indexer_score");
 }
 
-static csa_status indexer_paged(const char* what, const void* q_idx, const float* w, int nq, int n_heads,
-                                int d_idx, const void* key_pool, csa_fmt fmt, int64_t pool_rows,
-                                const int32_t* block_table, int64_t table_rows, int64_t blocks_per_seq,
-                                int block_rows, const int32_t* q_block_row, const int64_t* q_pos, int m,
-                                float* scores, int64_t ld, hipStream_t stream) {
+// The paged indexer's arguments: the checks of indexer_score plus the block
+// geometry; *empty when there is nothing to score.
+static csa_status paged_args(const char* what, const void* q_idx, const float* w, int nq, int n_heads, int d_idx,
+                             const void* key_pool, csa_fmt fmt, int64_t pool_rows, const int32_t* block_table,
+                             int64_t table_rows, int64_t blocks_per_seq, int block_rows, const int32_t* q_block_row,
+                             const int64_t* q_pos, int m, float* scores, int64_t ld, IndexerArgs* a, bool* empty) {
   if (fmt == CSA_F32) return fail(CSA_ERR_UNSUPPORTED, "%s: the paged path takes FP8 or MXFP4 keys", what);
-  IndexerArgs a{};
-  bool empty = false;
   // (block_table stands in for key_off in the shared null-pointer check)
   const csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, key_pool, fmt,
-                                     reinterpret_cast<const int64_t*>(block_table), q_pos, m, scores, ld, &a,
-                                     &empty);
+                                     reinterpret_cast<const int64_t*>(block_table), q_pos, m, scores, ld, a, empty);
   if (st != CSA_OK) return st;
   if (block_rows < 16 || block_rows > (1 << 20) || (block_rows & (block_rows - 1)) != 0)
     return fail(CSA_ERR_INVALID_ARG, "%s: block_rows must be a power of two in [16, 2^20]", what);
@@ -292,14 +290,28 @@ static csa_status indexer_paged(const char* what, const void* q_idx, const float
     return fail(CSA_ERR_UNSUPPORTED, "%s: the key pool must be smaller than 4 GiB", what);
   if (!q_block_row && table_rows < nq)
     return fail(CSA_ERR_INVALID_ARG, "%s: without q_block_row, query i reads table row i (table_rows < nq)", what);
+  a->key_off = nullptr;
+  a->blk_table = block_table;
+  a->blk_stride = blocks_per_seq;
+  a->blk_shift = __builtin_ctz(static_cast<unsigned>(block_rows));
+  a->pool_rows = pool_rows;
+  a->blk_row = q_block_row;
+  a->blk_rows = table_rows;
+  return CSA_OK;
+}
+
+static csa_status indexer_paged(const char* what, const void* q_idx, const float* w, int nq, int n_heads,
+                                int d_idx, const void* key_pool, csa_fmt fmt, int64_t pool_rows,
+                                const int32_t* block_table, int64_t table_rows, int64_t blocks_per_seq,
+                                int block_rows, const int32_t* q_block_row, const int64_t* q_pos, int m,
+                                float* scores, int64_t ld, hipStream_t stream) {
+  IndexerArgs a{};
+  bool empty = false;
+  const csa_status st = paged_args(what, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table,
+                                   table_rows, blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, &a,
+                                   &empty);
+  if (st != CSA_OK) return st;
   if (empty) { g_err[0] = '\0'; return CSA_OK; }
-  a.key_off = nullptr;
-  a.blk_table = block_table;
-  a.blk_stride = blocks_per_seq;
-  a.blk_shift = __builtin_ctz(static_cast<unsigned>(block_rows));
-  a.pool_rows = pool_rows;
-  a.blk_row = q_block_row;
-  a.blk_rows = table_rows;
   return launched(launch_indexer(a, stream), what);
 }
 
@@ -321,16 +333,11 @@ csa_status indexer_score_paged_rows(const void* q_idx, const float* w, int nq, i
                        stream);
 }
 
-csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
-                              const float* w, int nq, int n_heads, int d_idx, const void* keys,
-                              csa_fmt fmt, const int64_t* key_off, const int64_t* q_pos, int m,
-                              float* scores, int64_t ld, hipStream_t stream) {
-  const char* what = "csa_compress_score";
-  IndexerArgs ia{};
-  bool no_queries = false;
-  csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores,
-                               ld, &ia, &no_queries);
-  if (st != CSA_OK) return st;
+// The jobs of a compress + score call (the key job: the one that writes
+// `keys`) and its launch; ia holds the indexer's arguments.
+static csa_status compress_score_common(const char* what, const csa_compress_job* jobs, int n_jobs,
+                                        const void* keys, csa_fmt fmt, int d_idx, int nq, const IndexerArgs& ia,
+                                        bool no_queries, hipStream_t stream) {
   int key = -1;
   if (n_jobs > 0 && jobs) {
     for (int i = 0; i < n_jobs && i < CSA_COMPRESS_MAX_JOBS; ++i) {
@@ -348,12 +355,40 @@ csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const vo
   }
   CompressArgs a[CSA_COMPRESS_MAX_JOBS];
   int n = 0, map_key = -1;
-  st = batch_args(what, jobs, n_jobs, key, a, &n, &map_key);
+  const csa_status st = batch_args(what, jobs, n_jobs, key, a, &n, &map_key);
   if (st != CSA_OK) return st;
   hipError_t e = hipSuccess;
   if (no_queries) e = n > 0 ? launch_compress_jobs(a, n, stream) : hipSuccess;
   else e = launch_compress_score(a, n, map_key, ia, stream);
   return launched(e, what);
+}
+
+csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                              const float* w, int nq, int n_heads, int d_idx, const void* keys,
+                              csa_fmt fmt, const int64_t* key_off, const int64_t* q_pos, int m,
+                              float* scores, int64_t ld, hipStream_t stream) {
+  const char* what = "csa_compress_score";
+  IndexerArgs ia{};
+  bool no_queries = false;
+  const csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores,
+                                     ld, &ia, &no_queries);
+  if (st != CSA_OK) return st;
+  return compress_score_common(what, jobs, n_jobs, keys, fmt, d_idx, nq, ia, no_queries, stream);
+}
+
+csa_status csa_compress_score_paged(const csa_compress_job* jobs, int n_jobs, const void* q_idx, const float* w,
+                                    int nq, int n_heads, int d_idx, const void* key_pool, csa_fmt fmt,
+                                    int64_t pool_rows, const int32_t* block_table, int64_t table_rows,
+                                    int64_t blocks_per_seq, int block_rows, const int32_t* q_block_row,
+                                    const int64_t* q_pos, int m, float* scores, int64_t ld, hipStream_t stream) {
+  const char* what = "csa_compress_score_paged";
+  IndexerArgs ia{};
+  bool no_queries = false;
+  const csa_status st = paged_args(what, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table,
+                                   table_rows, blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, &ia,
+                                   &no_queries);
+  if (st != CSA_OK) return st;
+  return compress_score_common(what, jobs, n_jobs, key_pool, fmt, d_idx, nq, ia, no_queries, stream);
 }
 
 size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k) {

@@ -135,6 +135,15 @@ __device__ __forceinline__ buf_rsrc table_rsrc(const IndexerArgs& a, int64_t row
   return make_rsrc(a.blk_table + row * a.blk_stride, static_cast<uint32_t>(a.blk_stride * 4));
 }
 
+// Pool row of query i's logical row r (a table entry past the row reads as
+// block 0).  Wave-uniform.
+__device__ __forceinline__ int64_t pool_row(const IndexerArgs& a, int i, int64_t r) {
+  const int64_t lb = r >> a.blk_shift;
+  const int32_t blk = lb < a.blk_stride
+                          ? __builtin_amdgcn_readfirstlane(a.blk_table[table_row(a, i) * a.blk_stride + lb]) : 0;
+  return (static_cast<int64_t>(blk) << a.blk_shift) | (r & ((int64_t{1} << a.blk_shift) - 1));
+}
+
 __device__ __forceinline__ void paged_tab_load(const IndexerArgs& a, int i, uint32_t first, uint32_t step,
                                                int R, int lane, PagedTab& pt) {
   const int sh = a.blk_shift;
@@ -272,7 +281,9 @@ __device__ __forceinline__ void fp8_items(const IndexerArgs& a, int64_t n_items,
     // a segment at row seg_out_row + j)
     int64_t Ns = N;
     if (kNew && N >= 1 && i < nk.nseg) {
-      const int64_t j = uniform64(koff) + N - 1 - uniform64(row0);
+      // (paged: the pool row of the last visible row)
+      const int64_t last = kPaged ? pool_row(a, i, N - 1) : uniform64(koff) + N - 1;
+      const int64_t j = last - uniform64(row0);
       const int64_t end = uniform64(lo) + (j + 1) * nk.m;
       if (j >= 0 && uniform64(lo) % nk.m == 0 && end <= uniform64(hi) && end <= nk.n_tok) Ns = N - 1;
     }
@@ -354,7 +365,7 @@ __global__ void __launch_bounds__(256) indexer_fp8_kernel(IndexerArgs a, int64_t
 // key: the key sits in the MFMA column the streaming kernel gives it
 // ((N - 1) mod 16), with the same dim order, products, chain and head sum,
 // so the score has the same bits.
-template <int NHB>
+template <int NHB, bool kPaged>
 __device__ __forceinline__ void score_new_key(const IndexerArgs& a, const float* y, int s, int64_t row) {
   constexpr int H = NHB * 16;
   if (threadIdx.x >= 64 || s >= a.nq) return;          // wave 0; uniform
@@ -369,10 +380,11 @@ __device__ __forceinline__ void score_new_key(const IndexerArgs& a, const float*
     qraw[hb][1] = qp[1];
     wraw[hb] = *reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(s) * H + hb * 16 + g * 4);
   }
-  const int64_t qpos = scalar_load(a.q_pos, s), koff = scalar_load(a.key_off, s);
+  const int64_t qpos = scalar_load(a.q_pos, s), koff = kPaged ? 0 : scalar_load(a.key_off, s);
   int64_t N = (uniform64(qpos) + 1) / a.m;
   if (N > a.ld) N = a.ld;
-  if (N < 1 || uniform64(koff) + N - 1 != row) return;
+  if (N < 1) return;
+  if ((kPaged ? pool_row(a, s, N - 1) : uniform64(koff) + N - 1) != row) return;
   // lane (column j16, k-slot g) holds dims [32g + 8ks, +8) at k-step ks
   bf16x8 kk[4];
 #pragma unroll
@@ -410,7 +422,7 @@ __device__ __forceinline__ void score_new_key(const IndexerArgs& a, const float*
 // last visible row it is.  The rest stream every other score.  No workgroup
 // waits for another: a query's rows other than its last are not written by
 // the launch, and its last row is scored by exactly one side.
-template <int NHB, bool IL, bool kWithAny, int NB>
+template <int NHB, bool IL, bool kWithAny, int NB, bool kPaged>
 __global__ void __launch_bounds__(256) compress_score_kernel(CompressJobs J, int key_job, NewKeys nk,
                                                              IndexerArgs a, int64_t n_items, int64_t n_chunk,
                                                              int R, int n_cwg) {
@@ -423,12 +435,12 @@ __global__ void __launch_bounds__(256) compress_score_kernel(CompressJobs J, int
       while (j + 1 < J.n && b >= J.blk0[j + 1]) ++j;
       const CompressArgs& c = J.a[j];
       cmp::run_block<kWithAny>(c, J.kind[j], b - J.blk0[j], y, y + c.D, &slot);
-      if (j == key_job && slot.ok) score_new_key<NHB>(a, y, slot.seg, slot.row);
+      if (j == key_job && slot.ok) score_new_key<NHB, kPaged>(a, y, slot.seg, slot.row);
       __syncthreads();                                  // y and slot are reused by the next block
     }
     return;
   }
-  fp8_items<NHB, IL, true, NB>(a, n_items, n_chunk, R, blockIdx.x - n_cwg, gridDim.x - n_cwg, nk);
+  fp8_items<NHB, IL, true, NB, kPaged>(a, n_items, n_chunk, R, blockIdx.x - n_cwg, gridDim.x - n_cwg, nk);
 }
 
 // --------------------------------------------------------------- FP8, d = 128, shared keys
@@ -862,13 +874,19 @@ hipError_t launch_compress_score(const CompressArgs* jobs, int n, int key_job, c
   }
   const dim3 grid(static_cast<unsigned>(n_cwg) + p.grid), block(256);
   const size_t shm = cmp::shm_bytes(maxD);
-  log_launch("compress+score: one launch, %d jobs in %d workgroups + FP8 indexer of %d queries in %u workgroups "
-             "(%lld groups per wave)", J.n, n_cwg, a.nq, p.grid, static_cast<long long>(p.R));
+  const bool paged = a.blk_table != nullptr;
+  log_launch("compress+score: one launch%s, %d jobs in %d workgroups + FP8 indexer of %d queries in %u workgroups "
+             "(%lld groups per wave)", paged ? " (paged keys)" : "", J.n, n_cwg, a.nq, p.grid,
+             static_cast<long long>(p.R));
   const int r = static_cast<int>(p.R);
   const bool three = !il && p.R == 3;                 // every group of a three-group share in flight
 #define CSA_CS_LAUNCH(NB, IL, ANY, BUF)                                                                    \
-  hipLaunchKernelGGL((compress_score_kernel<NB, IL, ANY, BUF>), grid, block, shm, stream, J, kj, nk, a,   \
-                     p.n_items, p.n_chunk, r, n_cwg)
+  do {                                                                                                    \
+    if (paged) hipLaunchKernelGGL((compress_score_kernel<NB, IL, ANY, BUF, true>), grid, block, shm, stream, J, \
+                                  kj, nk, a, p.n_items, p.n_chunk, r, n_cwg);                             \
+    else hipLaunchKernelGGL((compress_score_kernel<NB, IL, ANY, BUF, false>), grid, block, shm, stream, J, kj, \
+                            nk, a, p.n_items, p.n_chunk, r, n_cwg);                                       \
+  } while (0)
 #define CSA_CS_CASE(NB)                                                                                   \
   case NB:                                                                                                \
     if (il) { if (any) CSA_CS_LAUNCH(NB, true, true, 2); else CSA_CS_LAUNCH(NB, true, false, 2); }       \

@@ -249,6 +249,35 @@ csa_status csa_compress_score(const csa_compress_job* jobs /*[host]*/, int n_job
                               hipStream_t stream);
 
 /*
+ * csa_compress_score_paged -- csa_compress_score over a paged key cache.
+ *
+ * Source: the passages of csa_compress_score; 硅星人 article, classic-cache
+ * paragraph (keys in fixed blocks of a shared pool, reached through a block
+ * table).
+ *
+ * The indexer side reads keys as indexer_score_paged_rows does (query i
+ * through table row q_block_row[i], or row i).  The key job writes the key
+ * pool: it is the job whose `out` equals key_pool, and its segment i writes
+ * pool rows seg_out_row[i] + j as csa_compress does, so a segment's new rows
+ * must lie in one block of the pool (a decode step writes one row per
+ * query).  Results: those of csa_compress_batch followed by
+ * indexer_score_paged_rows, when every key row written in segment i is the
+ * pool row of query i's last visible row (the physical row that query i's
+ * table maps logical row N_i - 1 to).
+ *
+ * Arguments: the jobs as for csa_compress_score; the rest as for
+ * indexer_score_paged_rows.
+ * Errors: those of csa_compress_score (with key_pool in place of keys) and of
+ * indexer_score_paged_rows.
+ */
+csa_status csa_compress_score_paged(const csa_compress_job* jobs /*[host]*/, int n_jobs, const void* q_idx,
+                                    const float* w, int nq, int n_heads, int d_idx, const void* key_pool,
+                                    csa_fmt fmt, int64_t pool_rows, const int32_t* block_table,
+                                    int64_t table_rows, int64_t blocks_per_seq, int block_rows,
+                                    const int32_t* q_block_row, const int64_t* q_pos, int m, float* scores,
+                                    int64_t ld, hipStream_t stream);
+
+/*
  * indexer_score_paged -- indexer_score over a paged key cache.
  *
  * Source: the passages of indexer_score; 硅星人 article, classic-cache

@@ -252,6 +252,15 @@ def test_paged_entry_points_argument_errors(lib):
     assert "indexer_score_paged_rows" in _last_error(lib)
     assert idr(nq=0) == OK
 
+    def cs(fmt=csa.FP8, table_rows=4, br=32):
+        return lib.csa_compress_score_paged(None, 0, p, p, 2, 64, 128, p, fmt, ctypes.c_int64(1000), tbl,
+                                            ctypes.c_int64(table_rows), ctypes.c_int64(10), br, p, p, 4, p,
+                                            ctypes.c_int64(1024), None)
+    assert cs(fmt=csa.F32) == UNSUPPORTED
+    assert cs(table_rows=0) == INVALID
+    assert cs(br=8) == INVALID
+    assert "csa_compress_score_paged" in _last_error(lib)
+
     def att(q_fmt=csa.BF16, kv_fmt=csa.SPLIT, br=32, bps=10, pool_rows=1000, table=tbl):
         return lib.hybrid_attn_decode_paged(p, q_fmt, 2, 64, 512, p, None, ctypes.c_float(1e-6), 64,
                                             ctypes.c_float(1e4), p, kv_fmt, ctypes.c_int64(pool_rows), table,

@@ -12,6 +12,7 @@ import torch
 import compressed_sparse_long_csa_amd as csa
 from compressed_sparse_long_csa_amd import synth
 from gpu_common import DEV, EPS, ROPE_BASE, dev
+from test_gpu_paged import _paginate
 from oracle import formats as OF
 from oracle import method as OM
 
@@ -181,3 +182,56 @@ def test_fused_scores_independent_of_batch_order():
     keys1, _, s1 = _run(sp, True)
     assert np.array_equal(keys1, keys0)
     assert np.array_equal(s1.view(np.uint32), s0[perm].view(np.uint32))
+
+
+def _run_paged(st, BR, seed):
+    """The step with the keys in shuffled blocks of a pool (硅星人 article,
+    classic-cache paragraph): the key job writes each new key at the pool row that its query's
+    table maps the last visible row to; the table rows are shuffled and named
+    by q_block_row."""
+    inp, B = st["inp"], st["B"]
+    rng = np.random.default_rng(seed)
+    rb = synth.row_bytes(inp.idx_fmt, inp.d_I)
+    pool, tab, bps, pool_rows = _paginate(inp.keys.reshape(-1, rb), inp.n_ent, inp.kv_off, BR, rng)
+    order = rng.permutation(B)                          # table row r holds query order[r]'s blocks
+    table = tab[order]
+    q_row = np.argsort(order).astype(np.int32)
+    n_ent = inp.n_ent.astype(np.int64)
+    last = [int(tab[b][(n - 1) // BR]) * BR + (n - 1) % BR if n > 0 else 0 for b, n in enumerate(n_ent)]
+    rows_h = np.array([last[b] if st["seg_len"][b] else 0 for b in range(B)], np.int64)
+    pool_d, kv = dev(pool), dev(inp.kv)
+    scores = torch.full((B, st["ld"]), SENTINEL, dtype=torch.float32, device=DEV)
+
+    def job(x, gate, Dj, normalize, Rj, out, fmt, rows):
+        return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=st["n_tok"], D=Dj, m=M, nseg=B,
+                    seg_tok_off=st["seg_off"], seg_pos0=st["pos0"], seg_out_row=rows,
+                    normalize=normalize, norm_w=None, eps=EPS, rope_dim=Rj, rope_base=ROPE_BASE,
+                    out=out, out_fmt=fmt)
+    jobs = [job(st["kv_tok"], st["kv_gate"], D, 1, R, kv, csa.SPLIT, st["rows"]),
+            job(st["key_tok"], st["key_gate"], inp.d_I, 0, 0, pool_d, inp.idx_fmt, dev(rows_h))]
+    csa.csa_compress_score_paged(jobs, st["q_idx"], st["w"], B, inp.H_I, inp.d_I, pool_d, inp.idx_fmt, pool_rows,
+                                 dev(table), B, bps, BR, dev(q_row), st["q_pos"], M, scores, st["ld"])
+    torch.cuda.synchronize()
+    return pool_d.cpu().numpy(), kv.cpu().numpy(), scores.cpu().numpy(), rows_h
+
+
+@pytest.mark.parametrize("H_I,BR,fmt", [(64, 32, csa.FP8), (64, 16, csa.FP8), (128, 64, csa.FP8),
+                                        (64, 32, csa.MXFP4)])
+def test_fused_step_paged_matches_contiguous(H_I, BR, fmt):
+    """csa_compress_score_paged gives the contiguous call's results: every new
+    key's bytes at its pool row, the KV entries, and every score bit (FP8: one
+    launch; MXFP4: the two launches)."""
+    lengths = [65536, 9000, 2052, 132, 8, 40000, 4, 3, 65536, 1000]
+    new = [True, False, True, True, True, False, True, False, True, True]
+    st = _case(lengths, new, H_I, fmt, 700 + H_I + BR)
+    st["seg_len"] = np.where(np.asarray(new), M, 0)
+    keys_c, kv_c, scores_c = _run(st, True)
+    pool, kv_p, scores_p, rows_h = _run_paged(st, BR, 800 + BR)
+    assert np.array_equal(scores_c.view(np.uint32), scores_p.view(np.uint32)), "scores differ"
+    assert np.array_equal(kv_c, kv_p), "KV entries differ"
+    inp = st["inp"]
+    rb = synth.row_bytes(inp.idx_fmt, inp.d_I)
+    kc = keys_c.reshape(-1, rb)
+    for b in np.flatnonzero(new):
+        row_c = int(inp.kv_off[b]) + int(inp.n_ent[b]) - 1
+        assert np.array_equal(kc[row_c], pool[rows_h[b]]), f"query {b}: new key bytes differ"
