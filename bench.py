@@ -149,21 +149,27 @@ def make_replicas(W, R):
     return reps
 
 
-def make_step(W, check=False, fused=True):
-    c, inp = W["c"], W["inp"]
-    B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
+def step_jobs(W):
+    """The decode step's compress jobs: the newest block's KV entry, its
+    indexer key, and the newest token's window row."""
+    B, m, D, R, d_I = W["B"], W["m"], W["D"], W["R"], W["d_I"]
 
     def job(x, gate, n_tok, D, mm, off, pos0, rows, normalize, R_, out, fmt):
         return dict(x=x, x_fmt=csa.BF16, gate=gate, gate_cols=1, n_tok=n_tok, D=D, m=mm, nseg=B,
                     seg_tok_off=off, seg_pos0=pos0, seg_out_row=rows, normalize=normalize,
                     norm_w=None, eps=EPS, rope_dim=R_, rope_base=BASE, out=out, out_fmt=fmt)
-    # the newest block's KV entry, its indexer key, and the newest token's window row
-    jobs = [job(W["kv_tok"], W["kv_gate"], B * m, D, m, W["seg_off"], W["seg_pos0"], W["seg_row"],
+    return [job(W["kv_tok"], W["kv_gate"], B * m, D, m, W["seg_off"], W["seg_pos0"], W["seg_row"],
                 1, R, W["kv"], csa.SPLIT),
             job(W["key_tok"], W["key_gate"], B * m, d_I, m, W["seg_off"], W["seg_pos0"],
                 W["seg_row"], 0, 0, W["keys"], csa.FP8),
             job(W["win_tok"], W["win_gate"], B, D, 1, W["win_seg_off"], W["win_pos0"], W["win_row"],
                 1, R, W["win"], csa.BF16)]
+
+
+def make_step(W, check=False, fused=True):
+    c, inp = W["c"], W["inp"]
+    B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
+    jobs = step_jobs(W)
 
     def k_compress():
         csa.csa_compress_batch(jobs, check=check)
@@ -551,27 +557,38 @@ def paged_replica(Wr, seed):
     return Wp
 
 
-def make_paged_step(Wp):
-    """The decode step over paged caches: csa_compress_batch (the new rows go
-    to their pool rows and window ring slots), indexer_score_paged,
-    topk_select, hybrid_attn_decode_paged."""
+def make_paged_step(Wp, fused=True):
+    """The decode step over paged caches: csa_compress_score_paged (the new
+    rows go to their pool rows and window ring slots; or, fused=False,
+    csa_compress_batch then indexer_score_paged), topk_select,
+    hybrid_attn_decode_paged."""
     c, inp = Wp["c"], Wp["inp"]
     B, m, D, R, d_I, H, k = Wp["B"], Wp["m"], Wp["D"], Wp["R"], Wp["d_I"], c["H"], c["k"]
     _, kern = make_step(Wp, check=False, fused=False)
     k_compress, k_topk = kern[0][1], kern[2][1]
     BR = PAGED_BLOCK_ROWS
+    jobs = step_jobs(Wp)
 
     def k_indexer():
         csa.indexer_score_paged(Wp["q_idx"], Wp["w"], B, c["H_I"], d_I, Wp["keys"], csa.FP8, Wp["pool_rows"],
                                 Wp["table"], Wp["bps"], BR, Wp["q_pos"], m, Wp["scores"], Wp["ld"], check=False)
+
+    def k_compress_score():
+        csa.csa_compress_score_paged(jobs, Wp["q_idx"], Wp["w"], B, c["H_I"], d_I, Wp["keys"], csa.FP8,
+                                     Wp["pool_rows"], Wp["table"], B, Wp["bps"], BR, None, Wp["q_pos"], m,
+                                     Wp["scores"], Wp["ld"], check=False)
 
     def k_attn():
         csa.hybrid_attn_decode_paged(Wp["q"], csa.BF16, B, H, D, Wp["q_pos"], None, EPS, R, BASE, Wp["kv"],
                                      csa.SPLIT, Wp["pool_rows"], Wp["table"], Wp["bps"], BR, m, Wp["idx"], k,
                                      Wp["win"], csa.BF16, inp.n_win, Wp["win_len"], Wp["sinks"], inp.scale,
                                      Wp["out"], csa.BF16, csa.VARIANT_AUTO, check=False, win_start=Wp["win_start"])
-    kernels = [("csa_compress_batch", k_compress), ("indexer_score_paged", k_indexer), ("topk_select", k_topk),
-               ("hybrid_attn_decode_paged", k_attn)]
+    if fused:
+        kernels = [("csa_compress_score_paged", k_compress_score), ("topk_select", k_topk),
+                   ("hybrid_attn_decode_paged", k_attn)]
+    else:
+        kernels = [("csa_compress_batch", k_compress), ("indexer_score_paged", k_indexer), ("topk_select", k_topk),
+                   ("hybrid_attn_decode_paged", k_attn)]
 
     def step():
         for _, f in kernels:
@@ -582,16 +599,20 @@ def make_paged_step(Wp):
 def paged_leg(reps, steps, warmup):
     """The headline step with its KV cache and index keys paged in 32-entry
     blocks and its window kept as a ring: ms per step and each kernel's
-    time."""
+    time, as three launches (compress + score in one) and as four."""
     pr = [paged_replica(Wr, 100 + j) for j, Wr in enumerate(reps)]
     made = [make_paged_step(Wp) for Wp in pr]
-    for st, _ in made:
+    made4 = [make_paged_step(Wp, fused=False) for Wp in pr]
+    for st, _ in made + made4:
         st()
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
+    ms4 = time_graph([m_[0] for m_ in made4], steps, warmup)
     us = kernel_periods([m_[1] for m_ in made], max(20, min(100, steps)))
+    us4 = kernel_periods([m_[1] for m_ in made4], max(20, min(100, steps)))
     out = {"block_rows": PAGED_BLOCK_ROWS, "window": "ring", "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
-           "kernels_us": {n: round(v, 2) for n, v in us.items()}}
+           "kernels_us": {n: round(v, 2) for n, v in us.items()},
+           "four_launches": {"ms_per_step": ms4, "kernels_us": {n: round(v, 2) for n, v in us4.items()}}}
     del pr, made
     torch.cuda.empty_cache()
     return out
