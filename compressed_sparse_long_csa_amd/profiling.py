@@ -121,7 +121,8 @@ def main(argv=None):
     for a in ("--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write", "--out"):
         t.add_argument(a, required=True)
     t.add_argument("--source", action="append", required=True)
-    t.add_argument("--copy-kernel", default="elementwise")
+    t.add_argument("--copy-kernel", default="MulFunctor",
+                   help="name part of the copy kernel (torch's multiply; its fill kernel must not match)")
     t.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy launch")
     c = sub.add_parser("counters")
     c.add_argument("--csv", required=True)

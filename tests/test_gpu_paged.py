@@ -74,7 +74,7 @@ def test_indexer_paged_long_rows_interleaved_shares():
                                         (64, 32, csa.MXFP4)])
 def test_indexer_paged_rows_matches_contiguous_bits(H_I, BR, fmt):
     """A prefill chunk of two sequences (1,102 queries: FP8 takes the
-    shared-key kernel, one four-query block straddling the two sequences)
+    shared-key kernel, one workgroup's query block straddling the two sequences)
     reads each sequence's keys through one shared block-table row
     (q_block_row) of a table with spare rows; the scores carry the bits of
     indexer_score over the same keys stored contiguously.  So do the same
