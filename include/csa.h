@@ -50,7 +50,10 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+/* 2: caller-owned top-k workspace (CSA_ERR_WORKSPACE), topk_select_noalloc.
+ * 3: hybrid_attn_prefill_paged, indexer_score_paged_rows,
+ *    csa_compress_score_paged, csa_debug_poison_lds (additions only). */
+#define CSA_ABI_VERSION 3
 
 typedef enum csa_status {
   CSA_OK = 0,

@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_status_strings_and_row_bytes(lib):
-    assert lib.csa_abi_version() >= 1
+    assert lib.csa_abi_version() == 3
     lib.csa_status_string.restype = ctypes.c_char_p
     for code, name in ((0, b"CSA_OK"), (1, b"CSA_ERR_INVALID_ARG"), (2, b"CSA_ERR_UNSUPPORTED"),
                        (3, b"CSA_ERR_HIP"), (4, b"CSA_ERR_WORKSPACE")):

@@ -112,6 +112,15 @@ def test_indexer_paged_rows_matches_contiguous_bits(H_I, BR, fmt):
                                      BR, None, q_pos_d, m, per_q, ld)
         torch.cuda.synchronize()
         assert torch.equal(ref.view(torch.int32), per_q.view(torch.int32)), "a table row per query: bits differ"
+    # rows outside the table are clamped into it: A in row 0 and B in the
+    # last row, named by -3 and 99 (the host check is bypassed)
+    table_c = table[[1, 0, 2, 3]]
+    q_row_c = np.array([-3] * nq_a + [99] * nq_b, np.int32)
+    clamped = torch.full((nq, ld), -7.0, dtype=torch.float32, device=DEV)
+    csa.indexer_score_paged_rows(q_idx, w, nq, H_I, d_I, pool_d, fmt, pool_rows, dev(table_c), 4, bps, BR,
+                                 dev(q_row_c), q_pos_d, m, clamped, ld, check=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), clamped.view(torch.int32)), "clamped table rows: bits differ"
     picks = np.array([0, 1, 2, 4, 7, 350, 699, 700, 701, 702, 1100, 1101])
     pk = torch.as_tensor(picks, device=DEV)
     small = torch.full((len(picks), ld), -7.0, dtype=torch.float32, device=DEV)

@@ -153,6 +153,8 @@ def test_prefill_paged_matches_contiguous_bits(m, k, BR):
              tok_pos0=dev(tok_pos0), sinks=dev(sinks), idx=dev(sel) if k else None)
     pool_d, table_d, q_row_d = dev(pool), dev(table), dev(q_row)
     per_q = dev(table[q_row])                            # one table row per query
+    table_c = dev(table[[1, 0, 2, 3]])
+    q_row_c = dev(np.array([-3] * na + [99] * nb, np.int32))
     for v in (csa.VARIANT_AUTO, csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
         ref = gpu_bytes(nq * H * tb)
         csa.hybrid_attn_prefill(g["q"], csa.BF16, nq, H, D, g["q_pos"], None, EPS, R, ROPE_BASE, g["kv"], csa.SPLIT,
@@ -168,7 +170,14 @@ def test_prefill_paged_matches_contiguous_bits(m, k, BR):
                                       csa.SPLIT, pool.shape[0], per_q, nq, bps, BR, None, m, g["idx"], k,
                                       g["tok"], csa.BF16, g["tok_off"], g["tok_pos0"], N_WIN, g["sinks"], scale,
                                       got2, csa.BF16, v)
+        # rows outside the table clamp into it: A's row first, B's last (host check bypassed)
+        got3 = gpu_bytes(nq * H * tb)
+        csa.hybrid_attn_prefill_paged(g["q"], csa.BF16, nq, H, D, g["q_pos"], None, EPS, R, ROPE_BASE, pool_d,
+                                      csa.SPLIT, pool.shape[0], table_c, 4, bps, BR, q_row_c, m, g["idx"], k,
+                                      g["tok"], csa.BF16, g["tok_off"], g["tok_pos0"], N_WIN, g["sinks"], scale,
+                                      got3, csa.BF16, v, check=False)
         torch.cuda.synchronize()
+        assert torch.equal(ref, got3), f"variant {v}: clamped table rows differ"
         assert torch.equal(ref, got), f"variant {v}: paged prefill (shared table rows) differs from contiguous"
         assert torch.equal(ref, got2), f"variant {v}: paged prefill (a table row per query) differs"
     # the first query of each sequence against the oracle, from the pool through the table
