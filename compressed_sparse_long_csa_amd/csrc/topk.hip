@@ -496,8 +496,12 @@ __global__ void __launch_bounds__(kThreads) topk_slice_kernel(TopkArgs a, int P,
                                                               int32_t* cidx, float* cscore) {
   __shared__ TopkSmem sm;
   extern __shared__ float vals[];
-  const int row = blockIdx.x / P;
-  const uint32_t p = blockIdx.x % P;
+  // slice-major: slice 0 of every row, then slice 1 of every row, ...  In a
+  // ragged batch the slices past a short row's end are empty; this order
+  // dispatches the slices that hold scores first and leaves the empty ones
+  // (which return at once) to trail, instead of interleaving them
+  const int row = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.nq));
+  const uint32_t p = blockIdx.x / static_cast<uint32_t>(a.nq);
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t n = row_len(a, row);
   const uint32_t s0 = p * Cs;
