@@ -5,8 +5,8 @@ include/csa.h); this package is its ctypes binding plus the seeded synthetic
 input generator (synth).  Build the library with
 `python -m compressed_sparse_long_csa_amd.build`.
 """
-from .binding import (BF16, F32, FP8, MXFP4, SPLIT, VARIANT_AUTO, VARIANT_HIGH_OCC,  # noqa: F401
-                      VARIANT_LOW_OCC, CsaError, csa_compress, csa_compress_batch, csa_compress_score,
+from .binding import (BF16, F32, FP8, MXFP4, SPLIT, VARIANT_AUTO, VARIANT_FULL_DIMS,  # noqa: F401
+                      VARIANT_HIGH_OCC, VARIANT_LOW_OCC, CsaError, csa_compress, csa_compress_batch, csa_compress_score,
                       csa_compress_score_paged,
                       debug_poison_lds,
                       hybrid_attn_decode, hybrid_attn_decode_paged,

@@ -14,7 +14,7 @@ import os
 import torch
 
 F32, BF16, FP8, MXFP4, SPLIT = 0, 1, 2, 3, 4
-VARIANT_AUTO, VARIANT_HIGH_OCC, VARIANT_LOW_OCC = 0, 1, 2
+VARIANT_AUTO, VARIANT_HIGH_OCC, VARIANT_LOW_OCC, VARIANT_FULL_DIMS = 0, 1, 2, 3
 _STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_HIP",
            4: "CSA_ERR_WORKSPACE"}
 

@@ -679,8 +679,8 @@ __device__ __forceinline__ void entry_loop(const Work& w, WaveSmem& ws, const QO
   }
 }
 
-// DVS = number of workgroups sharing one (query, 16-head tile): each owns
-// 512 / DVS output dims; every wave of it accumulates all of them over its
+// DVS = number of workgroups sharing one (query, 16-head tile) (1, 2 or 4):
+// each owns 512 / DVS output dims; every wave of it accumulates all of them over its
 // own entries, and the four partial states are merged at the end in wave
 // order.
 // PG: the instance for paged caches (block table, ring window); the other
@@ -1013,12 +1013,20 @@ attn_mfma_kernel(AttnArgs a, int n_units, int n_pad) {
 
 }  // namespace
 
-// HIGH_OCC: two workgroups per (query, 16 heads), 256 output dims each;
-// LOW_OCC: four, 128 dims each; AUTO fills the chip: the fewest workgroups
-// that still give every CU one.
-int pick_dvs(int variant, int units, int cus) {
+// FULL_DIMS: one workgroup per (query, 16 heads), all 512 output dims;
+// HIGH_OCC: two, 256 dims each; LOW_OCC: four, 128 dims each.  AUTO: the
+// fewest workgroups that still give every CU one (every workgroup of a head
+// tile computes the tile's logits, so fewer workgroups repeat less of that
+// work and pay fewer prologues) -- but one per tile only when the queries'
+// row counts are bounded (a selected list: at most k + n_win rows) or the
+// batch has four tiles per CU: with all-entry lists of very different
+// lengths the longest query's workgroups set the time, and splitting its
+// output dims over two workgroups halves their P.V work.
+int pick_dvs(int variant, int units, int cus, bool bounded_rows) {
+  if (variant == CSA_VARIANT_FULL_DIMS) return 1;
   if (variant == CSA_VARIANT_HIGH_OCC) return 2;
   if (variant == CSA_VARIANT_LOW_OCC) return 4;
+  if (units >= cus && (bounded_rows || units >= 4 * cus)) return 1;
   if (units * 2 >= cus) return 2;
   return 4;
 }
@@ -1041,14 +1049,14 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   }
   const int base_units = a.nq * (a.H / 16);
   const int variant = env_variant(a.variant);
-  const int dvs = pick_dvs(variant, base_units, device_cu_count());
+  const int dvs = pick_dvs(variant, base_units, device_cu_count(), a.idx != nullptr);
   const int units = base_units * dvs;
   const int n_pad = (units + 7) / 8 * 8;
   const size_t shm = sizeof(AttnSmem);
   log_launch("attention: MFMA path%s, %d queries x %d heads, variant %s (%s), %d output-dim slices, "
              "grid %d x 256 threads (%d padding), LDS %zu B",
              a.blk_table != nullptr ? " (paged)" : "", a.nq, a.H,
-             dvs == 2 ? "HIGH_OCC" : "LOW_OCC",
+             dvs == 1 ? "FULL_DIMS" : (dvs == 2 ? "HIGH_OCC" : "LOW_OCC"),
              a.variant != CSA_VARIANT_AUTO ? "requested" : (variant != CSA_VARIANT_AUTO ? "CSA_VARIANT" : "auto"),
              dvs, n_pad,
              n_pad - units, shm);
@@ -1057,7 +1065,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (attr_set_dev != dev) {
-    const void* fns[] = {reinterpret_cast<const void*>(&attn_mfma_kernel<2, false>),
+    const void* fns[] = {reinterpret_cast<const void*>(&attn_mfma_kernel<1, false>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<1, true>),
+                         reinterpret_cast<const void*>(&attn_mfma_kernel<2, false>),
                          reinterpret_cast<const void*>(&attn_mfma_kernel<4, false>),
                          reinterpret_cast<const void*>(&attn_mfma_kernel<2, true>),
                          reinterpret_cast<const void*>(&attn_mfma_kernel<4, true>)};
@@ -1070,11 +1080,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const dim3 g(n_pad), blk(kThreads);
   if (a.blk_table != nullptr) {
     switch (dvs) {
+      case 1: hipLaunchKernelGGL((attn_mfma_kernel<1, true>), g, blk, shm, stream, a, units, n_pad); break;
       case 2: hipLaunchKernelGGL((attn_mfma_kernel<2, true>), g, blk, shm, stream, a, units, n_pad); break;
       default: hipLaunchKernelGGL((attn_mfma_kernel<4, true>), g, blk, shm, stream, a, units, n_pad); break;
     }
   } else {
     switch (dvs) {
+      case 1: hipLaunchKernelGGL((attn_mfma_kernel<1, false>), g, blk, shm, stream, a, units, n_pad); break;
       case 2: hipLaunchKernelGGL((attn_mfma_kernel<2, false>), g, blk, shm, stream, a, units, n_pad); break;
       default: hipLaunchKernelGGL((attn_mfma_kernel<4, false>), g, blk, shm, stream, a, units, n_pad); break;
     }

@@ -50,6 +50,7 @@ int env_variant(int requested) {
     if (v == nullptr) return static_cast<int>(CSA_VARIANT_AUTO);
     if (strcmp(v, "high") == 0) return static_cast<int>(CSA_VARIANT_HIGH_OCC);
     if (strcmp(v, "low") == 0) return static_cast<int>(CSA_VARIANT_LOW_OCC);
+    if (strcmp(v, "full") == 0) return static_cast<int>(CSA_VARIANT_FULL_DIMS);
     return static_cast<int>(CSA_VARIANT_AUTO);
   }();
   return requested == CSA_VARIANT_AUTO ? forced : requested;
@@ -466,7 +467,7 @@ static csa_status attn_common(const char* name, AttnArgs& a, hipStream_t stream)
   if (a.rope_dim > 0 && !(a.rope_base > 0.0f))
     return fail(CSA_ERR_INVALID_ARG, "%s: rope_base must be > 0", name);
   if (!(a.eps >= 0.0f)) return fail(CSA_ERR_INVALID_ARG, "%s: eps must be >= 0", name);
-  if (a.variant < CSA_VARIANT_AUTO || a.variant > CSA_VARIANT_LOW_OCC)
+  if (a.variant < CSA_VARIANT_AUTO || a.variant > CSA_VARIANT_FULL_DIMS)
     return fail(CSA_ERR_INVALID_ARG, "%s: bad variant", name);
   if (!fmt_ok(a.q_fmt) || !fmt_ok(a.kv_fmt) || !fmt_ok(a.win_fmt) || !fmt_ok(a.out_fmt))
     return fail(CSA_ERR_INVALID_ARG, "%s: bad format", name);

@@ -104,7 +104,7 @@ int device_cu_count();
 
 // Diagnostics from the environment, read once per process.  CSA_LOG >= 1:
 // every error message, and each launch's kernel choice and grid, go to
-// stderr.  CSA_VARIANT = high | low: calls that pass CSA_VARIANT_AUTO take
+// stderr.  CSA_VARIANT = high | low | full: calls that pass CSA_VARIANT_AUTO take
 // that variant instead (explicit variants are kept).
 int env_log_level();
 int env_variant(int requested);

@@ -52,7 +52,8 @@ extern "C" {
 
 /* 2: caller-owned top-k workspace (CSA_ERR_WORKSPACE), topk_select_noalloc.
  * 3: hybrid_attn_prefill_paged, indexer_score_paged_rows,
- *    csa_compress_score_paged, csa_debug_poison_lds (additions only). */
+ *    csa_compress_score_paged, csa_debug_poison_lds, CSA_VARIANT_FULL_DIMS
+ *    (additions only). */
 #define CSA_ABI_VERSION 3
 
 typedef enum csa_status {
@@ -72,11 +73,17 @@ typedef enum csa_fmt {
 } csa_fmt;
 
 typedef enum csa_variant {
-  CSA_VARIANT_AUTO = 0,     /* the fewest workgroups per (query, 16 heads) -- 2
-                               or 4 -- that still give every CU one */
+  CSA_VARIANT_AUTO = 0,     /* the fewest workgroups per (query, 16 heads) --
+                               1, 2 or 4 -- that still give every CU one (1
+                               only with a selected list, or with at least
+                               four (query, 16 heads) per CU) */
   CSA_VARIANT_HIGH_OCC = 1, /* two workgroups per (query, 16 heads), 256 output
                                dims each: for a batch that fills the GPU */
-  CSA_VARIANT_LOW_OCC = 2   /* four, 128 output dims each: for a small batch.
+  CSA_VARIANT_LOW_OCC = 2,  /* four, 128 output dims each: for a small batch */
+  CSA_VARIANT_FULL_DIMS = 3 /* one workgroup per (query, 16 heads), all 512
+                               output dims: for a batch with at least one
+                               (query, 16 heads) per CU (prefill chunks, wide
+                               ragged batches).
                                All variants give the same bits (the fp32 path
                                has one kernel and ignores the variant). */
 } csa_variant;

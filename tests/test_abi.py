@@ -175,6 +175,7 @@ def test_attention_argument_errors(lib):
     assert call(H=40) == UNSUPPORTED                 # heads in tiles of 16
     assert call(q_fmt=csa.F32, kv_fmt=csa.F32, win_fmt=csa.F32, out_fmt=csa.F32, D=640) == UNSUPPORTED
     assert call(variant=7) == INVALID
+    assert call(variant=4) == INVALID                # AUTO, HIGH_OCC, LOW_OCC, FULL_DIMS are 0..3
     assert call(q=None) == INVALID
     assert "hybrid_attn_decode" in _last_error(lib)
 

@@ -125,10 +125,10 @@ def test_ragged_csa_hca_b64_ctx1k_1m():
         for _ in range(3):
             perm = rng.permutation(d["B"])
             assert np.array_equal(_attend(d, idx, perm), base[perm]), f"{layer}: permutation changed bits"
-        for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+        for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
             assert np.array_equal(_attend(d, idx, variant=v), base), f"{layer}: variant {v} changed bits"
         for b in picks:
-            for v in (csa.VARIANT_AUTO, csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+            for v in (csa.VARIANT_AUTO, csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
                 assert np.array_equal(_attend(d, idx, [b], v)[0], base[b]), \
                     f"{layer}: sequence {b} alone (variant {v}) changed bits"
         del d

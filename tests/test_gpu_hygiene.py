@@ -5,7 +5,8 @@ after the LDS of every CU has been filled with a 32-bit pattern
 (csa_debug_poison_lds), and the top-k's caller workspace is filled with byte
 patterns before its two-pass rows; every result must carry the bits of the
 run after a zero fill.  Also the environment switches: CSA_VARIANT forces a
-variant on calls that pass AUTO (the same bits, by invariance) and CSA_LOG=1
+variant (high, low, full) on calls that pass AUTO (the same bits, by
+invariance) and CSA_LOG=1
 names each launch's choice on stderr."""
 import os
 import subprocess
@@ -98,7 +99,7 @@ def test_decode_attention_ignores_stale_lds(cfg, lengths, csa_mode):
     b = upload_decode(inp)
     sel = dev(synth.random_selection(np.random.default_rng(906), inp.n_ent, inp.k)) if csa_mode else None
     out_fmt = csa.F32 if inp.q_fmt == csa.F32 else csa.BF16
-    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
         def run():
             out = gpu_bytes(inp.B * inp.H * csa.row_bytes(out_fmt, inp.D))
             csa.hybrid_attn_decode(b["q"], inp.q_fmt, inp.B, inp.H, inp.D, b["q_pos"], None, EPS, inp.R,
@@ -170,6 +171,9 @@ def test_variant_and_log_from_the_environment():
     forced, log = _child({"CSA_LOG": "1", "CSA_VARIANT": "low"}, csa.VARIANT_AUTO)
     assert forced == base, "a forced variant changed the bits"
     assert "variant LOW_OCC (CSA_VARIANT)" in log, log[-2000:]
+    full, log3 = _child({"CSA_LOG": "1", "CSA_VARIANT": "full"}, csa.VARIANT_AUTO)
+    assert full == base, "the FULL_DIMS variant changed the bits"
+    assert "variant FULL_DIMS (CSA_VARIANT)" in log3, log3[-2000:]
     kept, log2 = _child({"CSA_LOG": "1", "CSA_VARIANT": "low"}, csa.VARIANT_HIGH_OCC)
     assert kept == base
     assert "variant HIGH_OCC (requested)" in log2, log2[-2000:]

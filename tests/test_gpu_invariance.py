@@ -51,7 +51,7 @@ def test_attention_bits_independent_of_batch_and_variant(cfg, lengths, csa_mode)
     sel_t = dev(sel) if sel is not None else None
     B = inp.B
     base = _attn(inp, bufs, sel_t, list(range(B)), csa.VARIANT_AUTO)
-    variants = [csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC]
+    variants = [csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS]
     for v in variants:
         got = _attn(inp, bufs, sel_t, list(range(B)), v)
         assert np.array_equal(got, base), f"variant {v} changed the bits"

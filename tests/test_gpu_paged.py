@@ -174,7 +174,7 @@ def _attn_pair(inp, sel, BR, seed, variant, ring=False, hca=False):
 
 @pytest.mark.parametrize("BR,k,variant", [(32, 512, csa.VARIANT_AUTO), (1, 512, csa.VARIANT_LOW_OCC),
                                           (128, 1024, csa.VARIANT_HIGH_OCC), (32, 64, csa.VARIANT_AUTO),
-                                          (32, 2048, csa.VARIANT_AUTO)])
+                                          (32, 2048, csa.VARIANT_AUTO), (32, 512, csa.VARIANT_FULL_DIMS)])
 def test_attention_paged_matches_contiguous_bits(BR, k, variant):
     lengths = [65536, 9001, 2052, 130, 5, 3, 40000]
     inp = synth.decode_inputs(620 + BR, lengths, m=4, H=64, D=512, R=64, k=k)
@@ -183,7 +183,8 @@ def test_attention_paged_matches_contiguous_bits(BR, k, variant):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("BR,variant", [(1, csa.VARIANT_AUTO), (4, csa.VARIANT_LOW_OCC), (16, csa.VARIANT_AUTO)])
+@pytest.mark.parametrize("BR,variant", [(1, csa.VARIANT_AUTO), (4, csa.VARIANT_LOW_OCC), (16, csa.VARIANT_AUTO),
+                                        (2, csa.VARIANT_FULL_DIMS)])
 def test_hca_attention_paged_matches_contiguous_bits(BR, variant):
     """HCA (every visible entry attended; one entry per 128-token block at
     block_rows = 1), with lists past 1024 positions mapped inside the loop."""
@@ -193,7 +194,7 @@ def test_hca_attention_paged_matches_contiguous_bits(BR, variant):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("variant", [csa.VARIANT_AUTO, csa.VARIANT_LOW_OCC])
+@pytest.mark.parametrize("variant", [csa.VARIANT_AUTO, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS])
 def test_attention_window_ring_matches_rows_in_order(variant):
     """The request's window kept as a ring (random start, random bytes in the
     free slots) gives the bits of the window stored in order."""

@@ -512,7 +512,7 @@ def test_attn_decode_head_counts(H, csa_mode, k):
         s = sel[b][sel[b] >= 0] if sel is not None else None
         assert_lowp_close(got[b], oracle_decode_query(inp, b, s), what=f"H={H} b{b}")
     base = out.cpu().numpy()
-    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
         o2, _ = run_decode(inp, idx_t, v, bufs)
         assert np.array_equal(o2.cpu().numpy(), base), f"H={H}: variant {v} changed the bits"
 

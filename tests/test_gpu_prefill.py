@@ -76,7 +76,7 @@ def test_prefill_bits_match_decode_and_variants():
     c = _case(5, 3000, 64, 64, 4, 512)
     nq, H = c["chunk"], c["H"]
     base, bufs = _prefill(c, csa.VARIANT_AUTO)
-    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+    for v in (csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
         got, _ = _prefill(c, v, bufs)
         assert np.array_equal(got, base), f"variant {v} changed the bits"
     # decode of the same tokens, with their window rows copied out of the run
@@ -155,7 +155,7 @@ def test_prefill_paged_matches_contiguous_bits(m, k, BR):
     per_q = dev(table[q_row])                            # one table row per query
     table_c = dev(table[[1, 0, 2, 3]])
     q_row_c = dev(np.array([-3] * na + [99] * nb, np.int32))
-    for v in (csa.VARIANT_AUTO, csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC):
+    for v in (csa.VARIANT_AUTO, csa.VARIANT_HIGH_OCC, csa.VARIANT_LOW_OCC, csa.VARIANT_FULL_DIMS):
         ref = gpu_bytes(nq * H * tb)
         csa.hybrid_attn_prefill(g["q"], csa.BF16, nq, H, D, g["q_pos"], None, EPS, R, ROPE_BASE, g["kv"], csa.SPLIT,
                                 g["kv_off"], m, g["idx"], k, g["tok"], csa.BF16, g["tok_off"], g["tok_pos0"], N_WIN,
