@@ -10,7 +10,9 @@ path, every kernel from libcsa, in three launches:
                       the new keys scored by the workgroups that write them
   2. topk_select   -- the k best entries, ascending
   3. hybrid_attn_decode -- sink MQA over the selected entries + window
-`four_launches` times the same step with csa_compress_batch and
+`two_launches_topk_fused` times the same step with the top-k selected inside
+the first launch (csa_compress_score_topk: the last workgroup to finish a
+query's scores selects them), `four_launches` with csa_compress_batch and
 indexer_score as two launches.
 Inputs are seeded synthetic tensors already resident in HBM.  The per-layer
 state a step reads (KV cache, index keys, window rows) exists in R copies
@@ -166,10 +168,21 @@ def step_jobs(W):
                 1, R, W["win"], csa.BF16)]
 
 
-def make_step(W, check=False, fused=True):
+def make_step(W, check=False, fused=True, topk_fused=False):
+    """The decode step's launches.  fused (the default): csa_compress_score,
+    topk_select, hybrid_attn_decode; with topk_fused: csa_compress_score_topk,
+    hybrid_attn_decode (two launches); not fused: csa_compress_batch,
+    indexer_score, topk_select, hybrid_attn_decode."""
     c, inp = W["c"], W["inp"]
     B, m, D, R, d_I, H, k = W["B"], W["m"], W["D"], W["R"], W["d_I"], c["H"], c["k"]
     jobs = step_jobs(W)
+    if topk_fused and "tk_ws" not in W:
+        W["tk_ws"] = torch.zeros(csa.score_topk_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+
+    def k_compress_score_topk():
+        csa.csa_compress_score_topk(jobs, W["q_idx"], W["w"], B, c["H_I"], d_I, W["keys"], csa.FP8, W["kv_off"],
+                                    W["q_pos"], m, W["scores"], W["ld"], k, W["idx"], workspace=W["tk_ws"],
+                                    check=check)
 
     def k_compress():
         csa.csa_compress_batch(jobs, check=check)
@@ -191,7 +204,9 @@ def make_step(W, check=False, fused=True):
                                inp.n_win, W["win_len"], W["sinks"], inp.scale, W["out"], csa.BF16,
                                csa.VARIANT_AUTO, check=check)
 
-    if fused:
+    if fused and topk_fused:
+        kernels = [("csa_compress_score_topk", k_compress_score_topk), ("hybrid_attn_decode", k_attn)]
+    elif fused:
         kernels = [("csa_compress_score", k_compress_score), ("topk_select", k_topk),
                    ("hybrid_attn_decode", k_attn)]
     else:
@@ -222,6 +237,7 @@ def algorithmic_bytes(W):
         + B * k * 4 + B * H * D * 2 * 2 + H * 4,
     }
     per_kernel["csa_compress_score"] = per_kernel["csa_compress_batch"] + per_kernel["indexer_score"]
+    per_kernel["csa_compress_score_topk"] = per_kernel["csa_compress_score"] + B * k * 4
     # the indexer's inputs alone (every visible key, the index query and head
     # weights of each query): the step byte model's share of the launch, with
     # the score writes (scratch) and the compress jobs left out
@@ -237,7 +253,7 @@ def algorithmic_flops(W):
     N = inp.n_ent.astype(np.int64)
     sel = np.minimum(c["k"], N) + inp.win_len.astype(np.int64)
     idx = int(2 * N.sum() * c["H_I"] * W["d_I"])
-    return {"indexer_score": idx, "csa_compress_score": idx,
+    return {"indexer_score": idx, "csa_compress_score": idx, "csa_compress_score_topk": idx,
             "hybrid_attn_decode": int(2 * 2 * sel.sum() * c["H"] * W["D"])}
 
 
@@ -485,19 +501,26 @@ def context_scan(contexts, steps, warmup):
         # twice the 256 MB last-level cache
         n_rep = max(1, -(-600_000_000 // step_bytes))
         reps = make_replicas(W, n_rep)
-        made = [make_step(Wr, check=False) for Wr in reps]
-        for st, _ in made:
+        made3 = [make_step(Wr, check=False) for Wr in reps]
+        made = [make_step(Wr, check=False, topk_fused=True) for Wr in reps]
+        for st, _ in made + made3:
             st()
         torch.cuda.synchronize()
         ms = time_graph([m[0] for m in made], steps, warmup)
+        ms3 = time_graph([m[0] for m in made3], steps, warmup)
         per_us = kernel_periods([m[1] for m in made], max(20, min(60, steps)))
-        idx_gbps = kbytes["csa_compress_score"] / (per_us["csa_compress_score"] * 1e-6) / 1e9
-        rows.append({"context": L, "ms_per_step": ms, "query_tokens_per_s": W["B"] / (ms * 1e-3),
-                     "step_hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
-                     "kernels_us": {n: round(v, 2) for n, v in per_us.items()},
+        per_us3 = kernel_periods([m[1] for m in made3], max(20, min(60, steps)))
+        idx_gbps = kbytes["indexer_inputs"] / (per_us3["csa_compress_score"] * 1e-6) / 1e9
+        best = min(ms, ms3)
+        rows.append({"context": L, "ms_per_step": best, "query_tokens_per_s": W["B"] / (best * 1e-3),
+                     "form": "two launches (top-k fused)" if ms <= ms3 else "three launches",
+                     "step_hbm_gbps_algorithmic": step_bytes / (best * 1e-3) / 1e9,
+                     "two_launches": {"ms_per_step": ms, "kernels_us": {n: round(v, 2) for n, v in per_us.items()}},
+                     "three_launches": {"ms_per_step": ms3,
+                                        "kernels_us": {n: round(v, 2) for n, v in per_us3.items()}},
                      "compress_score_gbps": idx_gbps, "compress_score_hbm_frac": idx_gbps / HBM_PEAK_GBPS,
                      "state_replicas": n_rep})
-        del W, reps, made
+        del W, reps, made, made3
         torch.cuda.empty_cache()
     return rows
 
@@ -557,7 +580,7 @@ def paged_replica(Wr, seed):
     return Wp
 
 
-def make_paged_step(Wp, fused=True):
+def make_paged_step(Wp, fused=True, topk_fused=False):
     """The decode step over paged caches: csa_compress_score_paged (the new
     rows go to their pool rows and window ring slots; or, fused=False,
     csa_compress_batch then indexer_score_paged), topk_select,
@@ -583,7 +606,16 @@ def make_paged_step(Wp, fused=True):
                                      csa.SPLIT, Wp["pool_rows"], Wp["table"], Wp["bps"], BR, m, Wp["idx"], k,
                                      Wp["win"], csa.BF16, inp.n_win, Wp["win_len"], Wp["sinks"], inp.scale,
                                      Wp["out"], csa.BF16, csa.VARIANT_AUTO, check=False, win_start=Wp["win_start"])
-    if fused:
+    if topk_fused and "tk_ws" not in Wp:
+        Wp["tk_ws"] = torch.zeros(csa.score_topk_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+
+    def k_compress_score_topk():
+        csa.csa_compress_score_topk_paged(jobs, Wp["q_idx"], Wp["w"], B, c["H_I"], d_I, Wp["keys"], csa.FP8,
+                                          Wp["pool_rows"], Wp["table"], B, Wp["bps"], BR, None, Wp["q_pos"], m,
+                                          Wp["scores"], Wp["ld"], k, Wp["idx"], workspace=Wp["tk_ws"], check=False)
+    if fused and topk_fused:
+        kernels = [("csa_compress_score_topk_paged", k_compress_score_topk), ("hybrid_attn_decode_paged", k_attn)]
+    elif fused:
         kernels = [("csa_compress_score_paged", k_compress_score), ("topk_select", k_topk),
                    ("hybrid_attn_decode_paged", k_attn)]
     else:
@@ -602,18 +634,22 @@ def paged_leg(reps, steps, warmup):
     time, as three launches (compress + score in one) and as four."""
     pr = [paged_replica(Wr, 100 + j) for j, Wr in enumerate(reps)]
     made = [make_paged_step(Wp) for Wp in pr]
+    made3 = [make_paged_step(Wp, topk_fused=True) for Wp in pr]
     made4 = [make_paged_step(Wp, fused=False) for Wp in pr]
-    for st, _ in made + made4:
+    for st, _ in made + made3 + made4:
         st()
     torch.cuda.synchronize()
     ms = time_graph([m_[0] for m_ in made], steps, warmup)
+    ms3 = time_graph([m_[0] for m_ in made3], steps, warmup)
     ms4 = time_graph([m_[0] for m_ in made4], steps, warmup)
     us = kernel_periods([m_[1] for m_ in made], max(20, min(100, steps)))
+    us3 = kernel_periods([m_[1] for m_ in made3], max(20, min(100, steps)))
     us4 = kernel_periods([m_[1] for m_ in made4], max(20, min(100, steps)))
     out = {"block_rows": PAGED_BLOCK_ROWS, "window": "ring", "ms_per_step": ms, "query_tokens_per_s": pr[0]["B"] / (ms * 1e-3),
            "kernels_us": {n: round(v, 2) for n, v in us.items()},
+           "two_launches_topk_fused": {"ms_per_step": ms3, "kernels_us": {n: round(v, 2) for n, v in us3.items()}},
            "four_launches": {"ms_per_step": ms4, "kernels_us": {n: round(v, 2) for n, v in us4.items()}}}
-    del pr, made
+    del pr, made, made3, made4
     torch.cuda.empty_cache()
     return out
 
@@ -999,7 +1035,11 @@ def main():
     batch_us = {}
     event_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)), batch_us)
     per_us = batch_us
-    # the same step as four launches (compress, then the indexer), for comparison
+    # the same step as two launches (the top-k selected inside the compress +
+    # score launch) and as four (compress, then the indexer), for comparison
+    made3 = [make_step(Wr, check=False, fused=True, topk_fused=True) for Wr in reps]
+    ms3 = time_graph([m[0] for m in made3], args.steps, args.warmup)
+    per_us3 = kernel_periods([m[1] for m in made3], max(20, min(100, args.steps)))
     made4 = [make_step(Wr, check=False, fused=False) for Wr in reps]
     ms4 = time_graph([m[0] for m in made4], args.steps, args.warmup)
     per_us4 = kernel_periods([m[1] for m in made4], max(20, min(100, args.steps)))
@@ -1053,6 +1093,8 @@ def main():
                                "plus dispatch gap)"},
         "hbm_frac_step": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernels": kern,
+        "two_launches_topk_fused": {"ms_per_step": ms3, "query_tokens_per_s": B / (ms3 * 1e-3),
+                                    "kernels": table(per_us3)},
         "four_launches": {"ms_per_step": ms4, "query_tokens_per_s": B / (ms4 * 1e-3),
                           "kernels": table(per_us4)},
         "event_pair_floor_us": event_floor_us,

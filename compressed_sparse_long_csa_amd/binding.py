@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
-           "csa_compress", "csa_compress_batch", "csa_compress_score", "csa_compress_score_paged", "indexer_score",
+           "csa_compress", "csa_compress_batch", "csa_compress_score", "csa_compress_score_paged",
+           "csa_compress_score_topk", "csa_compress_score_topk_paged", "csa_score_topk_workspace_bytes", "indexer_score",
            "indexer_score_paged", "indexer_score_paged_rows", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
            "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged",
@@ -63,6 +64,14 @@ def load_library():
     lib.csa_compress_score_paged.restype = I
     lib.csa_compress_score_paged.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, I64, P, I64, I64, I,
                                              P, P, I, P, I64, P]
+    lib.csa_compress_score_topk.restype = I
+    lib.csa_compress_score_topk.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, P, P, I, P,
+                                            I64, I, P, P, U, P]
+    lib.csa_compress_score_topk_paged.restype = I
+    lib.csa_compress_score_topk_paged.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, I64, P, I64,
+                                                  I64, I, P, P, I, P, I64, I, P, P, U, P]
+    lib.csa_score_topk_workspace_bytes.restype = U
+    lib.csa_score_topk_workspace_bytes.argtypes = [I]
     lib.indexer_score_paged.restype = I
     lib.indexer_score_paged.argtypes = [P, P, I, I, I, P, I, I64, P, I64, I, P, I, P, I64, P]
     lib.indexer_score_paged_rows.restype = I
@@ -233,6 +242,54 @@ def csa_compress_score_paged(jobs, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, 
     _check(lib.csa_compress_score_paged(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool),
                                         fmt, pool_rows, _ptr(block_table), table_rows, blocks_per_seq, block_rows,
                                         _ptr(q_block_row), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
+
+
+def score_topk_workspace_bytes(nq):
+    """Device bytes of zeroed workspace csa_compress_score_topk needs for nq queries."""
+    return int(load_library().csa_score_topk_workspace_bytes(nq))
+
+
+def _score_topk_ws(workspace, nq, k, idx, device):
+    _need(idx, "idx", torch.int32, min_numel=nq * k)
+    if workspace is None:                  # a fresh zeroed workspace for this call
+        workspace = torch.zeros(max(1, score_topk_workspace_bytes(nq)), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def csa_compress_score_topk(jobs, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, k, idx,
+                            workspace=None, stream=None, check=True):
+    """csa_compress_score(...) then topk_select(scores, ...) in one launch.  workspace:
+    a uint8 device tensor of score_topk_workspace_bytes(nq) bytes, zero before its first
+    use (the call leaves it zero); None takes a fresh zeroed one for this call."""
+    lib = load_library()
+    arr = _job_array(jobs, check)
+    _indexer_checks(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, check)
+    workspace, ws_bytes = _score_topk_ws(workspace, nq, k, idx, scores.device)
+    _check(lib.csa_compress_score_topk(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(keys), fmt,
+                                       _ptr(key_off), _ptr(q_pos), m, _ptr(scores), ld, k, _ptr(idx),
+                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def csa_compress_score_topk_paged(jobs, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table,
+                                  table_rows, blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, k, idx,
+                                  workspace=None, stream=None, check=True):
+    """csa_compress_score_paged(...) then topk_select(scores, ...) in one launch."""
+    lib = load_library()
+    arr = _job_array(jobs, check)
+    rb = row_bytes(fmt, d_idx)
+    _need(q_idx, "q_idx", min_bytes=nq * n_heads * rb)
+    _need(w, "w", torch.float32, min_numel=nq * n_heads)
+    _need(q_pos, "q_pos", torch.int64, min_numel=nq)
+    _need(scores, "scores", torch.float32, min_numel=nq * ld)
+    _paged_checks(block_table, nq, blocks_per_seq, block_rows, key_pool, pool_rows, rb, q_pos, m, ld, check,
+                  table_rows=table_rows, q_block_row=q_block_row)
+    workspace, ws_bytes = _score_topk_ws(workspace, nq, k, idx, scores.device)
+    _check(lib.csa_compress_score_topk_paged(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx,
+                                             _ptr(key_pool), fmt, pool_rows, _ptr(block_table), table_rows,
+                                             blocks_per_seq, block_rows, _ptr(q_block_row), _ptr(q_pos), m,
+                                             _ptr(scores), ld, k, _ptr(idx), _ptr(workspace), ws_bytes,
+                                             _stream(stream)))
 
 
 def indexer_score(q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libcsa.so")
-SOURCES = ["csa_abi.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip"]
+SOURCES = ["csa_abi.hip", "compress.hip", "indexer.hip", "score_topk.hip", "topk.hip", "attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
@@ -29,6 +29,7 @@ FLAGS = [
 # accumulators are rescaled by VALU, and AGPR-held results would be copied
 # through VGPRs at every loop iteration)
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "score_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          # the ILP scheduler batches each step's operand reads ahead of its
          # MFMAs (one wave per SIMD has no other wave to hide LDS latency)
          "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}

@@ -336,9 +336,10 @@ csa_status indexer_score_paged_rows(const void* q_idx, const float* w, int nq, i
 
 // The jobs of a compress + score call (the key job: the one that writes
 // `keys`) and its launch; ia holds the indexer's arguments.
+// tk: the fused top-k of csa_compress_score_topk (its checks done), or null.
 static csa_status compress_score_common(const char* what, const csa_compress_job* jobs, int n_jobs,
                                         const void* keys, csa_fmt fmt, int d_idx, int nq, const IndexerArgs& ia,
-                                        bool no_queries, hipStream_t stream) {
+                                        bool no_queries, hipStream_t stream, const TopkFuse* tk = nullptr) {
   int key = -1;
   if (n_jobs > 0 && jobs) {
     for (int i = 0; i < n_jobs && i < CSA_COMPRESS_MAX_JOBS; ++i) {
@@ -360,8 +361,29 @@ static csa_status compress_score_common(const char* what, const csa_compress_job
   if (st != CSA_OK) return st;
   hipError_t e = hipSuccess;
   if (no_queries) e = n > 0 ? launch_compress_jobs(a, n, stream) : hipSuccess;
+  else if (tk) e = launch_compress_score_topk(a, n, map_key, ia, *tk, stream);
   else e = launch_compress_score(a, n, map_key, ia, stream);
   return launched(e, what);
+}
+
+// Checks of the selection arguments of csa_compress_score_topk(_paged).
+static csa_status score_topk_args(const char* what, int nq, csa_fmt fmt, int k, int32_t* idx, void* workspace,
+                                  size_t ws_bytes, TopkFuse* tk) {
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID_ARG, "%s: k must be in [1, 4096]", what);
+  if (nq <= 0) { *tk = TopkFuse{idx, static_cast<uint32_t*>(workspace), k}; return CSA_OK; }
+  if (!idx) return fail(CSA_ERR_INVALID_ARG, "%s: null idx", what);
+  if (fmt != CSA_FP8) return fail(CSA_ERR_UNSUPPORTED, "%s: the fused selection takes FP8 keys", what);
+  if (nq >= kShareMinQueries)
+    return fail(CSA_ERR_UNSUPPORTED, "%s: batches of %d queries or more take indexer_score + topk_select", what,
+                kShareMinQueries);
+  const size_t need = csa_score_topk_workspace_bytes(nq);
+  if (!workspace || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "%s: %d queries need a %zu-byte zeroed workspace, got %zu%s", what, nq, need,
+                ws_bytes, workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(CSA_ERR_WORKSPACE, "%s: the workspace must be 256-byte aligned", what);
+  *tk = TopkFuse{idx, static_cast<uint32_t*>(workspace), k};
+  return CSA_OK;
 }
 
 csa_status csa_compress_score(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
@@ -390,6 +412,46 @@ csa_status csa_compress_score_paged(const csa_compress_job* jobs, int n_jobs, co
                                    &no_queries);
   if (st != CSA_OK) return st;
   return compress_score_common(what, jobs, n_jobs, key_pool, fmt, d_idx, nq, ia, no_queries, stream);
+}
+
+size_t csa_score_topk_workspace_bytes(int nq) {
+  return nq <= 0 || nq >= kShareMinQueries ? 0 : static_cast<size_t>(nq) * kTkWsWords * sizeof(uint32_t);
+}
+
+csa_status csa_compress_score_topk(const csa_compress_job* jobs, int n_jobs, const void* q_idx, const float* w,
+                                   int nq, int n_heads, int d_idx, const void* keys, csa_fmt fmt,
+                                   const int64_t* key_off, const int64_t* q_pos, int m, float* scores, int64_t ld,
+                                   int k, int32_t* idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const char* what = "csa_compress_score_topk";
+  IndexerArgs ia{};
+  bool no_queries = false;
+  csa_status st = indexer_args(what, q_idx, w, nq, n_heads, d_idx, keys, fmt, key_off, q_pos, m, scores, ld, &ia,
+                               &no_queries);
+  if (st != CSA_OK) return st;
+  TopkFuse tk{};
+  st = score_topk_args(what, nq, fmt, k, idx, workspace, ws_bytes, &tk);
+  if (st != CSA_OK) return st;
+  return compress_score_common(what, jobs, n_jobs, keys, fmt, d_idx, nq, ia, no_queries, stream, &tk);
+}
+
+csa_status csa_compress_score_topk_paged(const csa_compress_job* jobs, int n_jobs, const void* q_idx,
+                                         const float* w, int nq, int n_heads, int d_idx, const void* key_pool,
+                                         csa_fmt fmt, int64_t pool_rows, const int32_t* block_table,
+                                         int64_t table_rows, int64_t blocks_per_seq, int block_rows,
+                                         const int32_t* q_block_row, const int64_t* q_pos, int m, float* scores,
+                                         int64_t ld, int k, int32_t* idx, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream) {
+  const char* what = "csa_compress_score_topk_paged";
+  IndexerArgs ia{};
+  bool no_queries = false;
+  csa_status st = paged_args(what, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, pool_rows, block_table,
+                             table_rows, blocks_per_seq, block_rows, q_block_row, q_pos, m, scores, ld, &ia,
+                             &no_queries);
+  if (st != CSA_OK) return st;
+  TopkFuse tk{};
+  st = score_topk_args(what, nq, fmt, k, idx, workspace, ws_bytes, &tk);
+  if (st != CSA_OK) return st;
+  return compress_score_common(what, jobs, n_jobs, key_pool, fmt, d_idx, nq, ia, no_queries, stream, &tk);
 }
 
 size_t csa_topk_workspace_bytes(int nq, int64_t ld, int k) {

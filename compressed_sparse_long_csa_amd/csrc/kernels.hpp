@@ -53,6 +53,21 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t stream);
 hipError_t launch_compress_score(const CompressArgs* jobs, int n, int key_job, const IndexerArgs& a,
                                  hipStream_t stream);
 
+// The top-k of a decode step selected in its compress + score launch
+// (csa_compress_score_topk): FP8 keys, the streaming indexer (nq below
+// kShareMinQueries).  ws: per query kTkWsWords words -- the level-1 bins of
+// the selection and an arrival counter -- zero on entry and left zero.
+constexpr int kShareMinQueries = 1024;   // FP8 batches this large take the shared-key indexer
+constexpr int kTkBins = 4096;
+constexpr int kTkWsWords = kTkBins + 64;
+struct TopkFuse {
+  int32_t* idx;      // [nq, k]
+  uint32_t* ws;      // [nq, kTkWsWords]
+  int k;
+};
+hipError_t launch_compress_score_topk(const CompressArgs* jobs, int n, int key_job, const IndexerArgs& a,
+                                      const TopkFuse& tk, hipStream_t stream);
+
 struct TopkArgs {
   const float* scores; int64_t ld; int nq; const int64_t* n_valid; int k;
   int32_t* idx; float* top_scores;

@@ -53,8 +53,10 @@ extern "C" {
 /* 2: caller-owned top-k workspace (CSA_ERR_WORKSPACE), topk_select_noalloc.
  * 3: hybrid_attn_prefill_paged, indexer_score_paged_rows,
  *    csa_compress_score_paged, csa_debug_poison_lds, CSA_VARIANT_FULL_DIMS
- *    (additions only). */
-#define CSA_ABI_VERSION 3
+ *    (additions only).
+ * 4: csa_compress_score_topk, csa_compress_score_topk_paged,
+ *    csa_score_topk_workspace_bytes (additions only). */
+#define CSA_ABI_VERSION 4
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -286,6 +288,67 @@ csa_status csa_compress_score_paged(const csa_compress_job* jobs /*[host]*/, int
                                     int64_t table_rows, int64_t blocks_per_seq, int block_rows,
                                     const int32_t* q_block_row, const int64_t* q_pos, int m, float* scores,
                                     int64_t ld, hipStream_t stream);
+
+/*
+ * csa_compress_score_topk -- a decode step's compress jobs, indexer scores
+ * and top-k selection in one call (one kernel launch).
+ *
+ * Source: the passages of csa_compress_score and topk_select; 硅星人 article,
+ * CSA paragraph (the lightning indexer scores every compressed entry and the
+ * top-k selector keeps the k best-scored ones for the attention).
+ *
+ * Results: exactly those of csa_compress_score(jobs, ..., scores, ld)
+ * followed by topk_select(scores, ld, nq, n_valid, k, idx, NULL, ...) with
+ * n_valid[i] = N_i = min(floor((q_pos[i] + 1) / m), ld): the same bytes in
+ * every compressed row, the same bits in every score (scores are still
+ * written) and the same index sets in idx [nq, k] int32 (ascending, -1
+ * padded; ties to the lower index), under csa_compress_score's precondition.
+ * The workgroups that score a query also count its scores into 4096 integer
+ * bins of the scores' order key (order-free atomics), and the last of them
+ * to finish selects the query's top-k from the scores just written, so the
+ * step needs no separate top-k launch.
+ *
+ * Supported: fmt == CSA_FP8 with nq < 1024 (the streaming indexer); other
+ * formats and larger batches are UNSUPPORTED (use csa_compress_score, or
+ * indexer_score, then topk_select).
+ * Workspace: caller-owned device memory of at least
+ * csa_score_topk_workspace_bytes(nq) bytes (nq * 16,640: per query 4096 bin
+ * counts and an arrival counter), 256-byte aligned, holding zeros before the
+ * first call.  Every call leaves the part it used at zero again, so the same
+ * workspace serves later calls without clearing; calls that may run at the
+ * same time need separate workspaces.  When the precondition of
+ * csa_compress_score does not hold, idx is undefined and the workspace must
+ * be zeroed again.
+ * Errors: those of csa_compress_score; INVALID_ARG for k < 1 or k > 4096 or
+ * a null idx; UNSUPPORTED as above; WORKSPACE when the workspace is NULL,
+ * shorter than required or misaligned.  nq = 0 runs the jobs alone.
+ */
+csa_status csa_compress_score_topk(const csa_compress_job* jobs /*[host]*/, int n_jobs, const void* q_idx,
+                                   const float* w, int nq, int n_heads, int d_idx, const void* keys,
+                                   csa_fmt fmt, const int64_t* key_off, const int64_t* q_pos, int m,
+                                   float* scores, int64_t ld, int k, int32_t* idx, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_compress_score_topk_paged -- csa_compress_score_topk over a paged key
+ * cache: the indexer side and the key job as in csa_compress_score_paged,
+ * the selection as in csa_compress_score_topk (same workspace rules).
+ *
+ * Source: the passages of csa_compress_score_paged and
+ * csa_compress_score_topk.
+ * Errors: those of csa_compress_score_paged and csa_compress_score_topk.
+ */
+csa_status csa_compress_score_topk_paged(const csa_compress_job* jobs /*[host]*/, int n_jobs, const void* q_idx,
+                                         const float* w, int nq, int n_heads, int d_idx, const void* key_pool,
+                                         csa_fmt fmt, int64_t pool_rows, const int32_t* block_table,
+                                         int64_t table_rows, int64_t blocks_per_seq, int block_rows,
+                                         const int32_t* q_block_row, const int64_t* q_pos, int m, float* scores,
+                                         int64_t ld, int k, int32_t* idx, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream);
+
+/* Bytes of zeroed workspace csa_compress_score_topk needs for nq queries
+ * (nq * 16,640); 0 for nq <= 0 or nq >= 1024. */
+size_t csa_score_topk_workspace_bytes(int nq);
 
 /*
  * indexer_score_paged -- indexer_score over a paged key cache.

@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_status_strings_and_row_bytes(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     lib.csa_status_string.restype = ctypes.c_char_p
     for code, name in ((0, b"CSA_OK"), (1, b"CSA_ERR_INVALID_ARG"), (2, b"CSA_ERR_UNSUPPORTED"),
                        (3, b"CSA_ERR_HIP"), (4, b"CSA_ERR_WORKSPACE")):
@@ -223,6 +223,39 @@ def test_compress_score_argument_errors(lib):
     assert call([key_job()], ld=0) == INVALID
     assert lib.csa_compress_score(None, 0, p, p, 0, 64, 128, keys, csa.FP8, p, p, 4, p,
                                   ctypes.c_int64(1024), None) == OK   # nothing to do
+
+
+def test_compress_score_topk_argument_errors(lib):
+    """csa_compress_score_topk's host checks: k, idx, the key format and batch
+    size of the one-launch selection, and the zeroed workspace it needs
+    (CSA_ERR_WORKSPACE when missing, short or misaligned); nothing is
+    launched when a check fails."""
+    p = _fake()
+    need = lib.csa_score_topk_workspace_bytes(16)
+    assert need == 16 * 16640
+    assert lib.csa_score_topk_workspace_bytes(0) == 0 and lib.csa_score_topk_workspace_bytes(1024) == 0
+    ws = ctypes.c_void_p(1 << 40)                              # 256-byte aligned (never touched)
+
+    def call(nq=16, fmt=csa.FP8, k=512, idx=p, w=ws, nb=need, ld=16384):
+        return lib.csa_compress_score_topk(None, 0, p, p, nq, 64, 128, p, fmt, p, p, 4, p, ctypes.c_int64(ld), k,
+                                           idx, w, nb, None)
+    for k in (0, 4097, -1):
+        assert call(k=k) == INVALID, k
+        assert "csa_compress_score_topk" in _last_error(lib)
+    assert call(idx=None) == INVALID
+    assert call(fmt=csa.MXFP4) == UNSUPPORTED
+    assert call(nq=1024) == UNSUPPORTED
+    assert call(w=None) == WORKSPACE
+    assert call(nb=need - 1) == WORKSPACE
+    assert call(w=ctypes.c_void_p((1 << 40) + 16)) == WORKSPACE
+    assert "aligned" in _last_error(lib)
+    assert call(ld=0) == INVALID                               # the indexer's own checks
+    assert call(nq=0, w=None, nb=0) == OK                      # nothing to do
+    tbl = _fake(3)
+    assert lib.csa_compress_score_topk_paged(None, 0, p, p, 2, 64, 128, p, csa.FP8, ctypes.c_int64(1000), tbl,
+                                             ctypes.c_int64(2), ctypes.c_int64(4), 32, None, p, 4, p,
+                                             ctypes.c_int64(128), 512, p, None, 0, None) == WORKSPACE
+    assert "csa_compress_score_topk_paged" in _last_error(lib)
 
 
 def test_paged_entry_points_argument_errors(lib):
