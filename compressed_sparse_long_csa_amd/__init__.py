@@ -8,6 +8,7 @@ input generator (synth).  Build the library with
 from .binding import (BF16, F32, FP8, MXFP4, SPLIT, VARIANT_AUTO, VARIANT_FULL_DIMS,  # noqa: F401
                       VARIANT_HIGH_OCC, VARIANT_LOW_OCC, CsaError, csa_compress, csa_compress_batch, csa_compress_score,
                       csa_compress_score_paged, csa_compress_score_topk, csa_compress_score_topk_paged,
+                      csa_select_and_pad,
                       debug_poison_lds,
                       hybrid_attn_decode, hybrid_attn_decode_paged,
                       hybrid_attn_prefill, hybrid_attn_prefill_paged, indexer_score, indexer_score_paged,

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libc
 # exported symbols declared in include/csa.h
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error", "csa_row_bytes",
            "csa_compress", "csa_compress_batch", "csa_compress_score", "csa_compress_score_paged",
-           "csa_compress_score_topk", "csa_compress_score_topk_paged", "csa_score_topk_workspace_bytes", "indexer_score",
+           "csa_compress_score_topk", "csa_compress_score_topk_paged", "csa_score_topk_workspace_bytes", "csa_select_and_pad",
+           "indexer_score",
            "indexer_score_paged", "indexer_score_paged_rows", "topk_select", "csa_topk_workspace_bytes", "topk_select_noalloc",
            "csa_topk_noalloc_max_bytes", "hybrid_attn_decode",
            "hybrid_attn_decode_paged", "hybrid_attn_prefill", "hybrid_attn_prefill_paged",
@@ -70,6 +71,8 @@ def load_library():
     lib.csa_compress_score_topk_paged.restype = I
     lib.csa_compress_score_topk_paged.argtypes = [ctypes.POINTER(CompressJob), I, P, P, I, I, I, P, I, I64, P, I64,
                                                   I64, I, P, P, I, P, I64, I, P, P, U, P]
+    lib.csa_select_and_pad.restype = I
+    lib.csa_select_and_pad.argtypes = [P, I, I64, I64, P, P, P]
     lib.csa_score_topk_workspace_bytes.restype = U
     lib.csa_score_topk_workspace_bytes.argtypes = [I]
     lib.indexer_score_paged.restype = I
@@ -242,6 +245,17 @@ def csa_compress_score_paged(jobs, q_idx, w, nq, n_heads, d_idx, key_pool, fmt, 
     _check(lib.csa_compress_score_paged(arr, len(jobs), _ptr(q_idx), _ptr(w), nq, n_heads, d_idx, _ptr(key_pool),
                                         fmt, pool_rows, _ptr(block_table), table_rows, blocks_per_seq, block_rows,
                                         _ptr(q_block_row), _ptr(q_pos), m, _ptr(scores), ld, _stream(stream)))
+
+
+def csa_select_and_pad(runs, n_shards, cap, row_bytes, n_valid, out, stream=None, check=True):
+    """runs: device buffer of n_shards * cap rows of row_bytes; n_valid: int64 [n_shards]
+    (device); out: n_shards * cap rows -- the valid rows in shard order, then zeros."""
+    lib = load_library()
+    if check:
+        _need(runs, "runs", min_bytes=n_shards * cap * row_bytes)
+        _need(out, "out", min_bytes=n_shards * cap * row_bytes)
+        _need(n_valid, "n_valid", torch.int64, min_numel=n_shards)
+    _check(lib.csa_select_and_pad(_ptr(runs), n_shards, cap, row_bytes, _ptr(n_valid), _ptr(out), _stream(stream)))
 
 
 def score_topk_workspace_bytes(nq):

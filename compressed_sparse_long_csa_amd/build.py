@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libcsa.so")
-SOURCES = ["csa_abi.hip", "compress.hip", "indexer.hip", "score_topk.hip", "topk.hip", "attn.hip"]
+SOURCES = ["csa_abi.hip", "compress.hip", "indexer.hip", "score_topk.hip", "topk.hip", "attn.hip", "cp_gather.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -414,6 +414,25 @@ csa_status csa_compress_score_paged(const csa_compress_job* jobs, int n_jobs, co
   return compress_score_common(what, jobs, n_jobs, key_pool, fmt, d_idx, nq, ia, no_queries, stream);
 }
 
+csa_status csa_select_and_pad(const void* in, int n_shards, int64_t cap, int64_t row_bytes,
+                              const int64_t* n_valid, void* out, hipStream_t stream) {
+  const char* what = "csa_select_and_pad";
+  if (n_shards < 1 || n_shards > kSelectPadMaxShards)
+    return fail(CSA_ERR_INVALID_ARG, "%s: n_shards must be in [1, %d]", what, kSelectPadMaxShards);
+  if (cap < 0 || cap > (int64_t{1} << 31)) return fail(CSA_ERR_INVALID_ARG, "%s: cap must be in [0, 2^31]", what);
+  if (row_bytes < 4 || row_bytes % 4 != 0 || row_bytes > (int64_t{1} << 20))
+    return fail(CSA_ERR_INVALID_ARG, "%s: row_bytes must be a multiple of 4 in [4, 2^20]", what);
+  if (cap == 0) { g_err[0] = '\0'; return CSA_OK; }
+  if (!in || !out || !n_valid) return fail(CSA_ERR_INVALID_ARG, "%s: null pointer", what);
+  if ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) % 4 != 0)
+    return fail(CSA_ERR_INVALID_ARG, "%s: in and out must be 4-byte aligned", what);
+  const uint8_t* i0 = static_cast<const uint8_t*>(in);
+  const uint8_t* o0 = static_cast<const uint8_t*>(out);
+  const int64_t bytes = static_cast<int64_t>(n_shards) * cap * row_bytes;
+  if (i0 < o0 + bytes && o0 < i0 + bytes) return fail(CSA_ERR_INVALID_ARG, "%s: in and out overlap", what);
+  return launched(launch_select_pad(in, n_shards, cap, row_bytes, n_valid, out, stream), what);
+}
+
 size_t csa_score_topk_workspace_bytes(int nq) {
   return nq <= 0 || nq >= kShareMinQueries ? 0 : static_cast<size_t>(nq) * kTkWsWords * sizeof(uint32_t);
 }

@@ -68,6 +68,14 @@ struct TopkFuse {
 hipError_t launch_compress_score_topk(const CompressArgs* jobs, int n, int key_job, const IndexerArgs& a,
                                       const TopkFuse& tk, hipStream_t stream);
 
+// Select-and-pad of context-parallel compression: n_shards runs of cap rows
+// (row_bytes, a multiple of 4), run s valid in its first n_valid[s] rows
+// (device, clamped to [0, cap]); out: the valid rows in shard order, then
+// zero rows (n_shards * cap rows).  n_shards <= kSelectPadMaxShards.
+constexpr int kSelectPadMaxShards = 256;
+hipError_t launch_select_pad(const void* in, int n_shards, int64_t cap, int64_t row_bytes, const int64_t* n_valid,
+                             void* out, hipStream_t stream);
+
 struct TopkArgs {
   const float* scores; int64_t ld; int nq; const int64_t* n_valid; int k;
   int32_t* idx; float* top_scores;

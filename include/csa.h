@@ -55,7 +55,7 @@ extern "C" {
  *    csa_compress_score_paged, csa_debug_poison_lds, CSA_VARIANT_FULL_DIMS
  *    (additions only).
  * 4: csa_compress_score_topk, csa_compress_score_topk_paged,
- *    csa_score_topk_workspace_bytes (additions only). */
+ *    csa_score_topk_workspace_bytes, csa_select_and_pad (additions only). */
 #define CSA_ABI_VERSION 4
 
 typedef enum csa_status {
@@ -345,6 +345,32 @@ csa_status csa_compress_score_topk_paged(const csa_compress_job* jobs /*[host]*/
                                          const int32_t* q_block_row, const int64_t* q_pos, int m, float* scores,
                                          int64_t ld, int k, int32_t* idx, void* workspace, size_t ws_bytes,
                                          hipStream_t stream);
+
+/*
+ * csa_select_and_pad -- join the compressed runs of the shards of one
+ * sequence into one contiguous run, the padding moved to its end.
+ *
+ * Source: DeepSeek-V4 blog, 百万 token 怎么切分到多张卡 (context parallelism:
+ * each rank receives the last m uncompressed tokens of the rank before it,
+ * compresses them with its own tokens into a fixed-length run of compressed
+ * blocks with a little padding, the runs are all-gathered, and a fused
+ * select-and-pad step reassembles them into one global compressed sequence
+ * with every padding row at its end).  On one GPU the shards' runs are
+ * regions of one buffer; the compression itself is csa_compress (segment i
+ * of a shard starts at the first token of a block, with the carried tokens).
+ *
+ *   in      [n_shards, cap] rows of row_bytes bytes (device); shard s's run
+ *           is valid in its first n_valid[s] rows (n_valid: device int64
+ *           [n_shards], clamped to [0, cap] on the device)
+ *   out     [n_shards * cap] rows (device): shard 0's valid rows, then shard
+ *           1's, ..., then zero rows; must not overlap `in`
+ * Pure data movement; the result does not depend on the launch.
+ * Errors: INVALID_ARG for n_shards outside [1, 256], cap outside [0, 2^31],
+ * row_bytes not a multiple of 4 in [4, 2^20], null pointers, unaligned or
+ * overlapping buffers.  cap = 0 does nothing.
+ */
+csa_status csa_select_and_pad(const void* in, int n_shards, int64_t cap, int64_t row_bytes,
+                              const int64_t* n_valid, void* out, hipStream_t stream);
 
 /* Bytes of zeroed workspace csa_compress_score_topk needs for nq queries
  * (nq * 16,640); 0 for nq <= 0 or nq >= 1024. */

@@ -258,6 +258,19 @@ def test_compress_score_topk_argument_errors(lib):
     assert "csa_compress_score_topk_paged" in _last_error(lib)
 
 
+def test_select_and_pad_argument_errors(lib):
+    """csa_select_and_pad's host checks (nothing is launched when one fails)."""
+    a, b, nv = ctypes.c_void_p(1 << 40), ctypes.c_void_p(1 << 41), _fake()
+
+    def call(S=4, cap=8, rb=576, i=a, o=b, n=nv):
+        return lib.csa_select_and_pad(i, S, ctypes.c_int64(cap), ctypes.c_int64(rb), n, o, None)
+    for bad in (dict(S=0), dict(S=257), dict(cap=-1), dict(rb=6), dict(rb=0), dict(i=None), dict(n=None),
+                dict(o=ctypes.c_void_p((1 << 40) + 1000)), dict(o=ctypes.c_void_p((1 << 41) + 2))):
+        assert call(**bad) == INVALID, bad
+        assert "csa_select_and_pad" in _last_error(lib)
+    assert call(cap=0, i=None, o=None, n=None) == OK             # nothing to do
+
+
 def test_paged_entry_points_argument_errors(lib):
     """indexer_score_paged / hybrid_attn_{decode,prefill}_paged: block geometry, pool
     size and format checks run on the host before any launch."""
