@@ -39,7 +39,9 @@ step at 256K and 1M tokens per sequence; `hca_decode` the HCA decode step
 (MXFP4 indexer, top-1,024) and an HCA layer over 64 sequences of 1K to 1M
 tokens; `prefill` the CSA prefill
 chunk (2,048 tokens after 131,072 cached: compress, indexer, top-k 1,024,
-prefill attention) and the contractions' MFMA rates.  `--copy-probe MIB` only
+prefill attention) and the contractions' MFMA rates; `cp_select_and_pad` the
+context-parallel reassembly of a 1M-token sequence's compressed cache from 8
+shards.  `--copy-probe MIB` only
 runs a plain copy of known size, the reference for rocprofv3 byte counters.
 """
 import argparse
@@ -866,6 +868,33 @@ def fp32_leg(steps, warmup):
             "kernels_us": {n: round(v, 2) for n, v in us.items()}, "graph": True}
 
 
+def cp_leg(reps=20, S=8, L=1048576, m=4):
+    """Context-parallel reassembly of one CSA layer's compressed cache: a
+    1,048,576-token sequence cut into S shards, each shard's fixed-length run
+    of compressed entries (576-byte rows, one padding row) joined by
+    csa_select_and_pad into one run with the padding at the end.  Bytes: the
+    valid rows read once, every output row written once.  Two copies of the
+    runs alternate so the gather reads HBM."""
+    rb = 576
+    n_all = L // m
+    cuts = np.linspace(0, L, S + 1).astype(np.int64)
+    cuts[1:-1] += np.random.default_rng(8).integers(-1000, 1000, size=S - 1)   # cuts off block boundaries
+    n_valid = [int(cuts[s + 1] // m - cuts[s] // m) if s + 1 < S else int(n_all - cuts[s] // m) for s in range(S)]
+    cap = max(n_valid) + 1
+    runs = [torch.randint(0, 256, (S * cap * rb,), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty(S * cap * rb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    nv = torch.tensor(n_valid, dtype=torch.int64, device="cuda")
+    fs = [lambda i=i: csa.csa_select_and_pad(runs[i], S, cap, rb, nv, outs[i], check=False) for i in range(2)]
+    for f in fs:
+        f()
+    torch.cuda.synchronize()
+    us = _batch_period(fs, reps)
+    nbytes = sum(n_valid) * rb + S * cap * rb
+    return {"workload": f"cp_reassembly_ctx{L}_{S}shards", "shards": S, "rows_per_shard": cap,
+            "valid_rows": sum(n_valid), "us": us, "bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
 def prefill_leg(reps=10):
     """The CSA prefill workload: a chunk of 2,048 tokens after 131,072 cached,
     on inputs drawn on the device (seeded).  One pass = csa_compress_batch
@@ -1112,6 +1141,7 @@ def main():
         line["ragged"] = ragged_leg(args.steps, args.warmup)
     if not args.no_prefill:
         line["prefill"] = prefill_leg()
+    line["cp_select_and_pad"] = cp_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -11,7 +11,8 @@
 //      first min(n_valid[s], cap) rows (n_valid clamped to [0, cap]);
 // out: n_shards * cap rows: shard 0's valid rows, then shard 1's, ..., then
 //      zero rows.  Pure data movement (integer work): the result does not
-//      depend on how the launch is split.
+//      depend on how the launch is split.  Shard s's valid rows are one
+//      contiguous run of `in`, so the join is a flat copy of words.
 #include "kernels.hpp"
 
 namespace csa {
@@ -19,22 +20,25 @@ namespace csa {
 namespace {
 
 constexpr int kGThreads = 256;
-constexpr int kGRowsPerWg = 16;            // one row per 16 lanes' worth of work, 4 rows per wave
+constexpr int kGWordsPerThread = 4;        // output words per thread per pass (loads in flight)
 
-__global__ void __launch_bounds__(kGThreads) select_pad_kernel(const uint32_t* in, int n_shards, int64_t cap,
-                                                               int64_t row_words, const int64_t* n_valid,
-                                                               uint32_t* out) {
-  // exclusive prefix of the shards' valid counts, in LDS (n_shards <= 256)
+// The output is a flat array of words (W = 16 bytes where rows allow, else
+// 4): shard s's valid rows are one contiguous run of the input, so output
+// word w below the valid total comes from the shard whose run holds it, at
+// the same offset into that run; words past it are zero.
+template <typename W>
+__global__ void __launch_bounds__(kGThreads) select_pad_kernel(const W* in, int n_shards, int64_t cap,
+                                                               int64_t row_words, const int64_t* n_valid, W* out) {
+  // exclusive prefix of the shards' valid counts, in words (n_shards <= 256)
   __shared__ int64_t pre[kGThreads + 1];
   __shared__ int64_t part[kGThreads / 64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   int64_t v = 0;
   if (t < n_shards) {
     v = n_valid[t];
-    v = v < 0 ? 0 : (v > cap ? cap : v);
+    v = (v < 0 ? 0 : (v > cap ? cap : v)) * row_words;
   }
-  // inclusive scan over the block: within the wave by shuffles, then the waves
-  int64_t x = v;
+  int64_t x = v;                                       // inclusive scan: the wave, then the waves
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int64_t y = __shfl_up(x, d);
@@ -48,24 +52,28 @@ __global__ void __launch_bounds__(kGThreads) select_pad_kernel(const uint32_t* i
   if (t == 0) pre[0] = 0;
   __syncthreads();
   const int64_t total = pre[n_shards];
-  const int64_t rows = static_cast<int64_t>(n_shards) * cap;
-  // each wave copies one output row at a time: row j < total comes from the
-  // shard s with pre[s] <= j < pre[s + 1], row pre[s] + r <- shard s row r
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * kGRowsPerWg + wv; j < rows;
-       j += static_cast<int64_t>(gridDim.x) * kGRowsPerWg) {
-    for (int64_t jj = j; jj < j + kGRowsPerWg && jj < rows; jj += kGThreads / 64) {
-      uint32_t* dst = out + jj * row_words;
-      if (jj < total) {
-        int lo = 0, hi = n_shards - 1;                 // the last s with pre[s] <= jj
+  const int64_t words = static_cast<int64_t>(n_shards) * cap * row_words;
+  const int64_t run = cap * row_words;                 // words per shard run
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kGThreads * kGWordsPerThread;
+  for (int64_t w0 = static_cast<int64_t>(blockIdx.x) * kGThreads * kGWordsPerThread + t; w0 < words; w0 += stride) {
+    W val[kGWordsPerThread];
+#pragma unroll
+    for (int u = 0; u < kGWordsPerThread; ++u) {
+      const int64_t w = w0 + static_cast<int64_t>(u) * kGThreads;   // coalesced within each u
+      val[u] = W{};
+      if (w < total) {
+        int lo = 0, hi = n_shards - 1;                 // the last s with pre[s] <= w
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= jj) lo = mid; else hi = mid - 1;
+          if (pre[mid] <= w) lo = mid; else hi = mid - 1;
         }
-        const uint32_t* src = in + (static_cast<int64_t>(lo) * cap + (jj - pre[lo])) * row_words;
-        for (int64_t c = lane; c < row_words; c += 64) dst[c] = src[c];
-      } else {
-        for (int64_t c = lane; c < row_words; c += 64) dst[c] = 0u;
+        val[u] = in[static_cast<int64_t>(lo) * run + (w - pre[lo])];
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kGWordsPerThread; ++u) {
+      const int64_t w = w0 + static_cast<int64_t>(u) * kGThreads;
+      if (w < words) out[w] = val[u];
     }
   }
 }
@@ -76,13 +84,21 @@ hipError_t launch_select_pad(const void* in, int n_shards, int64_t cap, int64_t 
                              void* out, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(n_shards) * cap;
   if (rows == 0) return hipSuccess;
-  const int64_t wgs = (rows + kGRowsPerWg - 1) / kGRowsPerWg;
-  const unsigned grid = static_cast<unsigned>(wgs < 65536 ? wgs : 65536);
-  log_launch("select-and-pad: %d shards x %lld rows of %lld bytes in %u workgroups", n_shards,
-             static_cast<long long>(cap), static_cast<long long>(row_bytes), grid);
-  hipLaunchKernelGGL(select_pad_kernel, dim3(grid), dim3(kGThreads), 0, stream,
-                     static_cast<const uint32_t*>(in), n_shards, cap, row_bytes / 4, n_valid,
-                     static_cast<uint32_t*>(out));
+  const bool w16 = row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) % 16 == 0;
+  const int64_t wb = w16 ? 16 : 4;
+  const int64_t words = rows * (row_bytes / wb);
+  const int64_t per_wg = static_cast<int64_t>(kGThreads) * kGWordsPerThread;
+  const int64_t wgs = (words + per_wg - 1) / per_wg;
+  const unsigned grid = static_cast<unsigned>(wgs < 8192 ? wgs : 8192);
+  log_launch("select-and-pad: %d shards x %lld rows of %lld bytes, %lld-byte words in %u workgroups", n_shards,
+             static_cast<long long>(cap), static_cast<long long>(row_bytes), static_cast<long long>(wb), grid);
+  if (w16)
+    hipLaunchKernelGGL(select_pad_kernel<uint4>, dim3(grid), dim3(kGThreads), 0, stream, static_cast<const uint4*>(in),
+                       n_shards, cap, row_bytes / 16, n_valid, static_cast<uint4*>(out));
+  else
+    hipLaunchKernelGGL(select_pad_kernel<uint32_t>, dim3(grid), dim3(kGThreads), 0, stream,
+                       static_cast<const uint32_t*>(in), n_shards, cap, row_bytes / 4, n_valid,
+                       static_cast<uint32_t*>(out));
   return hipGetLastError();
 }
 
