@@ -64,6 +64,20 @@ def test_compress_score_step_ignores_stale_lds():
     _same_under_poison(lambda: fused._run(st4, False), "compress + MXFP4 indexer")
 
 
+def test_fused_topk_ignores_stale_lds():
+    """csa_compress_score_topk after every LDS fill: the same scores and sets
+    (its LDS bins are cleared at the start of every workgroup)."""
+    import test_gpu_score_topk as stk
+    st = fused._case([65536, 9000, 2052, 132, 8, 40000], [True, False, True, True, True, False], 64, csa.FP8, 905)
+    ws = stk._workspace(st["B"])
+
+    def run():
+        _, _, scores, idx = stk._fused(st, 512, ws)
+        assert not torch.any(ws != 0).item()
+        return scores, idx
+    _same_under_poison(run, "csa_compress_score_topk")
+
+
 def test_topk_ignores_stale_lds_and_workspace():
     rng = np.random.default_rng(903)
     for nq, ld, k, ties in ((16, 16384, 512, 0), (5, 100000, 1024, 3), (3, 5000, 64, 5)):
