@@ -259,12 +259,14 @@ def algorithmic_flops(W):
             "hybrid_attn_decode": int(2 * 2 * sel.sum() * c["H"] * W["D"])}
 
 
-def time_graph(steps_r, steps, warmup):
+def time_graph(steps_r, steps, warmup, spread=0):
     """Replica r's step is captured once on its own and once more, in replica
     order, inside one graph of all R steps (a decode pass through R layers,
     as a model would capture it).  W warm-up steps, then exactly `steps` timed
     steps between two synchronised events: whole R-step graphs, then the
-    single-step graphs of the remainder.  Returns ms per step."""
+    single-step graphs of the remainder.  Returns ms per step; with spread > 0
+    also the p10 / median / p90 of ms per step over `spread` replays of the
+    R-step graph, each between its own pair of events."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -298,7 +300,18 @@ def time_graph(steps_r, steps, warmup):
     run(steps)
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    ms = e0.elapsed_time(e1) / steps
+    if spread <= 0:
+        return ms
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(spread + 1)]
+    ev[0].record()
+    for i in range(spread):
+        chain.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) / R for i in range(spread)])
+    return ms, {"p10": float(np.percentile(per, 10)), "median": float(np.median(per)),
+                "p90": float(np.percentile(per, 90)), "graphs": spread, "steps_per_graph": R}
 
 
 def _event_pairs(fs, steps):
@@ -1060,7 +1073,7 @@ def main():
     reps = make_replicas(W, max(1, args.replicas))
     made = [make_step(Wr, check=False) for Wr in reps]
     ms_warm = time_graph([made[0][0]], args.steps, args.warmup)
-    ms = time_graph([m[0] for m in made], args.steps, args.warmup)
+    ms, spread = time_graph([m[0] for m in made], args.steps, args.warmup, spread=200)
     batch_us = {}
     event_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)), batch_us)
     per_us = batch_us
@@ -1110,6 +1123,7 @@ def main():
                    "heads": W["c"]["H"], "head_dim": W["D"], "indexer": "fp8 64x128",
                    "window": 128, "graph": True, "steps_per_graph": len(reps), "variant": "auto",
                    "state_replicas": len(reps)},
+        "ms_per_step_spread": spread,
         "value_one_warm_cache": B / (ms_warm * 1e-3),
         "hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
         "step_bytes": step_bytes,
