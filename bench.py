@@ -314,6 +314,21 @@ def time_graph(steps_r, steps, warmup, spread=0):
                 "p90": float(np.percentile(per, 90)), "graphs": spread, "steps_per_graph": R}
 
 
+def time_eager(steps_r, steps, warmup):
+    """The same steps launched one call at a time from Python (no graph):
+    ms per step between two events; bound by the host's launch rate."""
+    for i in range(warmup):
+        steps_r[i % len(steps_r)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        steps_r[i % len(steps_r)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def _event_pairs(fs, steps):
     """Mean time between two events recorded around f() on the current stream,
     f taken in turn from fs.  A spin kernel is queued first, so every launch of
@@ -1074,6 +1089,7 @@ def main():
     made = [make_step(Wr, check=False) for Wr in reps]
     ms_warm = time_graph([made[0][0]], args.steps, args.warmup)
     ms, spread = time_graph([m[0] for m in made], args.steps, args.warmup, spread=200)
+    ms_eager = time_eager([m[0] for m in made], min(args.steps, 300), min(args.warmup, 30))
     batch_us = {}
     event_us, event_floor_us = time_kernels([m[1] for m in made], max(20, min(100, args.steps)), batch_us)
     per_us = batch_us
@@ -1124,6 +1140,7 @@ def main():
                    "window": 128, "graph": True, "steps_per_graph": len(reps), "variant": "auto",
                    "state_replicas": len(reps)},
         "ms_per_step_spread": spread,
+        "ms_per_step_no_graph": ms_eager,
         "value_one_warm_cache": B / (ms_warm * 1e-3),
         "hbm_gbps_algorithmic": step_bytes / (ms * 1e-3) / 1e9,
         "step_bytes": step_bytes,
