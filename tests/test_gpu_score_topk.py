@@ -222,3 +222,20 @@ def test_score_topk_in_a_graph():
         assert not torch.any(ws != 0).item(), rep
         other = _fused(st, k, ws)                        # eager work between replays
         assert np.array_equal(other[3], eager[3])
+
+
+def test_score_topk_many_calls_on_one_workspace():
+    """Thirty calls in a row over three batches (bench shape, ragged, long rows)
+    sharing one workspace: every call gives the two-call path's sets and
+    scores, and leaves the workspace at zero for the next."""
+    cases = [_case([65536] * 16, [True] * 16, 64, csa.FP8, 91),
+             _case(LENGTHS, NEW, 64, csa.FP8, 92),
+             _case([262144, 100000, 40000], [True, False, True], 64, csa.FP8, 93)]
+    refs = [_two_calls(st, 512) for st in cases]
+    ws = _workspace(16)
+    for rep in range(10):
+        for st, ref in zip(cases, refs):
+            got = _fused(st, 512, ws)
+            assert np.array_equal(got[3], ref[3]), f"call {rep}: sets differ"
+            assert np.array_equal(got[2].view(np.uint32), ref[2].view(np.uint32)), f"call {rep}: scores differ"
+    assert not torch.any(ws != 0).item()
