@@ -238,3 +238,50 @@ def test_paged_argument_errors():
     with pytest.raises(ValueError):                         # a query sees more rows than its table row holds
         csa.indexer_score_paged(dev(inp.q_idx), dev(inp.w), B, 64, 128, keys, csa.FP8, int(inp.n_ent.sum()),
                                 table[:, :1].contiguous(), 1, 16, dev(inp.q_pos), 4, scores, ld)
+
+
+def test_one_block_table_serves_the_csa_and_hca_pools():
+    """The classic cache's 128-token block (硅星人 article, classic-cache
+    paragraph): token block j of a sequence holds its 32 CSA entries (m = 4)
+    and its one HCA entry (m' = 128).  One block table per sequence names the
+    block in both pools -- CSA rows at block_rows = 32, HCA rows at
+    block_rows = 1 -- and the paged CSA and HCA attentions give the
+    contiguous calls' bits through it."""
+    lengths = [65636, 9000, 300, 640, 127]
+    ci = synth.decode_inputs(701, lengths, m=4, H=64, D=512, R=64, k=512)
+    hi = synth.decode_inputs(702, lengths, m=128, H=64, D=512, R=64, csa=False)
+    rb = synth.row_bytes(csa.SPLIT, 512, 64)
+    rng = np.random.default_rng(703)
+    nb = (ci.n_ent.astype(np.int64) + 31) // 32                 # token blocks (of 128) per sequence
+    assert np.all(hi.n_ent <= nb)
+    total = int(nb.sum()) + 2
+    bps = int(max(1, nb.max()))
+    perm = rng.permutation(total).astype(np.int32)
+    table = rng.integers(0, total, size=(len(lengths), bps)).astype(np.int32)
+    csa_pool = rng.integers(0, 256, size=(total * 32, rb), dtype=np.uint8)
+    hca_pool = rng.integers(0, 256, size=(total, rb), dtype=np.uint8)
+    crow, hrow = ci.kv.reshape(-1, rb), hi.kv.reshape(-1, rb)
+    nxt = 0
+    for i in range(len(lengths)):
+        for j in range(int(nb[i])):
+            blk = int(perm[nxt])
+            nxt += 1
+            table[i, j] = blk
+            lo, cnt = int(ci.kv_off[i]) + 32 * j, min(32, int(ci.n_ent[i]) - 32 * j)
+            csa_pool[blk * 32: blk * 32 + cnt] = crow[lo: lo + cnt]
+            if j < int(hi.n_ent[i]):
+                hca_pool[blk] = hrow[int(hi.kv_off[i]) + j]
+    sel = synth.random_selection(np.random.default_rng(704), ci.n_ent, ci.k)
+    tab = dev(table)
+    for inp, pool, BR, idx, k in ((ci, csa_pool, 32, dev(sel), ci.k), (hi, hca_pool, 1, None, 0)):
+        B, H, D = inp.B, inp.H, inp.D
+        q, q_pos, win, win_len, sinks = dev(inp.q), dev(inp.q_pos), dev(inp.win), dev(inp.win_len), dev(inp.sinks)
+        a, b = gpu_bytes(B * H * D * 2), gpu_bytes(B * H * D * 2)
+        csa.hybrid_attn_decode(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(inp.kv), csa.SPLIT,
+                               dev(inp.kv_off), inp.m, idx, k, win, csa.BF16, inp.n_win, win_len, sinks, inp.scale,
+                               a, csa.BF16, csa.VARIANT_AUTO)
+        csa.hybrid_attn_decode_paged(q, csa.BF16, B, H, D, q_pos, None, EPS, inp.R, ROPE_BASE, dev(pool), csa.SPLIT,
+                                     pool.shape[0], tab, bps, BR, inp.m, idx, k, win, csa.BF16, inp.n_win, win_len,
+                                     sinks, inp.scale, b, csa.BF16, csa.VARIANT_AUTO)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"m = {inp.m}: paged output differs"
